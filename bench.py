@@ -1,0 +1,288 @@
+"""Benchmark of the LoGRA per-layer hot path on one MI355X.
+
+One step = one training step of one layer as Algorithm 1 of the LoGRA paper
+runs it on the trainer: S <- 0, M sketch-accumulate calls (one per
+microbatch), the fused expand-and-merge of W.  Inputs for every microbatch
+are already resident in HBM; several distinct input sets rotate so that the
+working set exceeds the 256 MB last-level (MALL) cache and each step streams
+its inputs from HBM.
+
+Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
+  roofline     the sketch-accumulate call (projection + contraction kernels)
+               against MI355X's 8 TB/s HBM peak, timed with HIP events on the
+               stream the kernels run on;
+  merge        the fused merge against the same peak;
+  cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn1536]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "rank_gradient_sketching_accumulate_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+MALL_BYTES = 256 * 2**20
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def sketch_bytes(T, k, d, r):
+    """Algorithmic HBM bytes of one sketch call: X and dY read once (bf16),
+    S read and written once (fp32)."""
+    return 2 * T * (k + d) + 8 * d * r
+
+
+def merge_bytes(d, k, r):
+    """W read and written once (bf16), U read once (fp32)."""
+    return 4 * d * k + 4 * d * r
+
+
+def load_traffic(workload: str):
+    """HBM bytes per sketch call from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("sketch_call_bytes")
+
+
+def cpu_baseline(w, layer, r, seed, budget_s: float):
+    """Time the float64 oracle (as it stands) on host copies of the
+    workload's microbatches: dense G = dY^T X, then the projection."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    L = w.layers[layer]
+    A = oracle.rademacher_projection(seed, r, L.k)
+    S = np.zeros((L.d, r))
+    host = []
+    for m in range(min(w.M, 2)):
+        X, dY = wl.layer_inputs(w, layer, m, device="cpu")
+        host.append((X.float().numpy().astype(np.float64), dY.float().numpy().astype(np.float64)))
+    tokens = 0
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        Xh, dYh = host[n % len(host)]
+        S = oracle.sketch_accumulate(S, [Xh], [dYh], A)
+        tokens += Xh.shape[0]
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s/layer",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} microbatch sketch(es) of {w.T} tokens of the {L.name} {L.d}x{L.k} layer, r={r}: "
+                  f"dense fp64 G = dY^T X then G A^T, {dt:.1f} s of host time",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="attn1536")
+    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--rank", type=int, default=0, help="rank r (default: the workload's first)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(
+            "bench.py measures one GPU: this build has no multi-GPU path "
+            "(the sketch is additive over tokens; sharding is described in the design notes).",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import rank_gradient_sketching_accumulate_amd as lg
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    lg.load_library()
+
+    if args.calibrate_copy:
+        n = 2**29  # 1 GiB of int16
+        a = torch.ones(n, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 2 * n, "copies": 3}))
+        return
+
+    w = wl.WORKLOADS[args.workload]
+    L = w.layers[args.layer]
+    r = args.rank or w.ranks[0]
+    T, M, d, k = w.T, w.M, L.d, L.k
+    seed = wl.sign_seed(args.layer)
+    scale = w.scales[-1]
+
+    set_bytes = M * 2 * T * (k + d)
+    nsets = max(1, math.ceil(2.5 * MALL_BYTES / set_bytes)) if set_bytes < 2.5 * MALL_BYTES else 1
+    sets = []
+    for s in range(nsets):
+        mbs = []
+        for m in range(M):
+            X, dY = wl.layer_inputs(w, args.layer, m + M * s, device=dev)
+            mbs.append((X, dY))
+        sets.append(mbs)
+    S = torch.zeros((d, r), dtype=torch.float32, device=dev)
+    W = wl.layer_weight(w, args.layer, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        S.zero_()
+        for m, (X, dY) in enumerate(sets[i % nsets]):
+            if ev is not None:
+                ev[0][m].record(stream)
+            lg.sketch_accumulate(X, dY, seed, r, S)
+            if ev is not None:
+                ev[1][m].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        lg.merge_update(W, S, seed, r, scale)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Whole-step throughput: K steps between two synchronisations.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-call durations with events on the kernels' stream.
+    call_ms, merge_ms = [], []
+    for i in range(args.steps):
+        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(M)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(M)],
+              torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        step(i, ev)
+        torch.cuda.synchronize()
+        call_ms += [ev[0][m].elapsed_time(ev[1][m]) for m in range(M)]
+        merge_ms.append(ev[2].elapsed_time(ev[3]))
+    call_ms.sort()
+    merge_ms.sort()
+    t_call = sum(call_ms) / len(call_ms) * 1e-3
+    t_merge = sum(merge_ms) / len(merge_ms) * 1e-3
+    sb = sketch_bytes(T, k, d, r)
+    mb = merge_bytes(d, k, r)
+    sk_gbs = sb / t_call / 1e9
+    mg_gbs = mb / t_merge / 1e9
+
+    traffic = load_traffic(args.workload)
+    out = {
+        "metric": "sketch-accumulate tokens/s/layer + merge GB/s, % of MI355X HBM roofline",
+        "value": M * T / (step_ms * 1e-3),
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "wall_s": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, fp32 accumulation",
+        "data": "synthetic (seeded iid Gaussian activations and gradients, random-init bf16 weight)",
+        "config": {
+            "workload": w.title,
+            "layer": f"{L.name} d={d} k={k}",
+            "r": r,
+            "microbatches": M,
+            "tokens_per_microbatch": T,
+            "merge_scale": scale,
+            "input_sets_rotated": nsets,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "sketch_accumulate call (proj_kernel + contract_kernel)",
+            "bound": "hbm",
+            "achieved": sk_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": sk_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_call": sb,
+            "avg_call_us": t_call * 1e6,
+            "p10_call_us": call_ms[len(call_ms) // 10] * 1e3,
+            "p90_call_us": call_ms[(9 * len(call_ms)) // 10] * 1e3,
+        },
+        "merge": {
+            "kernel": "merge_kernel",
+            "bound": "hbm",
+            "achieved": mg_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": mg_gbs / HBM_PEAK_GBS,
+            "algorithmic_bytes": mb,
+            "avg_us": t_merge * 1e6,
+        },
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        del sets
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, args.layer, r, seed, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * logra.h -- C ABI of the LoGRA low-rank gradient sketch library (MI355X, gfx950).
+ *
+ * Source of the method: "LoGRA: Scaling LLM Reinforcement Learning with
+ * Low-Rank Gradient Sketches" (arXiv 2610.06647v2), section 2.1 ("Low-rank
+ * gradient sketches": equations 2-4), section 2.2 (Algorithm 1; "Memory and
+ * synchronization") and appendix B (RowAdam, equation 15).
+ *
+ * Notation.  One linear layer Y = X W^T with W in R^{d x k}.  X (T x k) holds
+ * the layer inputs of one microbatch of T tokens, dY (T x d) the gradients of
+ * the layer outputs, so the weight gradient is G = dY^T X (d x k).  A = s/sqrt(r)
+ * with s in {+1,-1}^{r x k} is the random sign projection, S = G A^T (d x r)
+ * the sketch.
+ *
+ * Conventions shared by every entry point.
+ *   - Matrices are row-major; `ld*` is the row stride in ELEMENTS and must be
+ *     >= the number of columns.
+ *   - Every pointer is a DEVICE pointer on the current HIP device, owned by the
+ *     caller; the library keeps no reference after the call returns.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising.  Scalar arguments are captured by value.
+ *   - Validation runs before anything is enqueued; on any error nothing is
+ *     written and a nonzero status is returned.  logra_last_error() then gives
+ *     a thread-local description.  No C++ exception crosses this boundary.
+ *   - 1 <= r <= LOGRA_MAX_RANK.
+ *   - NaN and Inf in the inputs propagate to the outputs; nothing traps.
+ *
+ * Sign generator (this library's fixed choice; the paper only requires
+ * independent random signs that the rollout side can regenerate from a seed):
+ *   s[i][j] = +1 if bit b is 0, -1 if it is 1, where b is bit (q mod 64) of
+ *   word (q / 64) of Philox4x64-10(counter = (j / 256, i, 0, 0),
+ *   key = (seed, 0)), q = j mod 256.  Philox4x64-10 is the generator of
+ *   Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as
+ *   1, 2, 3" (SC'11).  The sign of (i, j) does not depend on r or k.
+ */
+#ifndef LOGRA_H_
+#define LOGRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOGRA_ABI_VERSION 1
+#define LOGRA_MAX_RANK 256
+
+typedef enum {
+  LOGRA_OK = 0,
+  LOGRA_ERR_NULL = 1,   /* a required pointer is NULL                            */
+  LOGRA_ERR_SHAPE = 2,  /* negative size, ld < columns, or sizes that disagree   */
+  LOGRA_ERR_ALIGN = 3,  /* base pointer or ld breaks the stated alignment        */
+  LOGRA_ERR_RANGE = 4,  /* r, step, beta2 or eps_rel out of range                */
+  LOGRA_ERR_ALIAS = 5,  /* an output overlaps an input it must not overlap       */
+  LOGRA_ERR_HIP = 6,    /* a HIP runtime call or kernel launch failed            */
+  LOGRA_ERR_NOMEM = 7   /* the library could not obtain its scratch memory       */
+} logra_status;
+
+/*
+ * Sketch accumulation (paper section 2.1, equation 2, and Algorithm 1's
+ * direct sketch accumulation step):
+ *
+ *     S[d x r] += (1/sqrt(r)) * dY^T[d x T] * ( X[T x k] * s^T[k x r] )
+ *
+ * i.e. S += G A^T for this microbatch, computed by projecting the inputs first
+ * and never forming G.  Call it once per microbatch with the same seed and r;
+ * the caller zeroes S once per training step (Algorithm 1) -- the library
+ * only adds.
+ *
+ *   X    bf16, T x k, row stride ldx (elements).  16-byte aligned base,
+ *        ldx a multiple of 8.
+ *   dY   bf16, T x d, row stride lddy.  16-byte aligned base, lddy a multiple
+ *        of 8.
+ *   S    fp32, d x r, row stride lds >= r, read and written.  Must not overlap
+ *        X or dY.
+ *   T, k, d >= 0; T == 0, k == 0 or d == 0 leaves S unchanged.
+ *
+ * Internal scratch (the projected inputs P = X s^T, T x r) is held by the
+ * library per (device, stream) and grown on first use of a larger size;
+ * concurrent calls on different streams are safe, calls that update the same S
+ * must be ordered by the caller.  The result is not bitwise reproducible
+ * across runs when the token range is split over several workgroups (fp32
+ * atomic adds); any order is within the stated error bound.
+ */
+logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
+                                     const void* dY, int64_t lddy,
+                                     int64_t T, int64_t k, int64_t d,
+                                     uint64_t seed, int32_t r,
+                                     float* S, int64_t lds,
+                                     hipStream_t stream);
+
+/*
+ * Fused expand-and-merge (paper section 2.1, equations 3 and 4; Algorithm 1's
+ * trainer update):
+ *
+ *     W[d x k] <- RNE_bf16( W - scale * (1/sqrt(r)) * U[d x r] * s[r x k] )
+ *
+ * in place, with scale = alpha * eta supplied by the host.  U is the sketch S,
+ * or S after logra_rowadam_scale.  No d x k update buffer exists: each W tile
+ * is read, updated in fp32 and rounded to bf16 (round to nearest, ties to
+ * even) once.  U is first copied into library scratch (per device and
+ * stream) as a bf16 high/low pair, which carries it to about 2^-16 relative.
+ *
+ *   W    bf16, d x k, row stride ldw, read and written.  8-byte aligned base,
+ *        ldw a multiple of 4.
+ *   U    fp32, d x r, row stride ldu >= r, 4-byte aligned.  Must not overlap W.
+ *   d, k >= 0 (0 is a no-op).  scale may be any finite float; 0 leaves W
+ *   bitwise unchanged.
+ */
+logra_status logra_merge_update(void* W, int64_t ldw,
+                                const float* U, int64_t ldu,
+                                int64_t d, int64_t k,
+                                uint64_t seed, int32_t r, float scale,
+                                hipStream_t stream);
+
+/*
+ * RowAdam row scaling (paper appendix B, equation 15), S -> U in place:
+ *
+ *     m_i   = (1/r) sum_j S_ij^2
+ *     v_i  <- beta2 v_i + (1 - beta2) m_i
+ *     vh_i  = v_i / (1 - beta2^step)
+ *     eps   = max(eps_rel * mean_i sqrt(vh_i), 1e-30)
+ *     Ut_i  = S_i / (sqrt(vh_i) + eps)
+ *     U     = Ut * ||S||_F / ||Ut||_F        (U = 0 when ||Ut||_F = 0)
+ *
+ * Readings of words the appendix text lost: the stabiliser uses the MEAN over
+ * rows of sqrt(vh); the rescale restores the Frobenius norm of the incoming
+ * sketch; the sketch is used as passed in.
+ *
+ *   S     fp32, d x r, row stride lds >= r, overwritten with U.
+ *   v     fp32, d values, the per-row second moment, read and written; starts
+ *         at zero and persists across projection refreshes.  Must not overlap S.
+ *   step  >= 1, counts RowAdam updates of this matrix.
+ *   0 <= beta2 < 1, eps_rel >= 0.
+ * All reductions stay on the device; the result is deterministic.
+ */
+logra_status logra_rowadam_scale(float* S, int64_t lds, float* v,
+                                 int64_t d, int32_t r, int64_t step,
+                                 float beta2, float eps_rel,
+                                 hipStream_t stream);
+
+/*
+ * Materialise the signs s (r x k) as int8 (+1 / -1), row-major, row stride k,
+ * into `out` (device).  A test and debugging aid: the hot path never stores
+ * the signs.
+ */
+logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out,
+                         hipStream_t stream);
+
+/* Bytes of per-stream scratch logra_sketch_accumulate needs for T tokens at rank r. */
+size_t logra_workspace_bytes(int64_t T, int32_t r);
+
+/* Static text for a status code. */
+const char* logra_status_string(logra_status s);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* logra_last_error(void);
+
+/* LOGRA_ABI_VERSION of the built library. */
+int logra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGRA_H_ */

@@ -1,0 +1,219 @@
+"""LoGRA per-layer sketch-accumulate / RowAdam / merge on MI355X.
+
+Thin ctypes binding over the C ABI of ``liblogra.so`` (declared in
+``include/logra.h``).  This module only marshals arguments: every step of the
+path runs in the library's HIP kernels.  torch is used for device memory and
+for the current HIP stream; it is never used to compute.
+
+Method: "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
+Sketches" (arXiv 2610.06647v2), section 2.1 (equations 2-4), Algorithm 1 and
+appendix B (RowAdam).
+
+If the library has not been built, importing still works but every call
+raises ``LograError``: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LograError",
+    "LIB_PATH",
+    "MAX_RANK",
+    "load_library",
+    "library_loaded",
+    "sketch_accumulate",
+    "merge_update",
+    "rowadam_scale",
+    "signs",
+    "workspace_bytes",
+    "abi_version",
+    "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogra.so")
+MAX_RANK = 256
+
+# Every symbol include/logra.h declares.
+EXPORTED_SYMBOLS = (
+    "logra_sketch_accumulate",
+    "logra_merge_update",
+    "logra_rowadam_scale",
+    "logra_signs",
+    "logra_workspace_bytes",
+    "logra_status_string",
+    "logra_last_error",
+    "logra_abi_version",
+)
+
+
+class LograError(RuntimeError):
+    """A nonzero status from the library, or the library is missing."""
+
+    def __init__(self, msg: str, status: int | None = None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(lib):
+    c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
+    lib.logra_sketch_accumulate.restype = ctypes.c_int
+    lib.logra_merge_update.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_f, c_vp]
+    lib.logra_merge_update.restype = ctypes.c_int
+    lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
+    lib.logra_rowadam_scale.restype = ctypes.c_int
+    lib.logra_signs.argtypes = [c_u64, c_i32, c_i64, c_vp, c_vp]
+    lib.logra_signs.restype = ctypes.c_int
+    lib.logra_workspace_bytes.argtypes = [c_i64, c_i32]
+    lib.logra_workspace_bytes.restype = ctypes.c_size_t
+    lib.logra_status_string.argtypes = [ctypes.c_int]
+    lib.logra_status_string.restype = ctypes.c_char_p
+    lib.logra_last_error.argtypes = []
+    lib.logra_last_error.restype = ctypes.c_char_p
+    lib.logra_abi_version.argtypes = []
+    lib.logra_abi_version.restype = ctypes.c_int
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of liblogra.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise LograError(
+            f"{p} is missing: build it with `python -m rank_gradient_sketching_accumulate_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(p)
+    _declare(lib)
+    _lib = lib
+    return lib
+
+
+def library_loaded() -> bool:
+    return _lib is not None
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        name = lib.logra_status_string(status).decode()
+        detail = lib.logra_last_error().decode()
+        raise LograError(f"logra status {status} ({name}): {detail}", status)
+
+
+def _stream_handle(tensor) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(tensor.device).cuda_stream)
+
+
+def _need(t, dtype, name, ndim=2):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if ndim == 2:
+        if t.size(1) > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit column stride")
+    elif t.dim() == 1 and t.numel() > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ld(t) -> int:
+    return int(t.stride(0)) if t.size(0) > 1 else max(int(t.stride(0)), int(t.size(1)))
+
+
+def sketch_accumulate(X, dY, seed: int, r: int, S):
+    """S += (1/sqrt(r)) dY^T (X s^T) on the current stream; returns S.
+
+    X: (T, k) bf16, dY: (T, d) bf16, S: (d, r) float32 (updated in place).
+    """
+    import torch
+
+    lib = load_library()
+    _need(X, torch.bfloat16, "X")
+    _need(dY, torch.bfloat16, "dY")
+    _need(S, torch.float32, "S")
+    T, k = X.shape
+    if dY.size(0) != T:
+        raise ValueError("X and dY must have the same number of rows (tokens)")
+    d = dY.size(1)
+    if tuple(S.shape) != (d, r):
+        raise ValueError(f"S must be ({d}, {r}), got {tuple(S.shape)}")
+    _check(
+        lib.logra_sketch_accumulate(
+            X.data_ptr(), _ld(X), dY.data_ptr(), _ld(dY), T, k, d,
+            ctypes.c_uint64(seed & (2**64 - 1)), r, S.data_ptr(), _ld(S), _stream_handle(S),
+        )
+    )
+    return S
+
+
+def merge_update(W, U, seed: int, r: int, scale: float):
+    """W <- RNE_bf16(W - scale (1/sqrt(r)) U s) in place; returns W.
+
+    W: (d, k) bf16, U: (d, r) float32, scale = alpha * eta.
+    """
+    import torch
+
+    lib = load_library()
+    _need(W, torch.bfloat16, "W")
+    _need(U, torch.float32, "U")
+    d, k = W.shape
+    if tuple(U.shape) != (d, r):
+        raise ValueError(f"U must be ({d}, {r}), got {tuple(U.shape)}")
+    _check(
+        lib.logra_merge_update(
+            W.data_ptr(), _ld(W), U.data_ptr(), _ld(U), d, k,
+            ctypes.c_uint64(seed & (2**64 - 1)), r, float(scale), _stream_handle(W),
+        )
+    )
+    return W
+
+
+def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):
+    """RowAdam: S -> U in place, v (d,) float32 updated in place; returns S."""
+    import torch
+
+    lib = load_library()
+    _need(S, torch.float32, "S")
+    _need(v, torch.float32, "v", ndim=1)
+    d, r = S.shape
+    if v.numel() != d:
+        raise ValueError("v must have one value per row of S")
+    _check(lib.logra_rowadam_scale(S.data_ptr(), _ld(S), v.data_ptr(), d, r, int(step),
+                                   float(beta2), float(eps_rel), _stream_handle(S)))
+    return S
+
+
+def signs(seed: int, r: int, k: int, device="cuda"):
+    """The sign matrix s (r x k) as int8 +-1 (test and debugging aid)."""
+    import torch
+
+    lib = load_library()
+    out = torch.empty((r, k), dtype=torch.int8, device=device)
+    _check(lib.logra_signs(ctypes.c_uint64(seed & (2**64 - 1)), r, k, out.data_ptr() if k else None,
+                           _stream_handle(out)))
+    return out
+
+
+def workspace_bytes(T: int, r: int) -> int:
+    return int(load_library().logra_workspace_bytes(T, r))
+
+
+def abi_version() -> int:
+    return int(load_library().logra_abi_version())

@@ -1,0 +1,265 @@
+// C ABI of the LoGRA hot-path library: argument validation, per-stream
+// scratch, launch plans.  Declared in include/logra.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/logra.h"
+#include "logra_internal.h"
+
+namespace {
+
+using namespace logra;
+
+thread_local std::string g_last_error;
+
+logra_status fail(logra_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+logra_status hip_fail(hipError_t e, const char* what) {
+  return fail(LOGRA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
+}
+
+// Scratch per (device, purpose, stream).  It grows and never shrinks; before
+// it grows the stream is synchronised, so no queued kernel still uses the old
+// buffer.  New memory is zeroed (the sketch path keeps counters there that
+// must start at zero; its kernels leave them at zero).
+enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaMerge = 2 };
+struct Arena {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_arena_mu;
+std::map<std::pair<std::pair<int, int>, hipStream_t>, Arena> g_arenas;
+
+logra_status arena_get(int kind, hipStream_t stream, size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_arena_mu);
+  Arena& a = g_arenas[{{dev, kind}, stream}];
+  if (a.bytes < need) {
+    const char* fa = getenv("LOGRA_TEST_FAIL_ALLOC");
+    if (fa && fa[0] == '1') return fail(LOGRA_ERR_NOMEM, "scratch allocation refused (LOGRA_TEST_FAIL_ALLOC=1)");
+    if (a.ptr) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      e = hipFree(a.ptr);
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+      a.ptr = nullptr;
+      a.bytes = 0;
+    }
+    const size_t cap = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
+    e = hipMalloc(&a.ptr, cap);
+    if (e != hipSuccess) {
+      a.ptr = nullptr;
+      return fail(LOGRA_ERR_NOMEM, std::string("hipMalloc of scratch failed: ") + hipGetErrorString(e));
+    }
+    e = hipMemset(a.ptr, 0, cap);
+    if (e != hipSuccess) return hip_fail(e, "hipMemset");
+    a.bytes = cap;
+  }
+  *out = a.ptr;
+  return LOGRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T, int64_t k,
+                                     int64_t d, uint64_t seed, int32_t r, float* S, int64_t lds,
+                                     hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (T < 0 || k < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T, k and d must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
+    if (T == 0 || k == 0 || d == 0) return LOGRA_OK;
+    if (!X || !dY || !S) return fail(LOGRA_ERR_NULL, "X, dY and S must be non-null");
+    if (ldx < k) return fail(LOGRA_ERR_SHAPE, "ldx must be >= k");
+    if (lddy < d) return fail(LOGRA_ERR_SHAPE, "lddy must be >= d");
+    if (((uintptr_t)X & 15) || ((uintptr_t)dY & 15) || (ldx & 7) || (lddy & 7))
+      return fail(LOGRA_ERR_ALIGN, "X and dY need 16-byte aligned bases and row strides that are multiples of 8");
+    if ((uintptr_t)S & 3) return fail(LOGRA_ERR_ALIGN, "S must be 4-byte aligned");
+    const size_t sb = span_bytes(d, r, lds, 4);
+    if (overlaps(S, sb, X, span_bytes(T, k, ldx, 2)) || overlaps(S, sb, dY, span_bytes(T, d, lddy, 2)))
+      return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
+    if (T > ((int64_t)1 << 31) || k > ((int64_t)1 << 31) || d > ((int64_t)1 << 31))
+      return fail(LOGRA_ERR_SHAPE, "T, k and d must be below 2^31");
+
+    const SketchPlan pl = plan_sketch(T, k, d, r);
+    if ((size_t)pl.n_k * pl.Tpad * 16 * pl.NB * 4 > ((size_t)1 << 32) - 64)
+      return fail(LOGRA_ERR_SHAPE, "T too large for one call at this rank; split the microbatch");
+    void* ws = nullptr;
+    logra_status st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    if (st != LOGRA_OK) return st;
+    char* base = static_cast<char*>(ws);
+
+    ProjParams pp{};
+    pp.X = static_cast<const uint16_t*>(X);
+    pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
+    pp.n_tt = pl.n_tt; pp.n_k = pl.n_k; pp.cbs_per = pl.cbs_per; pp.ncb = pl.ncb;
+    pp.Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
+    pp.Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
+    pp.Ppart = reinterpret_cast<float*>(base + pl.off_part);
+    pp.part_stride = pl.Tpad * 16 * pl.NB;
+    pp.counters = reinterpret_cast<unsigned*>(base + pl.off_counters);
+    if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "projection launch");
+
+    ContractParams cp{};
+    cp.dY = static_cast<const uint16_t*>(dY);
+    cp.lddy = lddy; cp.T = T; cp.d = d;
+    cp.Phi = pp.Phi; cp.Plo = pp.Plo; cp.NB = pl.NB;
+    cp.S = S; cp.lds = lds; cp.r = r;
+    cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
+    cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
+    cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
+    if (!contract_launch(pl, cp, stream)) return fail(LOGRA_ERR_RANGE, "no contraction kernel for this tile");
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "contraction launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ldu, int64_t d, int64_t k,
+                                uint64_t seed, int32_t r, float scale, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "d and k must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (ldu < r) return fail(LOGRA_ERR_SHAPE, "ldu must be >= r");
+    if (d == 0 || k == 0) return LOGRA_OK;
+    if (!W || !U) return fail(LOGRA_ERR_NULL, "W and U must be non-null");
+    if (ldw < k) return fail(LOGRA_ERR_SHAPE, "ldw must be >= k");
+    if (((uintptr_t)W & 7) || (ldw & 3)) return fail(LOGRA_ERR_ALIGN, "W needs an 8-byte aligned base and ldw a multiple of 4");
+    if ((uintptr_t)U & 3) return fail(LOGRA_ERR_ALIGN, "U must be 4-byte aligned");
+    if (!isfinite(scale)) return fail(LOGRA_ERR_RANGE, "scale must be finite");
+    if (overlaps(W, span_bytes(d, k, ldw, 2), U, span_bytes(d, r, ldu, 4))) return fail(LOGRA_ERR_ALIAS, "W overlaps U");
+    if (d > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "d and k must be below 2^31");
+    if (scale == 0.0f) return LOGRA_OK;
+
+    const MergePlan pl = plan_merge(d, k, r);
+    void* ws = nullptr;
+    logra_status st = arena_get(kArenaMerge, stream, 2 * pl.u_bytes, &ws);
+    if (st != LOGRA_OK) return st;
+
+    USplitParams up{};
+    up.U = U; up.ldu = ldu; up.d = d; up.dpad = pl.dpad; up.r = r; up.KR = (r + 31) / 32 * 32;
+    up.Uhi = static_cast<uint16_t*>(ws);
+    up.Ulo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pl.u_bytes);
+
+    MergeParams mp{};
+    mp.W = static_cast<uint16_t*>(W);
+    mp.ldw = ldw; mp.d = d; mp.k = k; mp.Uhi = up.Uhi; mp.Ulo = up.Ulo; mp.seed = seed; mp.KR = up.KR;
+    mp.scale_eff = (float)((double)scale / sqrt((double)r));
+    mp.n_cb = pl.n_cb; mp.n_dt = pl.n_dt;
+    merge_launch(pl, up, mp, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int32_t r, int64_t step, float beta2,
+                                 float eps_rel, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (d < 0) return fail(LOGRA_ERR_SHAPE, "d must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
+    if (step < 1) return fail(LOGRA_ERR_RANGE, "step counts RowAdam updates and starts at 1");
+    if (!(beta2 >= 0.0f && beta2 < 1.0f)) return fail(LOGRA_ERR_RANGE, "beta2 must be in [0, 1)");
+    if (!(eps_rel >= 0.0f) || !isfinite(eps_rel)) return fail(LOGRA_ERR_RANGE, "eps_rel must be finite and >= 0");
+    if (d == 0) return LOGRA_OK;
+    if (!S || !v) return fail(LOGRA_ERR_NULL, "S and v must be non-null");
+    if (((uintptr_t)S & 3) || ((uintptr_t)v & 3)) return fail(LOGRA_ERR_ALIGN, "S and v must be 4-byte aligned");
+    if (overlaps(S, span_bytes(d, r, lds, 4), v, (size_t)d * 4)) return fail(LOGRA_ERR_ALIAS, "v overlaps S");
+
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t off_root = 0;
+    const size_t off_ssq = up((size_t)d * 4);
+    const size_t off_part = off_ssq + up((size_t)d * 4);
+    const size_t off_scal = off_part + up((size_t)2 * kRowAdamBlocks * 8);
+    const size_t total = off_scal + 256;
+    void* ws = nullptr;
+    logra_status st = arena_get(kArenaRowAdam, stream, total, &ws);
+    if (st != LOGRA_OK) return st;
+    char* base = static_cast<char*>(ws);
+    const double inv_bias = 1.0 / (1.0 - pow((double)beta2, (double)step));
+    rowadam_launch(S, lds, v, d, r, beta2, inv_bias, eps_rel, reinterpret_cast<float*>(base + off_root),
+                   reinterpret_cast<float*>(base + off_ssq), reinterpret_cast<double*>(base + off_part),
+                   reinterpret_cast<double*>(base + off_scal), stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "rowadam launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out, hipStream_t stream) {
+  g_last_error.clear();
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (k < 0) return fail(LOGRA_ERR_SHAPE, "k must be >= 0");
+  if (k == 0) return LOGRA_OK;
+  if (!out) return fail(LOGRA_ERR_NULL, "out must be non-null");
+  signs_launch(seed, r, k, out, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "signs launch");
+  return LOGRA_OK;
+}
+
+size_t logra_workspace_bytes(int64_t T, int32_t r) {
+  if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
+  // The largest plan over k and d for this T and r.
+  size_t best = 0;
+  for (int64_t k = 256; k <= ((int64_t)1 << 20); k *= 2) {
+    const SketchPlan pl = plan_sketch(T, k, 1 << 20, r);
+    if (pl.total > best) best = pl.total;
+  }
+  return best;
+}
+
+const char* logra_status_string(logra_status s) {
+  switch (s) {
+    case LOGRA_OK: return "ok";
+    case LOGRA_ERR_NULL: return "null pointer";
+    case LOGRA_ERR_SHAPE: return "bad shape";
+    case LOGRA_ERR_ALIGN: return "bad alignment";
+    case LOGRA_ERR_RANGE: return "argument out of range";
+    case LOGRA_ERR_ALIAS: return "overlapping buffers";
+    case LOGRA_ERR_HIP: return "HIP runtime error";
+    case LOGRA_ERR_NOMEM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+const char* logra_last_error(void) { return g_last_error.c_str(); }
+
+int logra_abi_version(void) { return LOGRA_ABI_VERSION; }
+
+}  // extern "C"

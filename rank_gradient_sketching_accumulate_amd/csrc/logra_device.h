@@ -1,0 +1,149 @@
+// Device helpers shared by the LoGRA kernels (gfx950 / CDNA4 only).
+//
+// Method: "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
+// Sketches", section 2.1 (equations 2-4).  The sign generator is this
+// library's own fixed choice (the paper asks only for independent random
+// signs regenerated from a seed, section 2.1 and section 2.2 "Memory and
+// synchronization"); it is Philox4x64-10 as defined by Salmon, Moraes, Dror
+// and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace logra {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// One wavefront is 64 lanes on CDNA.
+constexpr int kWave = 64;
+// Signs per Philox4x64 call (four 64-bit output words).
+constexpr int kSignBlock = 256;
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (SC'11, section 5): two 64x64->128 multiplies per round, key
+// bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+// Full 128-bit product of a and b from four 32x32->64 partial products; each
+// maps to one v_mad_u64_u32 with the carry folded into its addend.
+__device__ __forceinline__ void mul_wide64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t p01 = (uint64_t)a0 * b1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)a1 * b0 + (uint32_t)p01;
+  hi = (uint64_t)a1 * b1 + (p01 >> 32) + (p10 >> 32);
+  lo = (p10 << 32) | (uint32_t)p00;
+}
+
+// 256 sign bits of sign row `row`, columns [256*cblk, 256*cblk + 256):
+// Philox4x64-10(counter = (cblk, row, 0, 0), key = (seed, 0)).  Word q of the
+// output holds columns 64q .. 64q+63, least significant bit first; w[2q] is
+// the low half of word q.  Bit 1 means sign -1.
+__device__ __forceinline__ void philox_sign_block(uint64_t seed, uint32_t row, uint32_t cblk,
+                                                  uint32_t w[8]) {
+  uint64_t x0 = cblk, x1 = row, x2 = 0, x3 = 0;
+  uint64_t k0 = seed, k1 = 0;
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_wide64(kPhiloxM0, x0, hi0, lo0);
+    mul_wide64(kPhiloxM1, x2, hi1, lo1);
+    const uint64_t n0 = hi1 ^ x1 ^ k0;
+    const uint64_t n2 = hi0 ^ x3 ^ k1;
+    x0 = n0;
+    x1 = lo1;
+    x2 = n2;
+    x3 = lo0;
+  }
+  w[0] = (uint32_t)x0; w[1] = (uint32_t)(x0 >> 32);
+  w[2] = (uint32_t)x1; w[3] = (uint32_t)(x1 >> 32);
+  w[4] = (uint32_t)x2; w[5] = (uint32_t)(x2 >> 32);
+  w[6] = (uint32_t)x3; w[7] = (uint32_t)(x3 >> 32);
+}
+
+// Eight sign bits (bit e -> element e, 1 = negative) to eight bf16 values
+// +-1.0 packed two per dword, element 2q in the low half of dword q.  bf16
+// +1.0 is 0x3F80; the sign bit is bit 15 of each half.  The byte is copied
+// into both 16-bit halves, then one packed 16-bit shift per dword moves bit
+// 2q to bit 15 of the low half and bit 2q+1 to bit 15 of the high half.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_shl16(uint32_t x, unsigned short lo, unsigned short hi) {
+  const u16x2 v = __builtin_bit_cast(u16x2, x);
+  const u16x2 s = {lo, hi};
+  return __builtin_bit_cast(uint32_t, (u16x2)(v << s));
+}
+__device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t b) {
+  const uint32_t d = b * 0x00010001u;  // b < 256: byte in both halves
+  u32x4 o;
+  o[0] = (pk_shl16(d, 15, 14) & 0x80008000u) | 0x3F803F80u;
+  o[1] = (pk_shl16(d, 13, 12) & 0x80008000u) | 0x3F803F80u;
+  o[2] = (pk_shl16(d, 11, 10) & 0x80008000u) | 0x3F803F80u;
+  o[3] = (pk_shl16(d, 9, 8) & 0x80008000u) | 0x3F803F80u;
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer access with the agent-scope coherence bit (sc1): used for the
+// partial sums one workgroup hands to another inside a kernel, so that no
+// L2 write-back or invalidate of the whole cache is needed.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache-policy bit that sets sc1 on gfx950
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSc1);
+}
+__device__ __forceinline__ u32x4 load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+}
+// s_waitcnt vmcnt(0): every vector memory access of this wave has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// x = hi + lo + O(2^-17 |x|) with hi, lo bf16: the pair carries about 16
+// significant bits, so an MFMA over (hi, lo) reproduces fp32 operands to well
+// below the bf16 rounding error of a single operand.
+__device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16x32 bf16 -> fp32 (CDNA4).  Lane l = 16*g + i supplies
+//   A[i][k] and B[k][i] for the eight k in lane group g,
+// and receives D[4g + e][i], e = 0..3.  The kernels below always give A and B
+// the same (g, element) -> k assignment, so the reduction is right whatever
+// order the hardware walks k in.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+}  // namespace logra

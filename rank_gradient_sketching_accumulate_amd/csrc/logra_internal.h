@@ -1,0 +1,103 @@
+// Internal interface between the C ABI (logra_api.hip) and the kernel
+// translation units: parameter blocks, launch plans and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace logra {
+
+// ---------------------------------------------------------------------------
+// Sketch accumulation: projection P = X s^T, then S += (1/sqrt r) dY^T P.
+// ---------------------------------------------------------------------------
+struct ProjParams {
+  const uint16_t* X;
+  int64_t ldx, T, k;
+  uint64_t seed;
+  int r;
+  int n_tt;         // token tiles
+  int n_k;          // column splits across workgroups
+  int cbs_per;      // 256-column blocks per split
+  int ncb;          // 256-column blocks of k
+  uint16_t* Phi;    // P high halves, Pk order
+  uint16_t* Plo;    // P low halves, Pk order
+  float* Ppart;     // n_k fp32 partial sums, Pk order (n_k > 1 only)
+  int64_t part_stride;
+  unsigned* counters;  // one per token tile; zero between calls
+};
+
+struct ContractParams {
+  const uint16_t* dY;
+  int64_t lddy, T, d;
+  const uint16_t* Phi;
+  const uint16_t* Plo;
+  int NB;        // 16-column blocks in Pk
+  float* S;
+  int64_t lds;
+  int r;
+  float inv_sqrt_r;
+  int n_dt, n_ts;  // d tiles, token splits
+  int64_t ksp;     // 32-token steps per token split
+  int atomic_out;  // 1 when several workgroups add into the same S tile
+};
+
+struct SketchPlan {
+  int NB;                 // padded rank / 16 (power of two)
+  int MBW, WK;            // projection: 16-token blocks per wave, waves along k
+  int n_tt, n_k, cbs_per, ncb;
+  int64_t Tpad;
+  int cvar;               // contraction variant (see contract_launch)
+  int n_dt, n_ts;
+  int64_t ksp;
+  size_t off_counters, off_phi, off_plo, off_part, total;
+};
+
+SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r);
+bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s);
+bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Merge W <- RNE(W - scale_eff * U s).
+// ---------------------------------------------------------------------------
+struct USplitParams {
+  const float* U;
+  int64_t ldu, d;
+  int64_t dpad;     // rows written (multiple of 16, >= d); rows >= d are zero
+  int r, KR;        // rank, rank rounded up to 32
+  uint16_t* Uhi;    // Uk order, see merge_kernels.hip
+  uint16_t* Ulo;
+};
+
+struct MergeParams {
+  uint16_t* W;
+  int64_t ldw, d, k;
+  const uint16_t* Uhi;
+  const uint16_t* Ulo;
+  uint64_t seed;
+  int KR;
+  float scale_eff;
+  int n_cb, n_dt;
+};
+
+struct MergePlan {
+  int NBW;          // 16-row blocks per wave
+  int n_cb, n_dt;
+  int64_t dpad;
+  size_t u_bytes;   // scratch for the U hi/lo pair
+};
+
+MergePlan plan_merge(int64_t d, int64_t k, int r);
+bool merge_launch(const MergePlan& pl, const USplitParams& up, const MergeParams& mp, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// RowAdam and the sign dump.
+// ---------------------------------------------------------------------------
+constexpr int kRowAdamBlocks = 256;
+void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias,
+                    float eps_rel, float* root, float* ssq, double* partial, double* scal, hipStream_t s);
+void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s);
+
+int env_int(const char* name, int dflt);
+
+}  // namespace logra

@@ -1,0 +1,140 @@
+"""C-ABI checks that need no GPU.
+
+* liblogra.so loads and exports every function include/logra.h declares;
+* host-only entry points answer (version, status strings, workspace size);
+* argument validation rejects bad calls with the documented status before any
+  device work is enqueued (these calls return before touching HIP).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_gradient_sketching_accumulate_amd as lg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "logra.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_RANGE, ERR_ALIAS, ERR_HIP, ERR_NOMEM = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lg.LIB_PATH):
+        from rank_gradient_sketching_accumulate_amd.build import build_library
+
+        build_library()
+    return lg.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(logra_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(lg.EXPORTED_SYMBOLS) == _declared_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.logra_abi_version() == 1
+    for s in range(8):
+        assert lib.logra_status_string(s)
+    assert lib.logra_status_string(0) == b"ok"
+    assert lib.logra_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.logra_workspace_bytes(0, 64) == 0
+    assert lib.logra_workspace_bytes(4096, 0) == 0
+    a = lib.logra_workspace_bytes(4096, 64)
+    b = lib.logra_workspace_bytes(8192, 64)
+    # P as a bf16 hi/lo pair: 4 bytes per (token, rank) at least
+    assert a >= 4096 * 64 * 4 and b > a
+
+
+FAKE = 0x10000  # a well-aligned non-null address; never dereferenced on these paths
+
+
+def _sketch(lib, X=FAKE, ldx=512, dY=FAKE * 64, lddy=256, T=16, k=512, d=256, r=16, S=FAKE * 4096, lds=16):
+    return lib.logra_sketch_accumulate(X, ldx, dY, lddy, T, k, d, 0, r, S, lds, None)
+
+
+def test_sketch_validation(lib):
+    assert _sketch(lib, r=0) == ERR_RANGE
+    assert _sketch(lib, r=257) == ERR_RANGE
+    assert _sketch(lib, T=-1) == ERR_SHAPE
+    assert _sketch(lib, lds=8) == ERR_SHAPE
+    assert _sketch(lib, X=None) == ERR_NULL
+    assert b"non-null" in lib.logra_last_error()
+    assert _sketch(lib, ldx=500) == ERR_SHAPE
+    assert _sketch(lib, X=FAKE + 2) == ERR_ALIGN
+    assert _sketch(lib, ldx=516) == ERR_ALIGN
+    assert _sketch(lib, lddy=260) == ERR_ALIGN
+    assert _sketch(lib, S=FAKE + 2) == ERR_ALIGN
+    # S inside X's span
+    assert _sketch(lib, S=FAKE + 1024) == ERR_ALIAS
+    # empty problems are no-ops, even with null pointers
+    assert _sketch(lib, T=0, X=None, dY=None, S=None) == OK
+    assert _sketch(lib, k=0) == OK
+    assert _sketch(lib, d=0) == OK
+
+
+def _merge(lib, W=FAKE, ldw=512, U=FAKE * 64, ldu=16, d=256, k=512, r=16, scale=1e-3):
+    return lib.logra_merge_update(W, ldw, U, ldu, d, k, 0, r, ctypes.c_float(scale), None)
+
+
+def test_merge_validation(lib):
+    assert _merge(lib, r=0) == ERR_RANGE
+    assert _merge(lib, ldu=8) == ERR_SHAPE
+    assert _merge(lib, W=None) == ERR_NULL
+    assert _merge(lib, ldw=500) == ERR_SHAPE
+    assert _merge(lib, W=FAKE + 4) == ERR_ALIGN
+    assert _merge(lib, ldw=514) == ERR_ALIGN
+    assert _merge(lib, U=FAKE * 64 + 2) == ERR_ALIGN
+    assert _merge(lib, scale=float("inf")) == ERR_RANGE
+    assert _merge(lib, U=FAKE + 256) == ERR_ALIAS
+    assert _merge(lib, d=0) == OK
+    # scale 0 leaves W unchanged without any device work
+    assert _merge(lib, scale=0.0) == OK
+
+
+def _rowadam(lib, S=FAKE, lds=16, v=FAKE * 64, d=256, r=16, step=1, beta2=0.95, eps=1e-8):
+    return lib.logra_rowadam_scale(S, lds, v, d, r, step, ctypes.c_float(beta2), ctypes.c_float(eps), None)
+
+
+def test_rowadam_validation(lib):
+    assert _rowadam(lib, step=0) == ERR_RANGE
+    assert _rowadam(lib, beta2=1.0) == ERR_RANGE
+    assert _rowadam(lib, beta2=-0.1) == ERR_RANGE
+    assert _rowadam(lib, eps=-1.0) == ERR_RANGE
+    assert _rowadam(lib, S=None) == ERR_NULL
+    assert _rowadam(lib, lds=4) == ERR_SHAPE
+    assert _rowadam(lib, v=FAKE + 64) == ERR_ALIAS
+    assert _rowadam(lib, d=0) == OK
+
+
+def test_signs_validation(lib):
+    assert lib.logra_signs(0, 0, 10, FAKE, None) == ERR_RANGE
+    assert lib.logra_signs(0, 4, -1, FAKE, None) == ERR_SHAPE
+    assert lib.logra_signs(0, 4, 10, None, None) == ERR_NULL
+    assert lib.logra_signs(0, 4, 0, None, None) == OK
+
+
+def test_python_wrapper_type_checks(lib):
+    import torch
+
+    X = torch.zeros((4, 8), dtype=torch.bfloat16)
+    S = torch.zeros((4, 4), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        lg.sketch_accumulate(X, X, 0, 4, S)  # host tensors are refused
+    with pytest.raises(TypeError):
+        lg.sketch_accumulate(X.float(), X, 0, 4, S)

@@ -1,0 +1,414 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Every input is drawn once on the device by the seeded generators of
+``workloads`` and copied to the host for the oracle, so both sides consume
+identical bf16 values.  Sizes run from single elements through several
+tiles with ragged tails to the full workloads; at the largest sizes the
+oracle recomputes a seeded sample of rows of S (rows of S and of a plain
+merge are independent of each other).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests._util import (
+    assert_sketch_close,
+    assert_weight_close,
+    f64,
+    padded_ld,
+    rel_frob,
+    update_error_bound,
+)
+
+torch = pytest.importorskip("torch")
+lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _ragged_inputs(T, k, d, seed, sx=1.0, sdy=1e-2):
+    X = wl.gaussian_bf16((T, k), sx, seed, device=DEV, ld=padded_ld(k))
+    dY = wl.gaussian_bf16((T, d), sdy, seed + 1, device=DEV, ld=padded_ld(d))
+    return X, dY
+
+
+# ---------------------------------------------------------------------------
+# Signs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize(
+    "seed,r,k",
+    [(0, 16, 512), (1, 3, 700), (2**63 + 5, 5, 257), (42, 256, 1536), (7, 64, 33), (123, 1, 1), (9, 200, 5120)],
+)
+def test_signs_bit_exact(seed, r, k):
+    _say("signs", seed, r, k)
+    got = lg.signs(seed, r, k).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.sign_matrix(seed, r, k))
+
+
+# ---------------------------------------------------------------------------
+# Sketch accumulation
+# ---------------------------------------------------------------------------
+def _oracle_sketch(S0, Xs, dYs, seed, r, k, rows=None):
+    A = oracle.rademacher_projection(seed, r, k)
+    return oracle.sketch_accumulate(f64(S0), [f64(x) for x in Xs], [f64(y) for y in dYs], A, rows=rows)
+
+
+def test_sketch_tiny_workload():
+    w = wl.WORKLOADS["tiny"]
+    L = w.layers[0]
+    r = w.ranks[0]
+    seed = wl.sign_seed(0)
+    _say("tiny workload", L, r)
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    Xs, dYs = [], []
+    for m in range(w.M):
+        X, dY = wl.layer_inputs(w, 0, m, device=DEV)
+        Xs.append(X)
+        dYs.append(dY)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    ref = _oracle_sketch(torch.zeros_like(S), Xs, dYs, seed, r, L.k)
+    e = assert_sketch_close(f64(S), ref)
+    _say("tiny S rel err", e)
+
+
+@pytest.mark.parametrize(
+    "T,k,d,r",
+    [
+        (1, 8, 1, 1),
+        (33, 264, 17, 5),
+        (100, 700, 77, 40),
+        (257, 1000, 130, 16),
+        (500, 520, 300, 100),
+        (64, 256, 64, 256),
+        (2000, 300, 50, 128),
+        (96, 2056, 1100, 64),
+        (1500, 1536, 700, 256),
+    ],
+)
+def test_sketch_ragged(T, k, d, r):
+    _say("sketch ragged", T, k, d, r)
+    seed = 1000 + T + k
+    S = wl.random_tensor((d, r), seed + 7, device=DEV)
+    S0 = S.clone()
+    Xs, dYs = [], []
+    for m in range(2):
+        X, dY = _ragged_inputs(T, k, d, seed + 10 * m)
+        Xs.append(X)
+        dYs.append(dY)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    ref = _oracle_sketch(S0, Xs, dYs, seed, r, k)
+    # compare the accumulated increment, so the error is not diluted by S0
+    assert_sketch_close(f64(S) - f64(S0), ref - f64(S0))
+
+
+def test_sketch_attn1536_full():
+    """The 1.5B-class attention workload in full: 8 microbatches of 4096 tokens."""
+    w = wl.WORKLOADS["attn1536"]
+    L = w.layers[0]
+    r = w.ranks[0]
+    _say("attn1536 full", L, r)
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    G = np.zeros((L.d, L.k))
+    for m in range(w.M):
+        X, dY = wl.layer_inputs(w, 0, m, device=DEV)
+        lg.sketch_accumulate(X, dY, wl.sign_seed(0), r, S)
+        G += f64(dY).T @ f64(X)
+    ref = oracle.sketch_from_gradient(G, oracle.rademacher_projection(wl.sign_seed(0), r, L.k))
+    e = assert_sketch_close(f64(S), ref)
+    _say("attn1536 S rel err", e)
+
+
+def _sampled_rows(d, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(d, size=min(d, n), replace=False).tolist())
+    rows.update({0, d - 1})
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize(
+    "key,layer,r,M,heavy",
+    [
+        ("mlp1536", 0, 128, 2, False),
+        ("mlp1536", 1, 128, 1, False),
+        ("set7b", 2, 256, 1, False),
+        ("set7b", 3, 64, 1, False),
+        ("layer27b", 1, 256, 1, False),
+        ("layer27b", 0, 256, 1, True),
+    ],
+)
+def test_sketch_full_size_sampled_rows(key, layer, r, M, heavy):
+    """Full-size layers in the launch configuration the benchmark uses; the
+    oracle recomputes a seeded sample of rows of S."""
+    w = wl.WORKLOADS[key]
+    L = w.layers[layer]
+    seed = wl.sign_seed(layer)
+    _say("full size", key, L, r, M, "heavy" if heavy else "")
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    rows = _sampled_rows(L.d, 256, 17 + layer)
+    A = oracle.rademacher_projection(seed, r, L.k)
+    ref = np.zeros((len(rows), r))
+    for m in range(M):
+        X, dY = wl.layer_inputs(w, layer, m, device=DEV, heavy=heavy)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+        dYr = dY[:, torch.as_tensor(rows, device=DEV)]
+        ref += oracle.sketch_from_gradient(f64(dYr).T @ f64(X), A)
+        del X, dY, dYr
+    got = f64(S)[rows]
+    e = assert_sketch_close(got, ref)
+    _say("full size S rel err", e)
+
+
+PLAN_OVERRIDES = [
+    {},
+    {"LOGRA_PROJ_NK": 1},
+    {"LOGRA_PROJ_NK": 3},
+    {"LOGRA_PROJ_WK": 1, "LOGRA_PROJ_MB": 2},
+    {"LOGRA_PROJ_WK": 2, "LOGRA_PROJ_MB": 1, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_CON_TS": 1},
+    {"LOGRA_CON_TS": 7},
+]
+
+
+@pytest.mark.parametrize("r", [64, 128, 256])
+@pytest.mark.parametrize("env", PLAN_OVERRIDES, ids=lambda e: ",".join(f"{k[6:]}={v}" for k, v in e.items()) or "default")
+def test_sketch_launch_plans(r, env, monkeypatch):
+    """Every tiling the planner can pick (column splits across workgroups with
+    the last-arriver reduction, waves along k or tokens, token splits of the
+    contraction) gives the oracle's sketch."""
+    if r == 256 and env.get("LOGRA_PROJ_WK", 1) != 1:
+        pytest.skip("rank 256 runs with one wave column along k")
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    T, k, d = 700, 1300, 300
+    _say("plans", r, env)
+    X, dY = _ragged_inputs(T, k, d, 4242)
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    lg.sketch_accumulate(X, dY, 11, r, S)
+    ref = _oracle_sketch(torch.zeros((d, r)), [X], [dY], 11, r, k)
+    assert_sketch_close(f64(S), ref)
+
+
+def test_sketch_additivity_and_empty():
+    """M calls equal one call on the concatenated tokens (Algorithm 1 sums
+    microbatch contributions); empty calls leave S bitwise unchanged."""
+    T, k, d, r = 384, 768, 200, 64
+    seed = 5
+    parts = [_ragged_inputs(T, k, d, 300 + m) for m in range(3)]
+    S1 = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    for X, dY in parts:
+        lg.sketch_accumulate(X, dY, seed, r, S1)
+    Xc = torch.cat([p[0] for p in parts]).contiguous()
+    dYc = torch.cat([p[1] for p in parts]).contiguous()
+    S2 = torch.zeros_like(S1)
+    lg.sketch_accumulate(Xc, dYc, seed, r, S2)
+    assert rel_frob(f64(S1), f64(S2)) < 1e-5
+    before = S2.clone()
+    lg.sketch_accumulate(Xc[:0], dYc[:0], seed, r, S2)
+    lg.sketch_accumulate(Xc[:, :0], dYc, seed, r, S2)
+    torch.cuda.synchronize()
+    assert torch.equal(before, S2)
+
+
+def test_sketch_seed_changes_result():
+    T, k, d, r = 256, 512, 128, 16
+    X, dY = _ragged_inputs(T, k, d, 77)
+    S1 = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    S2 = torch.zeros_like(S1)
+    lg.sketch_accumulate(X, dY, 0, r, S1)
+    lg.sketch_accumulate(X, dY, 1, r, S2)
+    # same dense gradient, different projections: <G, S A> = ||S||^2 for both
+    G = f64(dY).T @ f64(X)
+    for seed, S in ((0, S1), (1, S2)):
+        A = oracle.rademacher_projection(seed, r, k)
+        Sg = f64(S)
+        assert math.isclose(float((G * (Sg @ A)).sum()), float((Sg * Sg).sum()), rel_tol=2e-4)
+    assert rel_frob(f64(S1), f64(S2)) > 0.5
+
+
+# ---------------------------------------------------------------------------
+# Merge
+# ---------------------------------------------------------------------------
+def _oracle_merge(W, U, seed, r, k, scale):
+    return oracle.merge_update(f64(W), f64(U), oracle.rademacher_projection(seed, r, k), scale)
+
+
+def test_merge_tiny_workload():
+    w = wl.WORKLOADS["tiny"]
+    L = w.layers[0]
+    r = w.ranks[0]
+    seed = wl.sign_seed(0)
+    _say("merge tiny")
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    for m in range(w.M):
+        X, dY = wl.layer_inputs(w, 0, m, device=DEV)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    W = wl.layer_weight(w, 0, device=DEV)
+    W0 = W.clone()
+    lg.merge_update(W, S, seed, r, w.scales[0])
+    ref = _oracle_merge(W0, S, seed, r, L.k, w.scales[0])
+    e, frac = assert_weight_close(f64(W), ref, bound=update_error_bound(f64(S), r, w.scales[0]))
+    _say("merge tiny rel err", e, "differing fraction", frac)
+    assert frac < 0.01
+    # the update is visible: W moved
+    assert not torch.equal(W, W0)
+
+
+@pytest.mark.parametrize(
+    "d,k,r",
+    [(1, 4, 1), (17, 260, 5), (130, 1000, 40), (64, 256, 256), (300, 516, 100), (1536, 1536, 64), (65, 2052, 128)],
+)
+def test_merge_ragged_and_zero_weight(d, k, r):
+    _say("merge", d, k, r)
+    seed = 31 + d + k
+    U = wl.random_tensor((d, r), seed, device=DEV, std=3.0)
+    scale = 1e-2
+    # W = 0 isolates the low-rank update: W' = -RNE(c U A)
+    W = torch.zeros((d, padded_ld(k, 4)), dtype=torch.bfloat16, device=DEV)[:, :k]
+    lg.merge_update(W, U, seed, r, scale)
+    ref = _oracle_merge(torch.zeros((d, k)), U, seed, r, k, scale)
+    assert_weight_close(f64(W), ref, what="dW", bound=update_error_bound(f64(U), r, scale))
+    # and on a real weight
+    W = wl.gaussian_bf16((d, k), 0.02, seed + 1, device=DEV, ld=padded_ld(k, 4))
+    W0 = W.clone()
+    lg.merge_update(W, U, seed, r, 1e-4)
+    assert_weight_close(f64(W), _oracle_merge(W0, U, seed, r, k, 1e-4), bound=update_error_bound(f64(U), r, 1e-4))
+
+
+def test_merge_scale_zero_and_zero_sketch_identity():
+    d, k, r = 200, 700, 32
+    W = wl.gaussian_bf16((d, k), 0.02, 3, device=DEV, ld=704)
+    W0 = W.clone()
+    U = wl.random_tensor((d, r), 4, device=DEV)
+    lg.merge_update(W, U, 9, r, 0.0)
+    lg.merge_update(W, torch.zeros_like(U), 9, r, 1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(W, W0)
+
+
+def test_merge_linearity():
+    d, k, r = 256, 1024, 64
+    U = wl.random_tensor((d, r), 12, device=DEV)
+    W1 = torch.zeros((d, k), dtype=torch.bfloat16, device=DEV)
+    W2 = torch.zeros_like(W1)
+    lg.merge_update(W1, U, 3, r, 2.0**-6)
+    lg.merge_update(W2, U, 3, r, 2.0**-5)
+    # a power-of-two scale only moves the exponent: exactly twice, bit for bit
+    torch.cuda.synchronize()
+    assert torch.equal(W2.float(), 2 * W1.float())
+
+
+@pytest.mark.parametrize("key,layer", [("layer27b", 0), ("set7b", 2)])
+def test_merge_full_size_sampled_rows(key, layer):
+    w = wl.WORKLOADS[key]
+    L = w.layers[layer]
+    r = 256
+    seed = wl.sign_seed(layer)
+    _say("merge full size", key, L)
+    U = wl.random_tensor((L.d, r), 99 + layer, device=DEV, std=50.0)
+    rows = _sampled_rows(L.d, 64, 5 + layer)
+    A = oracle.rademacher_projection(seed, r, L.k)
+    Ur = f64(U)[rows]
+    for scale in w.scales:
+        W = wl.layer_weight(w, layer, device=DEV)
+        Wr = f64(W)[rows]
+        lg.merge_update(W, U, seed, r, scale)
+        assert_weight_close(f64(W)[rows], oracle.merge_update(Wr, Ur, A, scale),
+                            bound=update_error_bound(Ur, r, scale))
+        del W
+
+
+# ---------------------------------------------------------------------------
+# RowAdam
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("beta2", [0.95, 0.999])
+@pytest.mark.parametrize("d,r", [(256, 16), (3584, 64), (1000, 100), (7, 256)])
+def test_rowadam_three_steps(beta2, d, r):
+    _say("rowadam", d, r, beta2)
+    v = torch.zeros(d, dtype=torch.float32, device=DEV)
+    v_ref = np.zeros(d)
+    for t in range(1, 4):
+        S = wl.random_tensor((d, r), 500 + t + d, device=DEV) * torch.logspace(
+            -2, 2, d, device=DEV
+        ).unsqueeze(1)
+        S_in = f64(S)
+        lg.rowadam_scale(S, v, t, beta2, 1e-8)
+        # the library takes beta2 and eps_rel as float32: give the oracle the same values
+        U_ref, v_ref = oracle.rowadam_scale(S_in, v_ref, t, float(np.float32(beta2)), float(np.float32(1e-8)))
+        assert_sketch_close(f64(S), U_ref, what=f"U step {t}")
+        assert rel_frob(f64(v), v_ref) < 1e-5
+        # Frobenius norm of the sketch is preserved
+        assert math.isclose(float(np.linalg.norm(f64(S))), float(np.linalg.norm(S_in)), rel_tol=1e-5)
+
+
+def test_rowadam_zero_sketch_gives_zero_update():
+    d, r = 300, 32
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    v = torch.rand(d, device=DEV)
+    lg.rowadam_scale(S, v, 2, 0.95, 1e-8)
+    torch.cuda.synchronize()
+    assert not S.any()
+
+
+# ---------------------------------------------------------------------------
+# Whole step on the small workload: sketch, RowAdam, merge.
+# ---------------------------------------------------------------------------
+def test_full_step_tiny_with_rowadam():
+    w = wl.WORKLOADS["tiny"]
+    L = w.layers[0]
+    r = w.ranks[0]
+    seed = wl.sign_seed(0)
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    Xs, dYs = [], []
+    for m in range(w.M):
+        X, dY = wl.layer_inputs(w, 0, m, device=DEV)
+        Xs.append(X)
+        dYs.append(dY)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    v = torch.zeros(L.d, dtype=torch.float32, device=DEV)
+    lg.rowadam_scale(S, v, 1, 0.999, 1e-8)
+    W = wl.layer_weight(w, 0, device=DEV)
+    W0 = W.clone()
+    lg.merge_update(W, S, seed, r, w.scales[0])
+    S_ref = _oracle_sketch(torch.zeros((L.d, r)), Xs, dYs, seed, r, L.k)
+    U_ref, _ = oracle.rowadam_scale(S_ref, np.zeros(L.d), 1, float(np.float32(0.999)), float(np.float32(1e-8)))
+    assert_sketch_close(f64(S), U_ref, what="U")
+    W_ref = oracle.merge_update(f64(W0), U_ref, oracle.rademacher_projection(seed, r, L.k), w.scales[0])
+    assert_weight_close(f64(W), W_ref, bound=update_error_bound(U_ref, r, w.scales[0]))
+
+
+# ---------------------------------------------------------------------------
+# Error paths with real device buffers
+# ---------------------------------------------------------------------------
+def test_errors_on_device_buffers():
+    X, dY = _ragged_inputs(64, 256, 64, 1)
+    S = torch.zeros((64, 16), dtype=torch.float32, device=DEV)
+    with pytest.raises(lg.LograError) as ei:
+        lg.sketch_accumulate(X[:, 1:], dY, 0, 16, S)  # misaligned base
+    assert ei.value.status == 3
+    buf = torch.zeros(64 * 256, dtype=torch.bfloat16, device=DEV)
+    Xa = buf.view(64, 256)
+    Sa = buf[: 2 * 64 * 16].view(torch.float32).view(64, 16)  # S overlapping X
+    with pytest.raises(lg.LograError) as ei:
+        lg.sketch_accumulate(Xa, dY, 0, 16, Sa)
+    assert ei.value.status == 5
+    with pytest.raises(lg.LograError):
+        lg.sketch_accumulate(X, dY, 0, 300, torch.zeros((64, 300), device=DEV))
