@@ -75,7 +75,9 @@ typedef enum {
  *        of 8.
  *   S    fp32, d x r, row stride lds >= r, read and written.  Must not overlap
  *        X or dY.
- *   T, k, d >= 0; T == 0, k == 0 or d == 0 leaves S unchanged.
+ *   T, k, d >= 0; T == 0, k == 0 or d == 0 leaves S unchanged.  X and dY
+ *   must each span less than 4 GiB (split larger microbatches into several
+ *   calls: the sketch is additive over tokens).
  *
  * Internal scratch (the projected inputs P = X s^T, T x r) is held by the
  * library per (device, stream) and grown on first use of a larger size;

@@ -106,6 +106,11 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
       return fail(LOGRA_ERR_SHAPE, "T, k and d must be below 2^31");
 
     const SketchPlan pl = plan_sketch(T, k, d, r);
+    // Kernels address X and dY through buffer descriptors with 32-bit byte
+    // offsets (rows past T read as zero): each operand must span < 4 GiB.
+    const uint64_t lim = ((uint64_t)1 << 32) - 4096;
+    if ((uint64_t)(pl.Tpad + 32) * (uint64_t)ldx * 2 >= lim || (uint64_t)(pl.Tpad + 32) * (uint64_t)lddy * 2 >= lim)
+      return fail(LOGRA_ERR_SHAPE, "X or dY spans 4 GiB or more; split the microbatch into several calls");
     if ((size_t)pl.n_k * pl.Tpad * 16 * pl.NB * 4 > ((size_t)1 << 32) - 64)
       return fail(LOGRA_ERR_SHAPE, "T too large for one call at this rank; split the microbatch");
     void* ws = nullptr;

@@ -95,6 +95,28 @@ __device__ __forceinline__ u32x4 signs_to_bf16x8(uint32_t b) {
   return o;
 }
 
+// The same expansion for lane group g straight from a dword holding four
+// sign bytes (byte g is this lane's): one v_perm copies byte g into both
+// 16-bit halves, then per output dword one packed shift and one and-or with
+// the +1.0 pattern kept in a register.
+struct SignExpander {
+  uint32_t sel;  // v_perm selector: byte g -> bytes 0 and 2, zero elsewhere
+  uint32_t one;  // 0x3F803F80 (two bf16 +1.0), held in a VGPR
+  __device__ __forceinline__ explicit SignExpander(int g) {
+    sel = 0x0C000C00u | ((uint32_t)g << 16) | (uint32_t)g;
+    asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(one));
+  }
+  __device__ __forceinline__ u32x4 operator()(uint32_t dw) const {
+    const uint32_t d = __builtin_amdgcn_perm(0u, dw, sel);
+    u32x4 o;
+    o[0] = (pk_shl16(d, 15, 14) & 0x80008000u) | one;
+    o[1] = (pk_shl16(d, 13, 12) & 0x80008000u) | one;
+    o[2] = (pk_shl16(d, 11, 10) & 0x80008000u) | one;
+    o[3] = (pk_shl16(d, 9, 8) & 0x80008000u) | one;
+    return o;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Raw buffer access with the agent-scope coherence bit (sc1): used for the
 // partial sums one workgroup hands to another inside a kernel, so that no
@@ -110,6 +132,14 @@ __device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ u32x4 load16_agent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
 }
+// Plain raw-buffer loads: SGPR base + 32-bit byte offset; offsets past the
+// descriptor's size read as zero (used for rows beyond the matrix).
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 // s_waitcnt vmcnt(0): every vector memory access of this wave has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -118,20 +148,28 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round to nearest, ties to even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Round to nearest, ties to even (v_cvt_pk_bf16_f32; NaN stays NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // x = hi + lo + O(2^-17 |x|) with hi, lo bf16: the pair carries about 16
 // significant bits, so an MFMA over (hi, lo) reproduces fp32 operands to well
-// below the bf16 rounding error of a single operand.
+// below the bf16 rounding error of a single operand.  Two values per call:
+// hi and lo come back packed (value a in the low half).
+__device__ __forceinline__ void split_hi_lo2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  const float ah = __uint_as_float(hi << 16), bh = __uint_as_float(hi & 0xffff0000u);
+  lo = pack_bf16x2(a - ah, b - bh);
+}
 __device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_rne(x);
-  lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+  uint32_t h, l;
+  split_hi_lo2(x, 0.f, h, l);
+  hi = h & 0xffffu;
+  lo = l & 0xffffu;
 }
 
 // ---------------------------------------------------------------------------

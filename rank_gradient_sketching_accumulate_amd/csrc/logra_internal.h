@@ -44,6 +44,7 @@ struct ContractParams {
 
 struct SketchPlan {
   int NB;                 // padded rank / 16 (power of two)
+  int small_proj;         // 1: proj_small_kernel (all signs of k in LDS)
   int MBW, WK;            // projection: 16-token blocks per wave, waves along k
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;

@@ -43,11 +43,10 @@ __global__ __launch_bounds__(256) void usplit_kernel(USplitParams p) {
     u32x4 hv, lv;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t h0, l0, h1, l1;
-      split_hi_lo(u[2 * q], h0, l0);
-      split_hi_lo(u[2 * q + 1], h1, l1);
-      hv[q] = h0 | (h1 << 16);
-      lv[q] = l0 | (l1 << 16);
+      uint32_t h, l;
+      split_hi_lo2(u[2 * q], u[2 * q + 1], h, l);
+      hv[q] = h;
+      lv[q] = l;
     }
     *reinterpret_cast<u32x4*>(p.Uhi + id * 8) = hv;
     *reinterpret_cast<u32x4*>(p.Ulo + id * 8) = lv;
@@ -115,12 +114,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   __syncthreads();
 
   // Wave w expands column blocks 4w .. 4w+3 of K step kk into stage buf.
+  const SignExpander ex(g);
   auto expand = [&](int kk, int buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int mb = 4 * wave + q;
-      const uint32_t dw = colbits[(16 * mb + i) * STR + kk];
-      sgn[buf][mb * 64 + lane] = signs_to_bf16x8((dw >> (8 * g)) & 0xffu);
+      sgn[buf][mb * 64 + lane] = ex(colbits[(16 * mb + i) * STR + kk]);
     }
   };
 
@@ -186,13 +185,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) wb[e] = (col + e < p.k) ? dst[e] : 0u;
       }
-      uint32_t h[4];
+      float nw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        h[e] = f32_to_bf16_rne(__fmaf_rn(-p.scale_eff, acc[mb][nb][e], bf16_to_f32(wb[e])));
+      for (int e = 0; e < 4; ++e) nw[e] = __fmaf_rn(-p.scale_eff, acc[mb][nb][e], bf16_to_f32(wb[e]));
+      const uint32_t p01 = pack_bf16x2(nw[0], nw[1]), p23 = pack_bf16x2(nw[2], nw[3]);
       if (full) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *reinterpret_cast<u32x2*>(dst) = u32x2{p01, p23};
       } else {
+        const uint32_t h[4] = {p01 & 0xffffu, p01 >> 16, p23 & 0xffffu, p23 >> 16};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (col + e < p.k) dst[e] = (uint16_t)h[e];

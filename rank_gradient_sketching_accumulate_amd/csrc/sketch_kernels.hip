@@ -49,6 +49,135 @@ __device__ __forceinline__ u32x4 load_x8(const uint16_t* X, int64_t ldx, int64_t
 }
 
 // ===========================================================================
+// Projection for small r*k (the signs of the whole k range fit in LDS).
+// A workgroup of eight waves owns TT = 16*MBW tokens; the waves split the
+// 32-column steps of k evenly.  Every wave issues its X loads first (a ring
+// of eight steps), then the workgroup regenerates all sign blocks once, then
+// each wave multiplies its steps, and the eight column partials are summed
+// through LDS.
+// ===========================================================================
+template <int NB, int MBW>
+__global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
+  constexpr int RP = 16 * NB;
+  constexpr int NW = 8;
+  constexpr int TT = 16 * MBW;
+  constexpr int SROW = 9;
+  extern __shared__ uint32_t lds[];
+
+  const int tt = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t t0 = (int64_t)tt * TT;
+  const int nks = (int)((p.k + 31) >> 5);
+  const int q = (nks + NW - 1) / NW;
+  const int ks0 = w * q;
+  const int nloc = max(0, min(nks, ks0 + q) - ks0);
+
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
+  uint32_t rowoff[MBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) rowoff[mb] = (uint32_t)((t0 + 16 * mb + i) * p.ldx * 2);
+
+  f32x4 acc[MBW][NB];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xr[8][MBW];
+  auto issue = [&](u32x4 (&slot)[MBW], int j) {
+    const int64_t col = (int64_t)(ks0 + j) * 32 + 8 * g;
+#pragma unroll
+    for (int mb = 0; mb < MBW; ++mb) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < nloc) {
+        v = buf_load16(rx, rowoff[mb] + (uint32_t)(col * 2));
+        if (col + 8 > p.k) {  // last step of a k that is not a multiple of 32
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e >= p.k) v[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+      }
+      slot[mb] = v;
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 7; ++j) issue(xr[j], j);
+
+  for (int b = threadIdx.x; b < RP * p.ncb; b += NW * 64) {
+    const int row = b % RP, cb = b / RP;
+    uint32_t wd[8];
+    philox_sign_block(p.seed, (uint32_t)row, (uint32_t)cb, wd);
+    uint32_t* dst = lds + (cb * RP + row) * SROW;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = wd[e];
+  }
+  __syncthreads();
+
+  const SignExpander ex(g);
+  for (int j0 = 0; j0 < nloc; j0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      if (j < nloc) {
+        issue(xr[(u + 7) & 7], j + 7);
+        const int ks = ks0 + j;
+        const uint32_t* sb = lds + ((ks >> 3) * RP + i) * SROW + (ks & 7);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const u32x4 bsg = ex(sb[16 * nb * SROW]);
+#pragma unroll
+          for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma_16x16x32(xr[u][mb], bsg, acc[mb][nb]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    if (16 * nb + i >= p.r)
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Eight-way sum of the column partials, one 16-token block at a time:
+  // every wave parks its partial in LDS, then each thread sums four
+  // consecutive tokens of one column and writes their hi/lo pair.
+  constexpr int CH = NB * 256;
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) {
+    __syncthreads();
+    float* mine = red + w * CH;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[mb][nb][e];
+    __syncthreads();
+    for (int v = threadIdx.x; v < CH / 4; v += NW * 64) {
+      const int ln = v & 63, nb = v >> 6;  // lane (g, i) of wave 0's layout, column block
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < NW; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += red[q * CH + (nb * 4 + e) * 64 + ln];
+      const int gg = ln >> 4, ii = ln & 15;
+      const int64_t e0 = pk_index(t0 + 16 * mb + 4 * gg, 16 * nb + ii, NB);
+      uint32_t h0, l0, h1, l1;
+      split_hi_lo2(sum[0], sum[1], h0, l0);
+      split_hi_lo2(sum[2], sum[3], h1, l1);
+      *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
+    }
+  }
+}
+
+size_t proj_small_lds_bytes(int NB, int ncb) {
+  const size_t signs = (size_t)16 * NB * ncb * 9 * 4;
+  const size_t red = (size_t)8 * NB * 256 * 4;
+  return signs > red ? signs : red;
+}
+
+// ===========================================================================
 // Projection.  A workgroup owns TT = (4/WK)*16*MBW tokens and the 256-column
 // blocks [cbb, cbe) of k.  Its WK wave columns take the blocks of one "round"
 // side by side; the 4/WK wave rows take different tokens.  Each round the
@@ -128,6 +257,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
     if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
     const int cb = cbb + j * WK + wk;
     const uint32_t* sb = &sbits[buf][(wk * RP + i) * SROW];
+    const SignExpander ex(g);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       if (s == 0)
@@ -137,8 +267,7 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
       if (cb < cbe) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t dw = sb[16 * nb * SROW + s];
-          const u32x4 bsg = signs_to_bf16x8((dw >> (8 * g)) & 0xffu);
+          const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = mfma_16x16x32(xr[s][mb], bsg, acc[mb][nb]);
         }
@@ -187,11 +316,11 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int64_t e0 = pk_index(tw + 16 * mb + 4 * g, 16 * nb + i, NB);
-          uint32_t h[4], l[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) split_hi_lo(acc[mb][nb][e], h[e], l[e]);
-          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-          *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+          uint32_t h0, l0, h1, l1;
+          split_hi_lo2(acc[mb][nb][0], acc[mb][nb][1], h0, l0);
+          split_hi_lo2(acc[mb][nb][2], acc[mb][nb][3], h1, l1);
+          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+          *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
         }
     }
     return;
@@ -230,11 +359,11 @@ __global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
       const uint32_t off = (uint32_t)(((int64_t)sp * p.part_stride + e0) * 4);
       sum += __builtin_bit_cast(f32x4, load16_agent(rs, off));
     }
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split_hi_lo(sum[e], h[e], l[e]);
-    *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    uint32_t h0, l0, h1, l1;
+    split_hi_lo2(sum[0], sum[1], h0, l0);
+    split_hi_lo2(sum[2], sum[3], h1, l1);
+    *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+    *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
   }
   if (threadIdx.x == 0) p.counters[tt] = 0u;
 }
@@ -300,27 +429,35 @@ __device__ __forceinline__ void store_s_tile(const ContractParams& p, f32x4 (&ac
     }
 }
 
-// Small ranks (NB <= 4): the four waves of a workgroup share 64 rows of S and
-// take every fourth 32-token step of the workgroup's token range.  Each wave
-// keeps three steps of dY and one step of P in flight.
-template <int NB>
-__global__ __launch_bounds__(256) void contract_small_kernel(ContractParams p) {
-  constexpr int WT = 4;
-  __shared__ float red[(WT - 1) * NB * 256];
+// Small ranks (NB <= 4): eight waves share 64 rows of S and take every
+// eighth 32-token step of the workgroup's token range.  A step's dY rows and
+// P words travel together in one ring slot (DEPTH steps in flight), so waiting
+// for one step never waits for a later one.  dY comes through a buffer
+// descriptor: token rows past T read as zero; columns past d only feed rows
+// of S that are not stored.
+template <int NB, int DEPTH>
+__global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
+  constexpr int NW = 8;
+  constexpr int CH = NB * 256;  // floats of one 16-row block of the tile
+  __shared__ float red[NW * CH];
+  // Token splits vary fastest among consecutive logical ids, so the
+  // workgroups that add into the same S tile share an XCD (and its L2).
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int ts = lin / p.n_dt;
-  const int dt = lin - ts * p.n_dt;
-  if (ts >= p.n_ts) return;
+  const int dt = lin / p.n_ts;
+  const int ts = lin - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
 
   const int lane = threadIdx.x & 63, wt = threadIdx.x >> 6;
   const int g = lane >> 4, i = lane & 15;
   const int64_t d0w = (int64_t)dt * 16 * kDC;
-  const int64_t col = d0w + kDC * i;
+  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
   const int64_t nks = (p.T + 31) >> 5;
   const int64_t ks_beg = ts * p.ksp;
   const int64_t ks_end = min(nks, ks_beg + p.ksp);
   const int64_t ks0 = ks_beg + wt;
-  const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + WT - 1) / WT) : 0;
+  const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + NW - 1) / NW) : 0;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+  const uint32_t rowstep = (uint32_t)(p.lddy * 2);
 
   f32x4 acc[kDC][NB];
 #pragma unroll
@@ -328,72 +465,76 @@ __global__ __launch_bounds__(256) void contract_small_kernel(ContractParams p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x2 y[4][8];
-  u32x4 bh[2][NB], bl[2][NB];
-  auto load_y = [&](u32x2 (&slot)[8], int m) {
-    const int64_t t = 32 * (ks0 + (int64_t)WT * m) + 8 * g;
+  u32x2 y[DEPTH][8];
+  u32x4 bh[DEPTH][NB], bl[DEPTH][NB];
+  auto issue = [&](int slot_y, int m) {
+    if (m >= nsteps) return;
+    const int64_t ks = ks0 + (int64_t)NW * m;
+    uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) slot[e] = load_dy4(p.dY, p.lddy, p.T, p.d, t + e, col);
-  };
-  auto load_b = [&](u32x4 (&h)[NB], u32x4 (&l)[NB], int m) {
-    const int64_t ks = ks0 + (int64_t)WT * m;
+    for (int e = 0; e < 8; ++e) {
+      y[slot_y][e] = buf_load8(ry, off);
+      off += rowstep;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int64_t off = ((ks * p.NB + nb) * 64 + lane) * 8;
-      h[nb] = *reinterpret_cast<const u32x4*>(p.Phi + off);
-      l[nb] = *reinterpret_cast<const u32x4*>(p.Plo + off);
+      const int64_t o = ((ks * p.NB + nb) * 64 + lane) * 8;
+      bh[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
+      bl[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
     }
   };
 
 #pragma unroll
-  for (int q = 0; q < 3; ++q)
-    if (q < nsteps) load_y(y[q], q);
-  if (nsteps > 0) load_b(bh[0], bl[0], 0);
-
-  for (int m0 = 0; m0 < nsteps; m0 += 4) {
+  for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
+  for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < DEPTH; ++u) {
       const int m = m0 + u;
       if (m < nsteps) {
-        if (m + 3 < nsteps) load_y(y[(u + 3) & 3], m + 3);
-        if (m + 1 < nsteps) load_b(bh[(u + 1) & 1], bl[(u + 1) & 1], m + 1);
+        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
         u32x4 a[kDC];
         transpose_dy(y[u], a);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int c = 0; c < kDC; ++c) {
-            acc[c][nb] = mfma_16x16x32(a[c], bh[u & 1][nb], acc[c][nb]);
-            acc[c][nb] = mfma_16x16x32(a[c], bl[u & 1][nb], acc[c][nb]);
+            acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
+            acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
           }
       }
     }
   }
 
-  // Sum the four waves' partials through LDS, one 16-row block at a time.
+  // Eight-way sum through LDS, one 16-row block (c) at a time: every wave
+  // parks its partial, then each wave sums and stores one eighth of the block.
 #pragma unroll
   for (int c = 0; c < kDC; ++c) {
-    if (wt > 0) {
-      float* dst = red + (wt - 1) * NB * 256;
+    float* mine = red + wt * CH;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(nb * 4 + e) * 64 + lane] = acc[c][nb][e];
-    }
+      for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[c][nb][e];
     __syncthreads();
-    if (wt == 0) {
+    for (int v = threadIdx.x; v < CH; v += NW * 64) {
+      float sum = 0.f;
 #pragma unroll
-      for (int w = 1; w < WT; ++w) {
-        const float* src = red + (w - 1) * NB * 256;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[c][nb][e] += src[(nb * 4 + e) * 64 + lane];
+      for (int q = 0; q < NW; ++q) sum += red[q * CH + v];
+      const int ln = v & 63, ne = v >> 6;  // lane and (nb*4 + e) of the element
+      const int nb = ne >> 2, e = ne & 3;
+      const int gg = ln >> 4, ii = ln & 15;
+      const int cc = 16 * nb + ii;
+      const int64_t row = d0w + (int64_t)kDC * (4 * gg + e) + c;
+      if (cc < p.r && row < p.d) {
+        float* dst = p.S + row * p.lds + cc;
+        const float val = sum * p.inv_sqrt_r;
+        if (p.atomic_out)
+          atomicAdd(dst, val);
+        else
+          *dst += val;
       }
     }
     __syncthreads();
   }
-  if (wt == 0) store_s_tile<NB>(p, acc, d0w, 0, g, i);
 }
 
 // Larger ranks (NB = 8 or 16): waves split the rows (WM) and the columns (WN)
@@ -510,53 +651,71 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   pl.NB = pow2_blocks(r);
   const int RP = 16 * pl.NB;
   pl.ncb = (int)((k + 255) / 256);
-
-  // Projection: waves along k (WK) so that RP*WK <= 256 sign blocks per round;
-  // MBW keeps the accumulators within 128 registers.
-  int WK = RP >= 256 ? 1 : (RP >= 128 ? 2 : 4);
-  if (WK > pl.ncb) WK = pl.ncb >= 2 ? 2 : 1;
-  int MBW = 32 / pl.NB;
-  if (MBW > 4) MBW = 4;
-  if (MBW < 1) MBW = 1;
-  // Fewer tokens per workgroup while that still leaves < 2 workgroups per CU.
-  auto tiles = [&](int mbw, int wk) { return (T + (4 / wk) * 16 * mbw - 1) / ((4 / wk) * 16 * mbw); };
-  while (MBW > 1 && tiles(MBW, WK) < 512) MBW >>= 1;
-  MBW = env_int("LOGRA_PROJ_MB", MBW);
-  WK = env_int("LOGRA_PROJ_WK", WK);
-  pl.MBW = MBW;
-  pl.WK = WK;
-  const int64_t TT = (4 / WK) * 16 * MBW;
-  // The contraction reads whole 32-token steps of P: cover them all, so the
-  // tokens in [T, Tpad) hold P = 0 written by the projection (X reads as 0).
   const int64_t T32 = (T + 31) / 32 * 32;
-  pl.n_tt = (int)((T32 + TT - 1) / TT);
+
+  // Projection.  Small r*k: the whole k range's signs fit in 64 KB of LDS.
+  pl.small_proj = ((size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
+  pl.small_proj = env_int("LOGRA_PROJ_SMALL", pl.small_proj);
+  int64_t TT;
+  if (pl.small_proj) {
+    // More tokens per workgroup amortise the signs; keep >= 256 workgroups.
+    int MBW = 4;
+    while (MBW > 1 && (MBW * pl.NB > 16 || (T32 + 16 * MBW - 1) / (16 * MBW) < 256)) MBW >>= 1;
+    MBW = env_int("LOGRA_PROJ_MB", MBW);
+    pl.MBW = MBW;
+    pl.WK = 8;
+    TT = 16 * MBW;
+    pl.n_tt = (int)((T32 + TT - 1) / TT);
+    pl.n_k = 1;
+    pl.cbs_per = pl.ncb;
+  } else {
+    // Waves along k (WK) so that RP*WK <= 256 sign blocks per round; MBW keeps
+    // the accumulators within 128 registers.
+    int WK = RP >= 256 ? 1 : (RP >= 128 ? 2 : 4);
+    if (WK > pl.ncb) WK = pl.ncb >= 2 ? 2 : 1;
+    int MBW = 32 / pl.NB;
+    if (MBW > 4) MBW = 4;
+    if (MBW < 1) MBW = 1;
+    auto tiles = [&](int mbw, int wk) { return (T32 + (4 / wk) * 16 * mbw - 1) / ((4 / wk) * 16 * mbw); };
+    while (MBW > 1 && tiles(MBW, WK) < 512) MBW >>= 1;
+    MBW = env_int("LOGRA_PROJ_MB", MBW);
+    WK = env_int("LOGRA_PROJ_WK", WK);
+    pl.MBW = MBW;
+    pl.WK = WK;
+    TT = (4 / WK) * 16 * MBW;
+    // The contraction reads whole 32-token steps of P: cover them all, so the
+    // tokens in [T, Tpad) hold P = 0 written by the projection (X reads as 0).
+    pl.n_tt = (int)((T32 + TT - 1) / TT);
+    int64_t nk = 1;
+    if (pl.n_tt < 256) nk = (256 + pl.n_tt - 1) / pl.n_tt;
+    const int64_t rounds = (pl.ncb + WK - 1) / WK;
+    if (nk > rounds) nk = rounds;
+    nk = env_int("LOGRA_PROJ_NK", (int)nk);
+    if (nk < 1) nk = 1;
+    const int64_t rounds_per = (rounds + nk - 1) / nk;
+    pl.cbs_per = (int)(rounds_per * WK);
+    pl.n_k = (int)((pl.ncb + pl.cbs_per - 1) / pl.cbs_per);
+  }
   pl.Tpad = pl.n_tt * TT;
-  int64_t nk = 1;
-  if (pl.n_tt < 256) nk = (256 + pl.n_tt - 1) / pl.n_tt;
-  const int64_t rounds = (pl.ncb + WK - 1) / WK;
-  if (nk > rounds) nk = rounds;
-  nk = env_int("LOGRA_PROJ_NK", (int)nk);
-  if (nk < 1) nk = 1;
-  const int64_t rounds_per = (rounds + nk - 1) / nk;
-  pl.cbs_per = (int)(rounds_per * WK);
-  pl.n_k = (int)((pl.ncb + pl.cbs_per - 1) / pl.cbs_per);
 
   // Contraction.
-  const int64_t nks = (T + 31) / 32;
-  int64_t BD;
+  const int64_t nks = T32 / 32;
+  int64_t BD, min_steps;
   if (pl.NB <= 4) {
-    pl.cvar = 0;
+    pl.cvar = 0;  // eight waves on every eighth step of 64 rows
     BD = 16 * kDC;
+    min_steps = 16;
   } else if (pl.NB == 8) {
     pl.cvar = 1;  // WN = 1, WM = 4
     BD = 4 * 16 * kDC;
+    min_steps = 16;
   } else {
     pl.cvar = 2;  // WN = 2, WM = 2
     BD = 2 * 16 * kDC;
+    min_steps = 16;
   }
   pl.n_dt = (int)((d + BD - 1) / BD);
-  const int64_t min_steps = pl.cvar == 0 ? 16 : 16;  // 32-token steps per workgroup
-  int64_t n_ts = (512 + pl.n_dt - 1) / pl.n_dt;
+  int64_t n_ts = (384 + pl.n_dt - 1) / pl.n_dt;
   int64_t max_ts = nks / min_steps;
   if (max_ts < 1) max_ts = 1;
   if (n_ts > max_ts) n_ts = max_ts;
@@ -580,6 +739,20 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
 }
 
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
+  if (pl.small_proj) {
+    const size_t shm = proj_small_lds_bytes(pl.NB, pl.ncb);
+#define LOGRA_PSMALL(nb, mb)                                                                       \
+    if (pl.NB == nb && pl.MBW == mb) {                                                             \
+      hipLaunchKernelGGL((proj_small_kernel<nb, mb>), dim3(pl.n_tt), dim3(512), shm, s, p);       \
+      return true;                                                                                 \
+    }
+    LOGRA_PSMALL(1, 1) LOGRA_PSMALL(1, 2) LOGRA_PSMALL(1, 4)
+    LOGRA_PSMALL(2, 1) LOGRA_PSMALL(2, 2) LOGRA_PSMALL(2, 4)
+    LOGRA_PSMALL(4, 1) LOGRA_PSMALL(4, 2) LOGRA_PSMALL(4, 4)
+    LOGRA_PSMALL(8, 1) LOGRA_PSMALL(8, 2)
+#undef LOGRA_PSMALL
+    return false;
+  }
   const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, 8);
 #define LOGRA_PROJ(nb, mb, wk)                                                            \
   if (pl.NB == nb && pl.MBW == mb && pl.WK == wk) {                                       \
@@ -606,9 +779,9 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
   const int grid = (int)align_up((size_t)pl.n_dt * pl.n_ts, 8);
   switch (pl.cvar) {
     case 0:
-      if (pl.NB == 1) hipLaunchKernelGGL((contract_small_kernel<1>), dim3(grid), dim3(256), 0, s, p);
-      else if (pl.NB == 2) hipLaunchKernelGGL((contract_small_kernel<2>), dim3(grid), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((contract_small_kernel<4>), dim3(grid), dim3(256), 0, s, p);
+      if (pl.NB == 1) hipLaunchKernelGGL((contract_small_kernel<1, 3>), dim3(grid), dim3(512), 0, s, p);
+      else if (pl.NB == 2) hipLaunchKernelGGL((contract_small_kernel<2, 3>), dim3(grid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((contract_small_kernel<4, 2>), dim3(grid), dim3(512), 0, s, p);
       return true;
     case 1:
       hipLaunchKernelGGL((contract_lds_kernel<8, 1>), dim3(grid), dim3(256), 0, s, p);

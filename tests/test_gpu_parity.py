@@ -179,21 +179,30 @@ def test_sketch_full_size_sampled_rows(key, layer, r, M, heavy):
 
 PLAN_OVERRIDES = [
     {},
-    {"LOGRA_PROJ_NK": 1},
-    {"LOGRA_PROJ_NK": 3},
-    {"LOGRA_PROJ_WK": 1, "LOGRA_PROJ_MB": 2},
-    {"LOGRA_PROJ_WK": 2, "LOGRA_PROJ_MB": 1, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_MB": 2},
+    {"LOGRA_PROJ_SMALL": 0},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NK": 1},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NK": 3},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_WK": 1, "LOGRA_PROJ_MB": 2},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_MB": 1, "LOGRA_PROJ_NK": 2},
     {"LOGRA_CON_TS": 1},
     {"LOGRA_CON_TS": 7},
 ]
 
 
+def _plan_id(e):
+    return ",".join(f"{k[6:]}={v}" for k, v in e.items()) or "default"
+
+
 @pytest.mark.parametrize("r", [64, 128, 256])
-@pytest.mark.parametrize("env", PLAN_OVERRIDES, ids=lambda e: ",".join(f"{k[6:]}={v}" for k, v in e.items()) or "default")
+@pytest.mark.parametrize("env", PLAN_OVERRIDES, ids=_plan_id)
 def test_sketch_launch_plans(r, env, monkeypatch):
-    """Every tiling the planner can pick (column splits across workgroups with
-    the last-arriver reduction, waves along k or tokens, token splits of the
+    """Every tiling the planner can pick (the all-signs-in-LDS projection, the
+    round-based projection with column splits across workgroups and the
+    last-arriver reduction, waves along k or tokens, token splits of the
     contraction) gives the oracle's sketch."""
+    if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
+        env = dict(env, LOGRA_PROJ_SMALL=0)  # rank 256 always takes the round-based projection
     if r == 256 and env.get("LOGRA_PROJ_WK", 1) != 1:
         pytest.skip("rank 256 runs with one wave column along k")
     for k_, v_ in env.items():
