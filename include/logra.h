@@ -102,8 +102,8 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
  * in place, with scale = alpha * eta supplied by the host.  U is the sketch S,
  * or S after logra_rowadam_scale.  No d x k update buffer exists: each W tile
  * is read, updated in fp32 and rounded to bf16 (round to nearest, ties to
- * even) once.  U is first copied into library scratch (per device and
- * stream) as a bf16 high/low pair, which carries it to about 2^-16 relative.
+ * even) once.  Inside the kernel U is carried as a bf16 high/low pair
+ * (about 2^-16 relative); the call needs no scratch memory.
  *
  *   W    bf16, d x k, row stride ldw, read and written.  8-byte aligned base,
  *        ldw a multiple of 4.

@@ -41,7 +41,7 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
 // it grows the stream is synchronised, so no queued kernel still uses the old
 // buffer.  New memory is zeroed (the sketch path keeps counters there that
 // must start at zero; its kernels leave them at zero).
-enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaMerge = 2 };
+enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1 };
 struct Arena {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -165,22 +165,18 @@ logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ld
     if (d > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "d and k must be below 2^31");
     if (scale == 0.0f) return LOGRA_OK;
 
+    if ((uint64_t)d * (uint64_t)ldw * 2 >= ((uint64_t)1 << 32) - 4096 ||
+        (uint64_t)d * (uint64_t)ldu * 4 >= ((uint64_t)1 << 32) - 4096)
+      return fail(LOGRA_ERR_SHAPE, "W or U spans 4 GiB or more; merge the rows in several calls");
     const MergePlan pl = plan_merge(d, k, r);
-    void* ws = nullptr;
-    logra_status st = arena_get(kArenaMerge, stream, 2 * pl.u_bytes, &ws);
-    if (st != LOGRA_OK) return st;
-
-    USplitParams up{};
-    up.U = U; up.ldu = ldu; up.d = d; up.dpad = pl.dpad; up.r = r; up.KR = (r + 31) / 32 * 32;
-    up.Uhi = static_cast<uint16_t*>(ws);
-    up.Ulo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pl.u_bytes);
-
     MergeParams mp{};
     mp.W = static_cast<uint16_t*>(W);
-    mp.ldw = ldw; mp.d = d; mp.k = k; mp.Uhi = up.Uhi; mp.Ulo = up.Ulo; mp.seed = seed; mp.KR = up.KR;
+    mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;
+    mp.u_vec = (((uintptr_t)U & 15) == 0 && (ldu & 3) == 0) ? 1 : 0;
+    mp.seed = seed; mp.KR = (r + 31) / 32 * 32;
     mp.scale_eff = (float)((double)scale / sqrt((double)r));
     mp.n_cb = pl.n_cb; mp.n_dt = pl.n_dt;
-    merge_launch(pl, up, mp, stream);
+    if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return LOGRA_OK;

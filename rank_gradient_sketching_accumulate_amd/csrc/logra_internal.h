@@ -61,35 +61,27 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
 // ---------------------------------------------------------------------------
 // Merge W <- RNE(W - scale_eff * U s).
 // ---------------------------------------------------------------------------
-struct USplitParams {
-  const float* U;
-  int64_t ldu, d;
-  int64_t dpad;     // rows written (multiple of 16, >= d); rows >= d are zero
-  int r, KR;        // rank, rank rounded up to 32
-  uint16_t* Uhi;    // Uk order, see merge_kernels.hip
-  uint16_t* Ulo;
-};
-
 struct MergeParams {
   uint16_t* W;
   int64_t ldw, d, k;
-  const uint16_t* Uhi;
-  const uint16_t* Ulo;
+  const float* U;
+  int64_t ldu;
+  int r;
+  int u_vec;        // U rows 16-byte aligned (ldu % 4 == 0, aligned base)
   uint64_t seed;
-  int KR;
-  float scale_eff;
-  int n_cb, n_dt;
+  int KR;           // r rounded up to 32
+  float scale_eff;  // scale / sqrt(r)
+  int n_cb, n_dt;   // column tiles, row tiles
 };
 
 struct MergePlan {
   int NBW;          // 16-row blocks per wave
+  int CB;           // 16-column blocks per workgroup (8 or 16)
   int n_cb, n_dt;
-  int64_t dpad;
-  size_t u_bytes;   // scratch for the U hi/lo pair
 };
 
 MergePlan plan_merge(int64_t d, int64_t k, int r);
-bool merge_launch(const MergePlan& pl, const USplitParams& up, const MergeParams& mp, hipStream_t s);
+bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // RowAdam and the sign dump.

@@ -302,6 +302,19 @@ def test_merge_ragged_and_zero_weight(d, k, r):
     assert_weight_close(f64(W), _oracle_merge(W0, U, seed, r, k, 1e-4), bound=update_error_bound(f64(U), r, 1e-4))
 
 
+@pytest.mark.parametrize("d,k,r", [(70, 520, 37), (300, 1030, 64)])
+def test_merge_unaligned_u_rows(d, k, r):
+    """U as a strided view (row stride r + 3, base offset by one float): the
+    kernel reads it element by element."""
+    seed = 7 + d
+    big = wl.random_tensor((d, r + 3), seed, device=DEV, std=2.0)
+    U = big[:, 1 : r + 1]
+    W = wl.gaussian_bf16((d, k), 0.02, seed + 1, device=DEV, ld=padded_ld(k, 4))
+    W0 = W.clone()
+    lg.merge_update(W, U, seed, r, 3e-3)
+    assert_weight_close(f64(W), _oracle_merge(W0, U, seed, r, k, 3e-3), bound=update_error_bound(f64(U), r, 3e-3))
+
+
 def test_merge_scale_zero_and_zero_sketch_identity():
     d, k, r = 200, 700, 32
     W = wl.gaussian_bf16((d, k), 0.02, 3, device=DEV, ld=704)
