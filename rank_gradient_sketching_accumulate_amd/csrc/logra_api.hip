@@ -173,9 +173,9 @@ logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ld
     mp.W = static_cast<uint16_t*>(W);
     mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;
     mp.u_vec = (((uintptr_t)U & 15) == 0 && (ldu & 3) == 0) ? 1 : 0;
-    mp.seed = seed; mp.KR = (r + 31) / 32 * 32;
+    mp.seed = seed;
     mp.scale_eff = (float)((double)scale / sqrt((double)r));
-    mp.n_cb = pl.n_cb; mp.n_dt = pl.n_dt;
+    mp.n_rb = pl.n_rb; mp.n_cr = pl.n_cr; mp.cr_cols = pl.cr_cols;
     if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "merge launch");

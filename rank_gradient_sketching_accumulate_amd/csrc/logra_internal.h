@@ -69,15 +69,17 @@ struct MergeParams {
   int r;
   int u_vec;        // U rows 16-byte aligned (ldu % 4 == 0, aligned base)
   uint64_t seed;
-  int KR;           // r rounded up to 32
   float scale_eff;  // scale / sqrt(r)
-  int n_cb, n_dt;   // column tiles, row tiles
+  int n_rb, n_cr;   // row blocks, column ranges
+  int64_t cr_cols;  // columns per range (a multiple of the chunk width)
 };
 
 struct MergePlan {
+  int NK;           // 32-wide steps of r (1, 2, 4 or 8; U zero-padded)
   int NBW;          // 16-row blocks per wave
-  int CB;           // 16-column blocks per workgroup (8 or 16)
-  int n_cb, n_dt;
+  int CB;           // 16-column blocks per chunk (4 or 8)
+  int n_rb, n_cr;
+  int64_t cr_cols;
 };
 
 MergePlan plan_merge(int64_t d, int64_t k, int r);

@@ -4,18 +4,21 @@
 // Algorithm 1's trainer update.  No d x k update buffer exists: every W tile
 // is read once, updated in fp32 and rounded to bf16 once.
 //
-// One kernel.  A workgroup owns rows [r0, r0 + 64*NBW) and 16*CB columns of
-// one 256-column sign block.  It regenerates that block's signs (Philox,
-// rows 0..KR-1) into LDS, bit-transposes them so that one byte holds 8 rows of
-// one column, and per 32-wide step of r expands the sign operands of its
-// column blocks once into a double-buffered LDS stage shared by its waves.
-// Each wave owns 16*NBW rows: it reads its U rows straight from memory,
-// splits them into a bf16 hi/lo pair in registers and runs the MFMAs.  The W
-// tile is fetched at the start and rewritten at the end.
+// One kernel.  A workgroup owns a block of 64*NBW rows and a range of
+// columns, which it walks in chunks of 16*CB columns.  Its waves (16*NBW rows
+// each) load their U rows once, split them into bf16 hi/lo pairs held in
+// registers for the whole range, and keep the W tiles of the next PD chunks
+// in flight.  Whenever the walk enters a new 256-column sign block the
+// workgroup regenerates that block's signs (Philox, rows 0 .. 32*NK-1) into
+// LDS and bit-transposes them so that one byte holds 8 rows of a column;
+// every wave then expands its own MFMA sign operands from those bytes.
 //
 // MFMA orientation D = s^T U^T: M = 16 columns of W, N = 16 rows of W,
 // K = 32 entries of r, so each lane ends with four consecutive columns of
-// one W row (one 8-byte access).
+// one W row.  W itself moves in row-contiguous pieces: each wave parks its
+// fp32 update tile in a private LDS slice and reads it back as 16*CB/4 lanes
+// x 4 columns per row, so one load or store instruction covers whole
+// 128-byte rows (the MFMA layout would touch 16 rows per instruction).
 #include "logra_device.h"
 #include "logra_internal.h"
 
@@ -37,167 +40,192 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
   return x;
 }
 
-template <int NBW, int CB>
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  constexpr int STR = 9;  // dwords per row (row-major bits) / per column (column-major bits)
-  __shared__ uint32_t rowbits[256 * STR];
-  __shared__ uint32_t colbits[16 * CB * STR];
-  __shared__ u32x4 sgn[2][CB * 64];
+template <int NBW, int CB, int NK, int PD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_kernel(MergeParams p) {
+  constexpr int STR = 9;        // dwords per row (row-major bits) / per column (column-major bits)
+  constexpr int CW = 16 * CB;   // columns per chunk
+  constexpr int KR = 32 * NK;   // sign rows generated (U entries >= r are zero)
+  constexpr int RW = 16 * NBW;  // rows per wave
+  constexpr int TSTR = CW + 4;  // floats per row of a wave's update tile (conflict-free)
+  constexpr int LPR = CW / 4;   // lanes per row in the row-contiguous layout
+  constexpr int RPI = 64 / LPR; // rows per W instruction
+  constexpr int NI = RW / RPI;  // W instructions per chunk
+  __shared__ uint32_t rowbits[KR * STR];
+  __shared__ uint32_t colbits[256 * STR];
+  __shared__ float tiles[4 * RW * TSTR];
 
   const int lin = xcd_linear_id_m(blockIdx.x, gridDim.x);
-  const int dt = lin / p.n_cb;
-  const int ct = lin - dt * p.n_cb;  // column tile of 16*CB columns
-  if (dt >= p.n_dt) return;
+  const int rb = lin / p.n_cr;
+  const int cr = lin - rb * p.n_cr;
+  if (rb >= p.n_rb) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, i = lane & 15;
-  const int64_t c0 = (int64_t)ct * 16 * CB;
-  const int sblk = (int)(c0 >> 8);   // 256-column sign block
-  const int cofs = (int)(c0 & 255);  // first column inside it
-  const int64_t rw = (int64_t)dt * 64 * NBW + (int64_t)wave * 16 * NBW;  // first row of this wave
-  const int NK = p.KR >> 5;
+  const int64_t rw = (int64_t)rb * 4 * RW + (int64_t)wave * RW;  // first row of this wave
+  const int64_t c_begin = (int64_t)cr * p.cr_cols;
+  const int64_t c_end = min(p.k, c_begin + p.cr_cols);
+  const int nch = (int)((c_end - c_begin + CW - 1) / CW);
 
-  // W tile of this lane: rows rw + 16*nb + i, columns c0 + 16*mb + 4g .. +3.
-  // Rows past d read as zero through the descriptor and are never written.
-  const __amdgpu_buffer_rsrc_t rwb = make_rsrc(p.W, (uint32_t)(p.d * p.ldw * 2));
-  u32x2 wv[CB][NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const uint32_t rowoff = (uint32_t)((rw + 16 * nb + i) * p.ldw * 2);
-#pragma unroll
-    for (int mb = 0; mb < CB; ++mb)
-      wv[mb][nb] = buf_load8(rwb, rowoff + (uint32_t)((c0 + 16 * mb + 4 * g) * 2));
-  }
-
-  // Signs of rows 0 .. KR-1 for this 256-column block, then bit-transpose the
-  // workgroup's columns so that one byte holds 8 consecutive rows of a column.
-  if (threadIdx.x < p.KR) {
-    uint32_t w[8];
-    philox_sign_block(p.seed, threadIdx.x, (uint32_t)sblk, w);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) rowbits[threadIdx.x * STR + q] = w[q];
-  }
-  __syncthreads();
-  {
-    const uint8_t* rb = reinterpret_cast<const uint8_t*>(rowbits);
-    uint8_t* cbt = reinterpret_cast<uint8_t*>(colbits);
-    constexpr int NCO = 2 * CB;  // column octets of this workgroup
-    for (int task = threadIdx.x; task < NCO * (p.KR >> 3); task += 256) {
-      const int co = task % NCO;  // column octet
-      const int ro = task / NCO;  // row octet
-      uint64_t x = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x |= (uint64_t)rb[(8 * ro + e) * STR * 4 + (cofs >> 3) + co] << (8 * e);
-      x = transpose8x8(x);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) cbt[(8 * co + b) * STR * 4 + ro] = (uint8_t)(x >> (8 * b));
-    }
-  }
-  __syncthreads();
-
-  // The four waves expand the column blocks of K step kk into stage buf.
-  const SignExpander ex(g);
-  auto expand = [&](int kk, int buf) {
-#pragma unroll
-    for (int q = 0; q < (CB + 3) / 4; ++q) {
-      const int mb = 4 * q + wave;
-      if (mb < CB) sgn[buf][mb * 64 + lane] = ex(colbits[(16 * mb + i) * STR + kk]);
-    }
-  };
-
-  // U rows of this wave, split into a bf16 hi/lo pair in registers.  Entries
-  // past r are zeroed; rows past d read as zero through the descriptor.
+  // U rows of this wave: 8 consecutive entries per (K step, row block) and
+  // lane.  Entries past r are zeroed; rows past d read as zero through the
+  // descriptor.  Queued first, split after the first sign block is built.
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.U, (uint32_t)(p.d * p.ldu * 4));
-  u32x4 bh[2][NBW], bl[2][NBW];
-  auto load_u = [&](int kk, int s) {
-    const int j0 = 32 * kk + 8 * g;
+  float uraw[NK][NBW][8];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
+      const int j0 = 32 * kk + 8 * g;
       const uint32_t off = (uint32_t)(((rw + 16 * nb + i) * p.ldu + j0) * 4);
-      float u[8];
-      if (p.u_vec) {
+      if (j0 >= p.r) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) uraw[kk][nb][e] = 0.f;
+      } else if (p.u_vec) {
         const f32x4 x0 = __builtin_bit_cast(f32x4, buf_load16(ru, off));
         const f32x4 x1 = __builtin_bit_cast(f32x4, buf_load16(ru, off + 16));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          u[e] = x0[e];
-          u[4 + e] = x1[e];
+          uraw[kk][nb][e] = x0[e];
+          uraw[kk][nb][4 + e] = x1[e];
         }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          u[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, off + 4 * e, 0, 0));
+          uraw[kk][nb][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, off + 4 * e, 0, 0));
       }
-      if (j0 + 8 > p.r) {
+      if (j0 < p.r && j0 + 8 > p.r) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (j0 + e >= p.r) u[e] = 0.f;
+          if (j0 + e >= p.r) uraw[kk][nb][e] = 0.f;
       }
+    }
+
+  // W tiles of the next PD chunks in the row-contiguous layout: the lane holds
+  // row rw + RPI*q + lane/LPR, columns chunk + 4*(lane%LPR) .. +3.  Rows past
+  // d read as zero and are never written; columns past k are never written.
+  const int lrow = lane / LPR, lcol = 4 * (lane % LPR);
+  const __amdgpu_buffer_rsrc_t rwb = make_rsrc(p.W, (uint32_t)(p.d * p.ldw * 2));
+  const uint32_t wbase = (uint32_t)(((rw + lrow) * p.ldw + c_begin + lcol) * 2);
+  const uint32_t wrowstep = (uint32_t)(RPI * p.ldw * 2);
+  u32x2 wv[PD][NI];
+  auto load_w = [&](int slot, int ch) {
+    if (ch >= nch) return;
+    uint32_t off = wbase + (uint32_t)(ch * CW * 2);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t h, l;
-        split_hi_lo2(u[2 * q], u[2 * q + 1], h, l);
-        bh[s][nb][q] = h;
-        bl[s][nb][q] = l;
-      }
+    for (int q = 0; q < NI; ++q) {
+      wv[slot][q] = buf_load8(rwb, off);
+      off += wrowstep;
     }
   };
+#pragma unroll
+  for (int q = 0; q < PD; ++q) load_w(q, q);
 
-  f32x4 acc[CB][NBW];
+  // Signs of the 256-column block holding col0: rows 0 .. KR-1 into rowbits,
+  // then the columns of this workgroup's range inside the block into colbits.
+  auto build_block = [&](int64_t col0) {
+    if (threadIdx.x < KR) {
+      uint32_t w[8];
+      philox_sign_block(p.seed, threadIdx.x, (uint32_t)(col0 >> 8), w);
 #pragma unroll
-  for (int mb = 0; mb < CB; ++mb)
+      for (int q = 0; q < 8; ++q) rowbits[threadIdx.x * STR + q] = w[q];
+    }
+    __syncthreads();  // also: every wave is done with the previous colbits
+    const uint8_t* rbt = reinterpret_cast<const uint8_t*>(rowbits);
+    uint8_t* cbt = reinterpret_cast<uint8_t*>(colbits);
+    const int co_lo = (int)(col0 & 255) >> 3;
+    const int64_t left = (c_end - col0 + 7) >> 3;
+    const int co_hi = left < 32 - co_lo ? co_lo + (int)left : 32;
+    const int nco = co_hi - co_lo;
+    for (int task = threadIdx.x; task < nco * (KR >> 3); task += 256) {
+      const int co = co_lo + task % nco;  // column octet
+      const int ro = task / nco;          // row octet
+      uint64_t x = 0;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) x |= (uint64_t)rbt[(8 * ro + e) * STR * 4 + co] << (8 * e);
+      x = transpose8x8(x);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) cbt[(8 * co + b) * STR * 4 + ro] = (uint8_t)(x >> (8 * b));
+    }
+    __syncthreads();
+  };
 
-  expand(0, 0);
-  load_u(0, 0);
-  __syncthreads();
-  for (int k0 = 0; k0 < NK; k0 += 2) {
+  if (nch > 0) build_block(c_begin);
+
+  u32x4 uh[NK][NBW], ul[NK][NBW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = k0 + u;
-      if (kk < NK) {
-        if (kk + 1 < NK) {
-          expand(kk + 1, u ^ 1);
-          load_u(kk + 1, u ^ 1);
-        }
+  for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-        for (int mb = 0; mb < CB; ++mb) {
-          const u32x4 a = sgn[u][mb * 64 + lane];
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) {
-            acc[mb][nb] = mfma_16x16x32(a, bh[u][nb], acc[mb][nb]);
-            acc[mb][nb] = mfma_16x16x32(a, bl[u][nb], acc[mb][nb]);
+      for (int q = 0; q < 4; ++q) {
+        float h0 = uraw[kk][nb][2 * q], h1 = uraw[kk][nb][2 * q + 1];
+        uint32_t h, l;
+        split_hi_lo2(h0, h1, h, l);
+        uh[kk][nb][q] = h;
+        ul[kk][nb][q] = l;
+      }
+
+  const SignExpander ex(g);
+  const float ns = -p.scale_eff;
+  float* tile = tiles + wave * RW * TSTR;
+  for (int ch0 = 0; ch0 < nch; ch0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int ch = ch0 + u;
+      if (ch < nch) {
+        const int64_t col0 = c_begin + (int64_t)ch * CW;
+        if (ch > 0 && (col0 & 255) == 0) build_block(col0);
+        const int cib = (int)(col0 & 255);
+
+        f32x4 acc[CB][NBW];
+#pragma unroll
+        for (int mb = 0; mb < CB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < CB; ++mb) {
+            const u32x4 a = ex(colbits[(cib + 16 * mb + i) * STR + kk]);
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+              acc[mb][nb] = mfma_16x16x32(a, uh[kk][nb], acc[mb][nb]);
+              acc[mb][nb] = mfma_16x16x32(a, ul[kk][nb], acc[mb][nb]);
+            }
+          }
+
+        // Park the tile (row 16*nb + i, columns 16*mb + 4g ..), then read it
+        // back row-contiguously.  The slice is private to this wave, whose
+        // LDS accesses complete in order.
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < CB; ++mb)
+            *reinterpret_cast<f32x4*>(tile + (16 * nb + i) * TSTR + 16 * mb + 4 * g) = acc[mb][nb];
+        __builtin_amdgcn_wave_barrier();
+        const int64_t col = col0 + lcol;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(tile + (RPI * q + lrow) * TSTR + lcol);
+          const int64_t row = rw + RPI * q + lrow;
+          if (row >= p.d || col >= p.k) continue;
+          const u32x2 v = wv[u][q];
+          const float w0 = __uint_as_float(v[0] << 16), w1 = __uint_as_float(v[0] & 0xffff0000u);
+          const float w2 = __uint_as_float(v[1] << 16), w3 = __uint_as_float(v[1] & 0xffff0000u);
+          const uint32_t p01 = pack_bf16x2(__fmaf_rn(ns, a[0], w0), __fmaf_rn(ns, a[1], w1));
+          const uint32_t p23 = pack_bf16x2(__fmaf_rn(ns, a[2], w2), __fmaf_rn(ns, a[3], w3));
+          uint16_t* dst = p.W + row * p.ldw + col;
+          if (col + 4 <= p.k) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{p01, p23};
+          } else {
+            const uint32_t h[4] = {p01 & 0xffffu, p01 >> 16, p23 & 0xffffu, p23 >> 16};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.k) dst[e] = (uint16_t)h[e];
           }
         }
-        __syncthreads();
-      }
-    }
-  }
-
-  const float ns = -p.scale_eff;
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int64_t row = rw + 16 * nb + i;
-    if (row >= p.d) continue;
-    uint16_t* wrow = p.W + row * p.ldw;
-#pragma unroll
-    for (int mb = 0; mb < CB; ++mb) {
-      const int64_t col = c0 + 16 * mb + 4 * g;
-      if (col >= p.k) continue;
-      const u32x2 v = wv[mb][nb];
-      const float w0 = __uint_as_float(v[0] << 16), w1 = __uint_as_float(v[0] & 0xffff0000u);
-      const float w2 = __uint_as_float(v[1] << 16), w3 = __uint_as_float(v[1] & 0xffff0000u);
-      const uint32_t p01 = pack_bf16x2(__fmaf_rn(ns, acc[mb][nb][0], w0), __fmaf_rn(ns, acc[mb][nb][1], w1));
-      const uint32_t p23 = pack_bf16x2(__fmaf_rn(ns, acc[mb][nb][2], w2), __fmaf_rn(ns, acc[mb][nb][3], w3));
-      uint16_t* dst = wrow + col;
-      if (col + 4 <= p.k) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{p01, p23};
-      } else {
-        const uint32_t h[4] = {p01 & 0xffffu, p01 >> 16, p23 & 0xffffu, p23 >> 16};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < p.k) dst[e] = (uint16_t)h[e];
+        __builtin_amdgcn_wave_barrier();
+        load_w(u, ch + PD);
       }
     }
   }
@@ -209,30 +237,46 @@ size_t align_up_m(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 MergePlan plan_merge(int64_t d, int64_t k, int r) {
   MergePlan pl{};
-  int NBW = 2, CB = 16;
-  auto tiles = [&](int nbw, int cb) {
-    return ((k + 16 * cb - 1) / (16 * cb)) * ((d + 64 * nbw - 1) / (64 * nbw));
+  pl.NK = r <= 32 ? 1 : (r <= 64 ? 2 : (r <= 128 ? 4 : 8));
+  // Tile per wave and chunk, chosen so that two waves fit per SIMD: two
+  // 16-row blocks x 64 columns (each expanded sign operand feeds both row
+  // blocks), except one 16-row block x 128 columns for r in (64, 128].
+  int NBW = pl.NK == 4 ? 1 : 2, CB = pl.NK == 4 ? 8 : 4;
+  auto units = [&](int nbw, int cb) {
+    return ((d + 64 * nbw - 1) / (64 * nbw)) * ((k + 16 * cb - 1) / (16 * cb));
   };
-  if (tiles(NBW, CB) < 512) NBW = 1;
-  if (tiles(NBW, CB) < 256) CB = 8;
-  NBW = env_int("LOGRA_MERGE_NBW", NBW) == 1 ? 1 : 2;
-  CB = env_int("LOGRA_MERGE_CB", CB) == 8 ? 8 : 16;
+  if (NBW == 2 && units(2, CB) < 512) NBW = 1;
+  NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
+  CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
+  if (NBW == 2 && CB == 8 && pl.NK >= 4) CB = 4;  // would not fit two waves per SIMD
   pl.NBW = NBW;
   pl.CB = CB;
-  pl.n_cb = (int)((k + 16 * CB - 1) / (16 * CB));
-  pl.n_dt = (int)((d + 64 * NBW - 1) / (64 * NBW));
+  pl.n_rb = (int)((d + 64 * NBW - 1) / (64 * NBW));
+  // Column ranges: as long as possible while about 1024 workgroups remain.
+  const int64_t CW = 16 * CB;
+  const int64_t chunks = (k + CW - 1) / CW;
+  int64_t target = env_int("LOGRA_MERGE_WGS", 1024);
+  if (target < 1) target = 1;
+  int64_t n_cr = (target + pl.n_rb - 1) / pl.n_rb;
+  if (n_cr > chunks) n_cr = chunks;
+  if (n_cr < 1) n_cr = 1;
+  pl.cr_cols = ((chunks + n_cr - 1) / n_cr) * CW;
+  pl.n_cr = (int)((k + pl.cr_cols - 1) / pl.cr_cols);
   (void)r;
   return pl;
 }
 
 bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s) {
-  const int grid = (int)align_up_m((size_t)pl.n_cb * pl.n_dt, 8);
-#define LOGRA_MERGE(nbw, cb)                                                              \
-  if (pl.NBW == nbw && pl.CB == cb) {                                                     \
-    hipLaunchKernelGGL((merge_kernel<nbw, cb>), dim3(grid), dim3(256), 0, s, mp);         \
-    return true;                                                                          \
+  const int grid = (int)align_up_m((size_t)pl.n_cr * pl.n_rb, 8);
+#define LOGRA_MERGE(nbw, cb, nk)                                                            \
+  if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                        \
+    hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, mp);    \
+    return true;                                                                            \
   }
-  LOGRA_MERGE(1, 8) LOGRA_MERGE(1, 16) LOGRA_MERGE(2, 8) LOGRA_MERGE(2, 16)
+  LOGRA_MERGE(1, 4, 1) LOGRA_MERGE(1, 8, 1) LOGRA_MERGE(2, 4, 1) LOGRA_MERGE(2, 8, 1)
+  LOGRA_MERGE(1, 4, 2) LOGRA_MERGE(1, 8, 2) LOGRA_MERGE(2, 4, 2) LOGRA_MERGE(2, 8, 2)
+  LOGRA_MERGE(1, 4, 4) LOGRA_MERGE(1, 8, 4) LOGRA_MERGE(2, 4, 4)
+  LOGRA_MERGE(1, 4, 8) LOGRA_MERGE(1, 8, 8) LOGRA_MERGE(2, 4, 8)
 #undef LOGRA_MERGE
   return false;
 }

@@ -187,11 +187,35 @@ PLAN_OVERRIDES = [
     {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_MB": 1, "LOGRA_PROJ_NK": 2},
     {"LOGRA_CON_TS": 1},
     {"LOGRA_CON_TS": 7},
+    {"LOGRA_CON_TS": 3, "LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NK": 2},
 ]
 
 
 def _plan_id(e):
     return ",".join(f"{k[6:]}={v}" for k, v in e.items()) or "default"
+
+
+def test_sketch_consecutive_calls_changing_shapes():
+    """Consecutive calls on one stream with changing shapes and inputs (so
+    changing plans, tile counts and scratch layouts, including the column
+    splits whose last-arriving workgroup sums the partials) each give the
+    oracle's sketch: nothing one call leaves in the scratch leaks into the
+    next."""
+    cases = [(4096, 1536, 1536, 64), (700, 1300, 300, 64), (33, 264, 17, 5), (4096, 1536, 1536, 64),
+             (9000, 520, 130, 16), (1, 8, 1, 1), (2500, 700, 77, 40), (700, 1300, 300, 64),
+             (300, 5120, 96, 256), (1000, 2056, 200, 128), (300, 5120, 96, 256)]
+    for j, (T, k, d, r) in enumerate(cases):
+        _say("handoff", j, T, k, d, r)
+        seed = 5000 + j
+        X, dY = _ragged_inputs(T, k, d, seed)
+        X2, dY2 = _ragged_inputs(T, k, d, seed + 50)
+        S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+        lg.sketch_accumulate(X2, dY2, seed, r, S)  # same plan, new inputs
+        rows = None if d <= 300 else np.arange(0, d, 37)
+        ref = _oracle_sketch(torch.zeros_like(S), [X, X2], [dY, dY2], seed, r, k, rows=rows)
+        got = f64(S) if rows is None else f64(S)[rows]
+        assert_sketch_close(got, ref)
 
 
 @pytest.mark.parametrize("r", [64, 128, 256])
@@ -313,6 +337,34 @@ def test_merge_unaligned_u_rows(d, k, r):
     W0 = W.clone()
     lg.merge_update(W, U, seed, r, 3e-3)
     assert_weight_close(f64(W), _oracle_merge(W0, U, seed, r, k, 3e-3), bound=update_error_bound(f64(U), r, 3e-3))
+
+
+MERGE_PLANS = [
+    {},
+    {"LOGRA_MERGE_WGS": 1},
+    {"LOGRA_MERGE_WGS": 100000},
+    {"LOGRA_MERGE_NBW": 1, "LOGRA_MERGE_CB": 8, "LOGRA_MERGE_WGS": 7},
+    {"LOGRA_MERGE_NBW": 2, "LOGRA_MERGE_CB": 4, "LOGRA_MERGE_WGS": 30},
+    {"LOGRA_MERGE_NBW": 2, "LOGRA_MERGE_CB": 8},
+    {"LOGRA_MERGE_NBW": 1, "LOGRA_MERGE_CB": 4},
+]
+
+
+@pytest.mark.parametrize("r", [16, 64, 100, 256])
+@pytest.mark.parametrize("env", MERGE_PLANS, ids=_plan_id)
+def test_merge_launch_plans(r, env, monkeypatch):
+    """Every tiling of the merge (rows per wave, chunk width, column ranges that
+    start inside a sign block or span several blocks) gives the oracle's W."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    d, k = 150, 1100
+    seed = 77 + r
+    _say("merge plans", r, env)
+    U = wl.random_tensor((d, r), seed, device=DEV, std=2.0)
+    W = wl.gaussian_bf16((d, k), 0.02, seed + 1, device=DEV, ld=padded_ld(k, 4))
+    W0 = W.clone()
+    lg.merge_update(W, U, seed, r, 1e-2)
+    assert_weight_close(f64(W), _oracle_merge(W0, U, seed, r, k, 1e-2), bound=update_error_bound(f64(U), r, 1e-2))
 
 
 def test_merge_scale_zero_and_zero_sketch_identity():
