@@ -49,6 +49,7 @@ struct SketchPlan {
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)
+  int WM;                 // contraction row groups per workgroup (cvar 5)
   int n_dt, n_ts;
   int64_t ksp;
   size_t off_counters, off_phi, off_plo, off_part, total;

@@ -628,6 +628,221 @@ __global__ __launch_bounds__(256) void contract_lds_kernel(ContractParams p) {
   store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
 }
 
+// Larger ranks on big problems: eight waves, each owning 64 rows x 128
+// columns of S (128 accumulator registers, two waves per SIMD); WM = 8/WN row
+// groups x WN column groups give a 512 x 128 (r <= 128) or 256 x 256 tile.
+// The step's P tile sits in a double-buffered LDS stage shared by all waves;
+// every wave loads the dY rows of its row group itself.
+template <int NB, int WN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void contract_big_kernel(ContractParams p) {
+  constexpr int NBW = NB / WN;           // column blocks per wave
+  constexpr int WM = 8 / WN;             // row groups
+  constexpr int PV = NB * 64;            // u32x4 words per half-tile of a step
+  constexpr int PER = 2 * PV / 512;      // u32x4 words each thread moves per step
+  __shared__ u32x4 pt[2][2 * PV];
+  // Token splits vary fastest among consecutive logical ids, so the
+  // workgroups that add into the same S tile share an XCD (and its L2).
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int dt = lin / p.n_ts;
+  const int ts = lin - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int wn = wave % WN, wm = wave / WN;
+  const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
+  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+  const int64_t nks = (p.T + 31) >> 5;
+  const int64_t ks_beg = ts * p.ksp;
+  const int64_t ks_end = min(nks, ks_beg + p.ksp);
+  const int nsteps = ks_end > ks_beg ? (int)(ks_end - ks_beg) : 0;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+  const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+
+  f32x4 acc[kDC][NBW];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x2 y[2][8];
+  u32x4 stg[PER];
+  auto load_y = [&](u32x2 (&slot)[8], int m) {
+    uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      slot[e] = buf_load8(ry, off);
+      off += rowstep;
+    }
+  };
+  // Thread q moves words q, q + 512, ... of the step's [hi | lo] tile.
+  auto load_p = [&](int m) {
+    const int64_t base = (ks_beg + m) * (int64_t)PV;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int w = threadIdx.x + 512 * j;
+      const uint16_t* src = (w < PV) ? p.Phi + (base + w) * 8 : p.Plo + (base + w - PV) * 8;
+      stg[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto store_p = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pt[buf][threadIdx.x + 512 * j] = stg[j];
+  };
+
+  if (nsteps > 0) {
+    load_p(0);
+    load_y(y[0], 0);
+    store_p(0);
+  }
+  __syncthreads();
+  for (int m0 = 0; m0 < nsteps; m0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = m0 + u;
+      if (m < nsteps) {
+        const bool more = m + 1 < nsteps;
+        if (more) {
+          load_p(m + 1);
+          load_y(y[u ^ 1], m + 1);
+        }
+        u32x4 a[kDC];
+        transpose_dy(y[u], a);
+        const u32x4* ph = &pt[u][0];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const u32x4 bh = ph[(wn * NBW + nb) * 64 + lane];
+          const u32x4 bl = ph[PV + (wn * NBW + nb) * 64 + lane];
+#pragma unroll
+          for (int c = 0; c < kDC; ++c) {
+            acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
+            acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
+          }
+        }
+        if (more) store_p(u ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
+}
+
+// General tiling for larger ranks: NW waves arranged as WM row groups (64
+// rows of S each) x WN column groups (16*NB/WN columns each) x WT token lanes.
+// A wave takes every WT-th 32-token step of the workgroup's token range and
+// loads its own dY rows and P operands (DEPTH steps in flight, no LDS stage
+// and no barrier in the main loop); the WT token-lane partials of each tile
+// are summed through LDS at the end.  Small per-workgroup S tiles keep the
+// token splits (and so the atomic adds into S) few, at the price of reading
+// P from L2 once per 64*WM rows.
+template <int NB, int WM, int WN, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void contract_tile_kernel(ContractParams p) {
+  constexpr int WT = NW / (WM * WN);
+  constexpr int NBW = NB / WN;
+  constexpr int CH = NBW * 256;  // floats of one 16-row block of one wave's tile
+  static_assert(WT * WM * WN == NW, "wave arrangement");
+  __shared__ float red[WT > 1 ? NW * CH : 4];
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int dt = lin / p.n_ts;
+  const int ts = lin - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int wt = w % WT, wn = (w / WT) % WN, wm = w / (WT * WN);
+  const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
+  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+  const int64_t nks = (p.T + 31) >> 5;
+  const int64_t ks_beg = ts * p.ksp;
+  const int64_t ks_end = min(nks, ks_beg + p.ksp);
+  const int64_t ks0 = ks_beg + wt;
+  const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + WT - 1) / WT) : 0;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+  const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+
+  f32x4 acc[kDC][NBW];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x2 y[DEPTH][8];
+  u32x4 bh[DEPTH][NBW], bl[DEPTH][NBW];
+  auto issue = [&](int slot, int m) {
+    if (m >= nsteps) return;
+    const int64_t ks = ks0 + (int64_t)WT * m;
+    uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[slot][e] = buf_load8(ry, off);
+      off += rowstep;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int64_t o = ((ks * p.NB + wn * NBW + nb) * 64 + lane) * 8;
+      bh[slot][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
+      bl[slot][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
+  for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int m = m0 + u;
+      if (m < nsteps) {
+        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
+        u32x4 a[kDC];
+        transpose_dy(y[u], a);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int c = 0; c < kDC; ++c) {
+            acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
+            acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
+          }
+      }
+    }
+  }
+
+  if constexpr (WT == 1) {
+    store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
+  } else {
+    // Sum the WT token lanes of every (row group, column group) through LDS,
+    // one 16-row block (c) at a time.
+#pragma unroll
+    for (int c = 0; c < kDC; ++c) {
+      float* mine = red + w * CH;
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[c][nb][e];
+      __syncthreads();
+      for (int v = threadIdx.x; v < (NW / WT) * CH; v += NW * 64) {
+        const int gm = v / CH, rest = v - gm * CH;  // gm = wm * WN + wn
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < WT; ++q) sum += red[(gm * WT + q) * CH + rest];
+        const int ln = rest & 63, ne = rest >> 6;  // lane and (nb*4 + e) of the element
+        const int nb = ne >> 2, e = ne & 3;
+        const int gg = ln >> 4, ii = ln & 15;
+        const int cc = 16 * ((gm % WN) * NBW + nb) + ii;
+        const int64_t row = ((int64_t)dt * WM + gm / WN) * 16 * kDC + (int64_t)kDC * (4 * gg + e) + c;
+        if (cc < p.r && row < p.d) {
+          float* dst = p.S + row * p.lds + cc;
+          const float val = sum * p.inv_sqrt_r;
+          if (p.atomic_out)
+            atomicAdd(dst, val);
+          else
+            *dst += val;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ===========================================================================
 // Host: plans and launchers.
 // ===========================================================================
@@ -705,19 +920,55 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     pl.cvar = 0;  // eight waves on every eighth step of 64 rows
     BD = 16 * kDC;
     min_steps = 16;
-  } else if (pl.NB == 8) {
-    pl.cvar = 1;  // WN = 1, WM = 4
-    BD = 4 * 16 * kDC;
-    min_steps = 16;
   } else {
-    pl.cvar = 2;  // WN = 2, WM = 2
-    BD = 2 * 16 * kDC;
+    // Eight-wave tiles (512 x 128 or 256 x 256) where they still give a few
+    // hundred workgroups; the four-wave tiles otherwise.
+    // Token-lane tiles (64 rows per workgroup, few token splits) unless the
+    // rank is 256 and the microbatch long: there every 64-row tile would read
+    // eight times the dY bytes in P, and the 256 x 256 tiles win.
+    const int tile = env_int("LOGRA_CON_TILE", (pl.NB == 8 || T <= 8192) ? 1 : 0);
+    const int big = env_int("LOGRA_CON_BIG", -1);
+    const int64_t bd8 = pl.NB == 8 ? 8 * 16 * kDC : 4 * 16 * kDC;
+    const bool use_big = big >= 0 ? big != 0 : ((d + bd8 - 1) / bd8) * (nks / 16) >= 256;
+    if (tile) {
+      // NB = 8: 2 column groups; NB = 16: 4 column groups; WM row groups.
+      const int wn = pl.NB / 4;
+      int wm = env_int("LOGRA_CON_WM", 1);
+      if (wm < 1 || wm * wn > 8) wm = 1;
+      pl.WM = wm;
+      pl.cvar = 5;
+      BD = 16 * kDC * wm;
+    } else if (use_big) {
+      pl.cvar = pl.NB == 8 ? 3 : 4;
+      BD = bd8;
+    } else if (pl.NB == 8) {
+      pl.cvar = 1;  // WN = 1, WM = 4
+      BD = 4 * 16 * kDC;
+    } else {
+      pl.cvar = 2;  // WN = 2, WM = 2
+      BD = 2 * 16 * kDC;
+    }
     min_steps = 16;
   }
   pl.n_dt = (int)((d + BD - 1) / BD);
   int64_t n_ts = (384 + pl.n_dt - 1) / pl.n_dt;
   int64_t max_ts = nks / min_steps;
   if (max_ts < 1) max_ts = 1;
+  if (pl.cvar >= 3) {
+    // One eight-wave workgroup per CU (256 on MI355X): fill whole rounds of
+    // the chip, preferring fewer token splits (less atomic traffic into S).
+    double best = 0.0;
+    for (int R = 1; R <= 4; ++R) {
+      int64_t t = (256 * R) / pl.n_dt;
+      if (t < 1) t = 1;
+      if (t > max_ts) t = max_ts;
+      const double eff = (double)(pl.n_dt * t) / (256.0 * ((pl.n_dt * t + 255) / 256));
+      if (eff > best + 0.05) {
+        best = eff;
+        n_ts = t;
+      }
+    }
+  }
   if (n_ts > max_ts) n_ts = max_ts;
   n_ts = env_int("LOGRA_CON_TS", (int)n_ts);
   if (n_ts < 1) n_ts = 1;
@@ -789,6 +1040,22 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
     case 2:
       hipLaunchKernelGGL((contract_lds_kernel<16, 2>), dim3(grid), dim3(256), 0, s, p);
       return true;
+    case 3:
+      hipLaunchKernelGGL((contract_big_kernel<8, 1>), dim3(grid), dim3(512), 0, s, p);
+      return true;
+    case 4:
+      hipLaunchKernelGGL((contract_big_kernel<16, 2>), dim3(grid), dim3(512), 0, s, p);
+      return true;
+    case 5: {
+#define LOGRA_CT(nb, wm, wn)                                                                          \
+      if (pl.NB == nb && pl.WM == wm) {                                                               \
+        hipLaunchKernelGGL((contract_tile_kernel<nb, wm, wn, 8, 2>), dim3(grid), dim3(512), 0, s, p);   \
+        return true;                                                                                  \
+      }
+      LOGRA_CT(8, 1, 2) LOGRA_CT(8, 2, 2) LOGRA_CT(8, 4, 2) LOGRA_CT(16, 1, 4) LOGRA_CT(16, 2, 4)
+#undef LOGRA_CT
+      return false;
+    }
   }
   return false;
 }

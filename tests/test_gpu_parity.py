@@ -188,6 +188,11 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_TS": 1},
     {"LOGRA_CON_TS": 7},
     {"LOGRA_CON_TS": 3, "LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_TS": 5},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 0},
+    {"LOGRA_CON_WM": 2},
+    {"LOGRA_CON_WM": 4, "LOGRA_CON_TS": 2},
 ]
 
 
