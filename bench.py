@@ -9,8 +9,8 @@ its inputs from HBM.
 
 Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
   roofline     the sketch-accumulate call (projection + contraction kernels)
-               against MI355X's 8 TB/s HBM peak, timed with HIP events on the
-               stream the kernels run on;
+               against MI355X's 8 TB/s HBM peak: HIP events on the kernels'
+               stream around M*K back-to-back calls over the rotating inputs;
   merge        the fused merge against the same peak;
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
@@ -177,19 +177,11 @@ def main():
     W = wl.layer_weight(w, args.layer, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
         S.zero_()
-        for m, (X, dY) in enumerate(sets[i % nsets]):
-            if ev is not None:
-                ev[0][m].record(stream)
+        for X, dY in sets[i % nsets]:
             lg.sketch_accumulate(X, dY, seed, r, S)
-            if ev is not None:
-                ev[1][m].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
         lg.merge_update(W, S, seed, r, scale)
-        if ev is not None:
-            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -208,20 +200,33 @@ def main():
     wall = time.perf_counter() - t_wall
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # Per-call durations with events on the kernels' stream.
-    call_ms, merge_ms = [], []
-    for i in range(args.steps):
-        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(M)],
-              [torch.cuda.Event(enable_timing=True) for _ in range(M)],
-              torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        step(i, ev)
-        torch.cuda.synchronize()
-        call_ms += [ev[0][m].elapsed_time(ev[1][m]) for m in range(M)]
-        merge_ms.append(ev[2].elapsed_time(ev[3]))
-    call_ms.sort()
-    merge_ms.sort()
-    t_call = sum(call_ms) / len(call_ms) * 1e-3
-    t_merge = sum(merge_ms) / len(merge_ms) * 1e-3
+    # Per-launch durations, live, with events on the kernels' stream: M*K
+    # back-to-back sketch calls over the same rotating inputs, then merges
+    # over enough copies of W to exceed the MALL (in a step, W was last
+    # touched a whole step earlier).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    n_calls = args.steps * M
+    ev0.record(stream)
+    for i in range(n_calls):
+        X, dY = sets[(i // M) % nsets][i % M]
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_call = ev0.elapsed_time(ev1) / n_calls * 1e-3
+    n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
+    Ws = [W.clone() for _ in range(n_w)]
+    for Wc in Ws:
+        lg.merge_update(Wc, S, seed, r, scale)
+    torch.cuda.synchronize()
+    n_merges = max(args.steps, 2 * n_w)
+    ev0.record(stream)
+    for i in range(n_merges):
+        lg.merge_update(Ws[i % n_w], S, seed, r, scale)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_merge = ev0.elapsed_time(ev1) / n_merges * 1e-3
+    del Ws
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
     sk_gbs = sb / t_call / 1e9
@@ -262,8 +267,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_call": sb,
             "avg_call_us": t_call * 1e6,
-            "p10_call_us": call_ms[len(call_ms) // 10] * 1e3,
-            "p90_call_us": call_ms[(9 * len(call_ms)) // 10] * 1e3,
+            "calls_timed": n_calls,
         },
         "merge": {
             "kernel": "merge_kernel",
@@ -274,6 +278,8 @@ def main():
             "frac": mg_gbs / HBM_PEAK_GBS,
             "algorithmic_bytes": mb,
             "avg_us": t_merge * 1e6,
+            "merges_timed": n_merges,
+            "weight_copies_rotated": n_w,
         },
         "kernel_source_sha": kernel_source_sha(),
     }
