@@ -15,6 +15,7 @@ Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn1536]
+       python bench.py --sweep    (per-layer table, one JSON line per layer and rank)
 """
 
 from __future__ import annotations
@@ -112,6 +113,73 @@ def cpu_baseline(w, layer, r, seed, budget_s: float):
     }
 
 
+def sweep(steps: int):
+    """Per-layer table: every layer and rank of every workload, one JSON line
+    each.  Sketch calls are timed back to back over enough distinct seeded
+    inputs to exceed the MALL; merges over enough copies of W."""
+    import torch
+
+    import rank_gradient_sketching_accumulate_amd as lg
+    import workloads as wl
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    seen = set()
+    for name, w in wl.WORKLOADS.items():
+        for li, L in enumerate(w.layers):
+            for r in w.ranks:
+                key = (w.T, L.d, L.k, r)
+                if key in seen:
+                    continue
+                seen.add(key)
+                T, d, k = w.T, L.d, L.k
+                per = 2 * T * (k + d)
+                ns = max(1, math.ceil(2.5 * MALL_BYTES / per))
+                ins = [wl.layer_inputs(w, li, m, device=dev) for m in range(ns)]
+                S = torch.zeros((d, r), dtype=torch.float32, device=dev)
+                seed = wl.sign_seed(li)
+                for X, dY in ins:
+                    lg.sketch_accumulate(X, dY, seed, r, S)
+                torch.cuda.synchronize()
+                n = max(steps, 2 * ns)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for j in range(n):
+                    X, dY = ins[j % ns]
+                    lg.sketch_accumulate(X, dY, seed, r, S)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_call = e0.elapsed_time(e1) / n * 1e-3
+                del ins
+                torch.cuda.empty_cache()
+                n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
+                Ws = [wl.layer_weight(w, li, device=dev) for _ in range(min(n_w, 4))]
+                while len(Ws) < n_w:
+                    Ws.append(Ws[len(Ws) % 4].clone())
+                for Wc in Ws:
+                    lg.merge_update(Wc, S, seed, r, w.scales[-1])
+                torch.cuda.synchronize()
+                nm = max(steps, 2 * n_w)
+                e0.record(stream)
+                for j in range(nm):
+                    lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_merge = e0.elapsed_time(e1) / nm * 1e-3
+                del Ws, S
+                torch.cuda.empty_cache()
+                sb, mb = sketch_bytes(T, k, d, r), merge_bytes(d, k, r)
+                print(json.dumps({
+                    "workload": name, "layer": L.name, "T": T, "d": d, "k": k, "r": r,
+                    "sketch_call_us": t_call * 1e6, "sketch_tokens_per_s": T / t_call,
+                    "sketch_GBps": sb / t_call / 1e9, "sketch_frac": sb / t_call / 1e9 / HBM_PEAK_GBS,
+                    "merge_us": t_merge * 1e6, "merge_GBps": mb / t_merge / 1e9,
+                    "merge_frac": mb / t_merge / 1e9 / HBM_PEAK_GBS,
+                    "kernel_source_sha": kernel_source_sha(),
+                }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-layer table over every workload, layer and rank (one JSON line each)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -146,6 +216,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     lg.load_library()
+
+    if args.sweep:
+        sweep(args.steps)
+        return
 
     if args.calibrate_copy:
         n = 2**29  # 1 GiB of int16
