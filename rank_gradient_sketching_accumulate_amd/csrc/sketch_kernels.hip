@@ -186,15 +186,18 @@ size_t proj_small_lds_bytes(int NB, int ncb) {
 // seven 32-column steps in flight in a register ring.
 // ===========================================================================
 template <int NB, int MBW, int WK>
-__global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(ProjParams p) {
   constexpr int RP = 16 * NB;
   constexpr int WT = 4 / WK;
   constexpr int TT = WT * 16 * MBW;
   constexpr int SROW = 9;  // 8 dwords of sign bits + 1 pad dword (bank spread)
   constexpr int NGEN = (RP * WK + 255) / 256;
   constexpr int RED = WK > 1 ? (WK - 1) * WT * NB * 256 : 4;
+  static_assert(RED <= 2 * WK * RP * SROW, "the k-split sums reuse the sign buffers");
   __shared__ uint32_t sbits[2][WK * RP * SROW];
-  __shared__ float red[RED];
+  // After the last round (which ends with a barrier) the sign buffers are free
+  // and hold the partial sums of the WK wave columns.
+  float* const red = reinterpret_cast<float*>(&sbits[0][0]);
   __shared__ int s_last;
 
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
@@ -884,15 +887,17 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     pl.n_k = 1;
     pl.cbs_per = pl.ncb;
   } else {
-    // Waves along k (WK) so that RP*WK <= 256 sign blocks per round; MBW keeps
-    // the accumulators within 128 registers.
-    int WK = RP >= 256 ? 1 : (RP >= 128 ? 2 : 4);
-    if (WK > pl.ncb) WK = pl.ncb >= 2 ? 2 : 1;
-    int MBW = 32 / pl.NB;
+    // Four waves along k (WK) sharing one token tile, so that each expanded
+    // sign operand feeds MBW MFMAs and the grid still has a few hundred
+    // workgroups of 32-64 tokens; MBW keeps the accumulators within 128
+    // registers (two waves per SIMD).
+    int WK = pl.ncb >= 4 ? 4 : (pl.ncb >= 2 ? 2 : 1);
+    int MBW = pl.NB >= 8 ? 2 : 32 / pl.NB;
     if (MBW > 4) MBW = 4;
     if (MBW < 1) MBW = 1;
     auto tiles = [&](int mbw, int wk) { return (T32 + (4 / wk) * 16 * mbw - 1) / ((4 / wk) * 16 * mbw); };
-    while (MBW > 1 && tiles(MBW, WK) < 512) MBW >>= 1;
+    // (rank >= 128 keeps two token blocks per wave and splits k instead)
+    while (pl.NB < 8 && MBW > 1 && tiles(MBW, WK) < 512) MBW >>= 1;
     MBW = env_int("LOGRA_PROJ_MB", MBW);
     WK = env_int("LOGRA_PROJ_WK", WK);
     pl.MBW = MBW;
@@ -901,8 +906,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     // The contraction reads whole 32-token steps of P: cover them all, so the
     // tokens in [T, Tpad) hold P = 0 written by the projection (X reads as 0).
     pl.n_tt = (int)((T32 + TT - 1) / TT);
+    // Column splits across workgroups (fp32 partials, last arriver sums) until
+    // about 512 workgroups: two per CU.
     int64_t nk = 1;
-    if (pl.n_tt < 256) nk = (256 + pl.n_tt - 1) / pl.n_tt;
+    if (pl.n_tt < 512) nk = (512 + pl.n_tt - 1) / pl.n_tt;
     const int64_t rounds = (pl.ncb + WK - 1) / WK;
     if (nk > rounds) nk = rounds;
     nk = env_int("LOGRA_PROJ_NK", (int)nk);
@@ -1019,9 +1026,10 @@ bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   LOGRA_PROJ(4, 1, 1) LOGRA_PROJ(4, 2, 1) LOGRA_PROJ(4, 4, 1)
   LOGRA_PROJ(4, 1, 2) LOGRA_PROJ(4, 2, 2) LOGRA_PROJ(4, 4, 2)
   LOGRA_PROJ(4, 1, 4) LOGRA_PROJ(4, 2, 4) LOGRA_PROJ(4, 4, 4)
-  LOGRA_PROJ(8, 1, 1) LOGRA_PROJ(8, 2, 1) LOGRA_PROJ(8, 4, 1)
-  LOGRA_PROJ(8, 1, 2) LOGRA_PROJ(8, 2, 2) LOGRA_PROJ(8, 4, 2)
-  LOGRA_PROJ(16, 1, 1) LOGRA_PROJ(16, 2, 1)
+  LOGRA_PROJ(8, 1, 1) LOGRA_PROJ(8, 2, 1)
+  LOGRA_PROJ(8, 1, 2) LOGRA_PROJ(8, 2, 2)
+  LOGRA_PROJ(16, 1, 1) LOGRA_PROJ(16, 2, 1) LOGRA_PROJ(16, 1, 2) LOGRA_PROJ(16, 2, 2)
+  LOGRA_PROJ(16, 1, 4) LOGRA_PROJ(16, 2, 4) LOGRA_PROJ(8, 1, 4) LOGRA_PROJ(8, 2, 4)
 #undef LOGRA_PROJ
   return false;
 }

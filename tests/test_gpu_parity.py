@@ -193,6 +193,8 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 0},
     {"LOGRA_CON_WM": 2},
     {"LOGRA_CON_WM": 4, "LOGRA_CON_TS": 2},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_WK": 4, "LOGRA_PROJ_MB": 2},
+    {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_WK": 4, "LOGRA_PROJ_MB": 1, "LOGRA_PROJ_NK": 2},
 ]
 
 
