@@ -139,9 +139,18 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
     cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
     cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
+    if (pl.use_part) {
+      cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
+      cp.part_split = d * 16 * pl.NB;
+    }
     if (!contract_launch(pl, cp, stream)) return fail(LOGRA_ERR_RANGE, "no contraction kernel for this tile");
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "contraction launch");
+    if (pl.use_part) {
+      reduce_launch(pl, cp, stream);
+      e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
+    }
     return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");

@@ -40,24 +40,30 @@ struct ContractParams {
   int n_dt, n_ts;  // d tiles, token splits
   int64_t ksp;     // 32-token steps per token split
   int atomic_out;  // 1 when several workgroups add into the same S tile
+  float* part;      // non-null: token split ts stores its tile at part + ts*part_split instead
+  int64_t part_split;  // floats per split (d x 16*NB, row stride 16*NB)
 };
 
 struct SketchPlan {
   int NB;                 // padded rank / 16 (power of two)
   int small_proj;         // 1: proj_small_kernel (all signs of k in LDS)
   int MBW, WK;            // projection: 16-token blocks per wave, waves along k
+  int PNW;                // projection (round-based): waves per workgroup (4 or 8)
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)
   int WM;                 // contraction row groups per workgroup (cvar 5)
   int n_dt, n_ts;
   int64_t ksp;
-  size_t off_counters, off_phi, off_plo, off_part, total;
+  int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce
+  size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };
 
 SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r);
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s);
 bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s);
+// S += sum over token splits of the stored partial tiles (use_part plans).
+void reduce_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Merge W <- RNE(W - scale_eff * U s).

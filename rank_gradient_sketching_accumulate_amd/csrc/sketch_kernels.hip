@@ -185,19 +185,21 @@ size_t proj_small_lds_bytes(int NB, int ncb) {
 // it multiplies the current ones, and every wave keeps X loads for the next
 // seven 32-column steps in flight in a register ring.
 // ===========================================================================
-template <int NB, int MBW, int WK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(ProjParams p) {
+template <int NB, int MBW, int WK, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void proj_kernel(ProjParams p) {
   constexpr int RP = 16 * NB;
-  constexpr int WT = 4 / WK;
+  constexpr int NT = NW * 64;  // threads
+  constexpr int WT = NW / WK;
   constexpr int TT = WT * 16 * MBW;
   constexpr int SROW = 9;  // 8 dwords of sign bits + 1 pad dword (bank spread)
-  constexpr int NGEN = (RP * WK + 255) / 256;
+  constexpr int NGEN = (RP * WK + NT - 1) / NT;
   constexpr int RED = WK > 1 ? (WK - 1) * WT * NB * 256 : 4;
-  static_assert(RED <= 2 * WK * RP * SROW, "the k-split sums reuse the sign buffers");
-  __shared__ uint32_t sbits[2][WK * RP * SROW];
+  constexpr int SB = 2 * WK * RP * SROW;
+  __shared__ uint32_t smem[SB > RED ? SB : RED];
+  uint32_t (*const sbits)[WK * RP * SROW] = reinterpret_cast<uint32_t (*)[WK * RP * SROW]>(smem);
   // After the last round (which ends with a barrier) the sign buffers are free
   // and hold the partial sums of the WK wave columns.
-  float* const red = reinterpret_cast<float*>(&sbits[0][0]);
+  float* const red = reinterpret_cast<float*>(smem);
   __shared__ int s_last;
 
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto gen = [&](int j, int buf) {
 #pragma unroll
     for (int q = 0; q < NGEN; ++q) {
-      const int b = threadIdx.x + 256 * q;
+      const int b = threadIdx.x + NT * q;
       if (b < RP * WK) {
         const int row = b % RP, wkk = b / RP;
         const int cb = cbb + j * WK + wkk;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (!s_last) return;
   // Walk the tile in the units the waves stored: four consecutive tokens of
   // one column (16 bytes of fp32 per split).
-  for (int v = threadIdx.x; v < TT * RP / 4; v += 256) {
+  for (int v = threadIdx.x; v < TT * RP / 4; v += NT) {
     const int col = v % RP;
     const int64_t tq = t0 + 4 * (int64_t)(v / RP);
     const int64_t e0 = pk_index(tq, col, NB);
@@ -409,27 +411,65 @@ __device__ __forceinline__ void transpose_dy(const u32x2 (&y)[8], u32x4 (&a)[kDC
     }
 }
 
-template <int NBW>
-__device__ __forceinline__ void store_s_tile(const ContractParams& p, f32x4 (&acc)[kDC][NBW], int64_t d0w,
-                                             int nb0, int g, int i) {
+// Stores a wave's finished 64 x 16*NBW tile of S.  The store mode and the
+// bounds checks are decided once per tile (interior tiles need none), not
+// once per element.
+template <int NBW, int MODE>
+__device__ __forceinline__ void store_s_tile_mode(const ContractParams& p, const f32x4 (&acc)[kDC][NBW], int64_t d0w,
+                                                  int nb0, int g, int i, int ts, bool full) {
+  float* const base = MODE == 0 ? p.part + (int64_t)ts * p.part_split : p.S;
+  const int64_t ld = MODE == 0 ? 16 * p.NB : p.lds;
 #pragma unroll
   for (int c = 0; c < kDC; ++c)
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const int cc = 16 * (nb0 + nb) + i;
-      if (cc >= p.r) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = d0w + (int64_t)kDC * (4 * g + e) + c;
-        if (row >= p.d) continue;
-        float* dst = p.S + row * p.lds + cc;
-        const float val = acc[c][nb][e] * p.inv_sqrt_r;
-        if (p.atomic_out)
-          atomicAdd(dst, val);
-        else
-          *dst += val;
+        if (full || (cc < p.r && row < p.d)) {
+          float* dst = base + row * ld + cc;
+          const float val = acc[c][nb][e] * p.inv_sqrt_r;
+          if constexpr (MODE == 0)
+            *dst = val;
+          else if constexpr (MODE == 1)
+            atomicAdd(dst, val);
+          else
+            *dst += val;
+        }
       }
     }
+}
+
+template <int NBW>
+__device__ __forceinline__ void store_s_tile(const ContractParams& p, const f32x4 (&acc)[kDC][NBW], int64_t d0w,
+                                             int nb0, int g, int i, int ts) {
+  const bool full = d0w + 16 * kDC <= p.d && 16 * (nb0 + NBW) <= p.r;
+  if (p.part) {
+    if (full) store_s_tile_mode<NBW, 0>(p, acc, d0w, nb0, g, i, ts, true);
+    else store_s_tile_mode<NBW, 0>(p, acc, d0w, nb0, g, i, ts, false);
+  } else if (p.atomic_out) {
+    if (full) store_s_tile_mode<NBW, 1>(p, acc, d0w, nb0, g, i, ts, true);
+    else store_s_tile_mode<NBW, 1>(p, acc, d0w, nb0, g, i, ts, false);
+  } else {
+    if (full) store_s_tile_mode<NBW, 2>(p, acc, d0w, nb0, g, i, ts, true);
+    else store_s_tile_mode<NBW, 2>(p, acc, d0w, nb0, g, i, ts, false);
+  }
+}
+
+// Adds one finished value of S (the LDS-reduced paths): into the caller's S
+// (atomically when several token splits share the tile), or as a plain store
+// into the split's partial tile.
+__device__ __forceinline__ void put_s(const ContractParams& p, int ts, int64_t row, int cc, float val) {
+  if (p.part) {
+    p.part[(int64_t)ts * p.part_split + row * (16 * p.NB) + cc] = val;
+  } else {
+    float* dst = p.S + row * p.lds + cc;
+    if (p.atomic_out)
+      atomicAdd(dst, val);
+    else
+      *dst += val;
+  }
 }
 
 // Small ranks (NB <= 4): eight waves share 64 rows of S and take every
@@ -628,7 +668,7 @@ __global__ __launch_bounds__(256) void contract_lds_kernel(ContractParams p) {
       }
     }
   }
-  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
+  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
 }
 
 // Larger ranks on big problems: eight waves, each owning 64 rows x 128
@@ -727,7 +767,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
       }
     }
   }
-  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
+  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
 }
 
 // General tiling for larger ranks: NW waves arranged as WM row groups (64
@@ -810,7 +850,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 
   if constexpr (WT == 1) {
-    store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i);
+    store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
   } else {
     // Sum the WT token lanes of every (row group, column group) through LDS,
     // one 16-row block (c) at a time.
@@ -832,18 +872,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int gg = ln >> 4, ii = ln & 15;
         const int cc = 16 * ((gm % WN) * NBW + nb) + ii;
         const int64_t row = ((int64_t)dt * WM + gm / WN) * 16 * kDC + (int64_t)kDC * (4 * gg + e) + c;
-        if (cc < p.r && row < p.d) {
-          float* dst = p.S + row * p.lds + cc;
-          const float val = sum * p.inv_sqrt_r;
-          if (p.atomic_out)
-            atomicAdd(dst, val);
-          else
-            *dst += val;
-        }
+        if (cc < p.r && row < p.d) put_s(p, ts, row, cc, sum * p.inv_sqrt_r);
       }
       __syncthreads();
     }
   }
+}
+
+// S[row][c] += sum over token splits of part[ts][row][c]; one thread per four
+// columns of a row.
+__global__ __launch_bounds__(256) void sketch_reduce_kernel(ContractParams p, int n_ts) {
+  const int RP = 16 * p.NB;
+  const int nq = (p.r + 3) >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / nq;
+  if (row >= p.d) return;
+  const int c0 = 4 * (int)(idx - row * nq);
+  const float* src = p.part + row * RP + c0;
+  // Four splits' loads in flight at a time.
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  int t = 0;
+  for (; t + 4 <= n_ts; t += 4) {
+    s0 += *reinterpret_cast<const f32x4*>(src + (int64_t)t * p.part_split);
+    s1 += *reinterpret_cast<const f32x4*>(src + (int64_t)(t + 1) * p.part_split);
+    s2 += *reinterpret_cast<const f32x4*>(src + (int64_t)(t + 2) * p.part_split);
+    s3 += *reinterpret_cast<const f32x4*>(src + (int64_t)(t + 3) * p.part_split);
+  }
+  for (; t < n_ts; ++t) s0 += *reinterpret_cast<const f32x4*>(src + (int64_t)t * p.part_split);
+  const f32x4 sum = (s0 + s1) + (s2 + s3);
+  float* dst = p.S + row * p.lds + c0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (c0 + e < p.r) dst[e] += sum[e];
 }
 
 // ===========================================================================
@@ -900,16 +960,22 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     while (pl.NB < 8 && MBW > 1 && tiles(MBW, WK) < 512) MBW >>= 1;
     MBW = env_int("LOGRA_PROJ_MB", MBW);
     WK = env_int("LOGRA_PROJ_WK", WK);
+    // Eight-wave workgroups (two token rows) halve the sign generation per
+    // token at rank >= 128, where Philox costs more than the expansion.
+    int NW = env_int("LOGRA_PROJ_NW", k >= 8192 ? 8 : 4) == 8 ? 8 : 4;
+    if (NW == 8 && !(pl.NB >= 8 && MBW == 2 && WK >= 2)) NW = 4;
+    pl.PNW = NW;
     pl.MBW = MBW;
     pl.WK = WK;
-    TT = (4 / WK) * 16 * MBW;
+    TT = (NW / WK) * 16 * MBW;
     // The contraction reads whole 32-token steps of P: cover them all, so the
     // tokens in [T, Tpad) hold P = 0 written by the projection (X reads as 0).
     pl.n_tt = (int)((T32 + TT - 1) / TT);
     // Column splits across workgroups (fp32 partials, last arriver sums) until
-    // about 512 workgroups: two per CU.
+    // there are two waves per SIMD: 512 four-wave or 256 eight-wave groups.
+    const int64_t want = NW == 8 ? 256 : 512;
     int64_t nk = 1;
-    if (pl.n_tt < 512) nk = (512 + pl.n_tt - 1) / pl.n_tt;
+    if (pl.n_tt < want) nk = (want + pl.n_tt - 1) / pl.n_tt;
     const int64_t rounds = (pl.ncb + WK - 1) / WK;
     if (nk > rounds) nk = rounds;
     nk = env_int("LOGRA_PROJ_NK", (int)nk);
@@ -992,6 +1058,13 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   off += align_up((size_t)pl.Tpad * RP * 2, 256);
   pl.off_part = off;
   if (pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
+  // Token splits of the large-rank tilings store partial tiles (a plain,
+  // coalesced stream) that one small kernel sums into S: L2 retires fp32
+  // atomic adds at about one element per channel and clock.
+  pl.use_part = env_int("LOGRA_CON_PART", ((pl.cvar == 3 || pl.cvar == 4) && pl.n_ts >= 4) ? 1 : 0) && pl.n_ts > 1 &&
+                pl.cvar >= 1;
+  pl.off_cpart = off;
+  if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
   return pl;
 }
@@ -1012,10 +1085,15 @@ bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
     return false;
   }
   const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, 8);
-#define LOGRA_PROJ(nb, mb, wk)                                                            \
-  if (pl.NB == nb && pl.MBW == mb && pl.WK == wk) {                                       \
-    hipLaunchKernelGGL((proj_kernel<nb, mb, wk>), dim3(grid), dim3(256), 0, s, p);        \
-    return true;                                                                          \
+#define LOGRA_PROJ(nb, mb, wk)                                                                \
+  if (pl.NB == nb && pl.MBW == mb && pl.WK == wk && pl.PNW == 4) {                            \
+    hipLaunchKernelGGL((proj_kernel<nb, mb, wk, 4>), dim3(grid), dim3(256), 0, s, p);         \
+    return true;                                                                              \
+  }
+#define LOGRA_PROJ8(nb, mb, wk)                                                               \
+  if (pl.NB == nb && pl.MBW == mb && pl.WK == wk && pl.PNW == 8) {                            \
+    hipLaunchKernelGGL((proj_kernel<nb, mb, wk, 8>), dim3(grid), dim3(512), 0, s, p);         \
+    return true;                                                                              \
   }
   LOGRA_PROJ(1, 1, 1) LOGRA_PROJ(1, 2, 1) LOGRA_PROJ(1, 4, 1)
   LOGRA_PROJ(1, 1, 2) LOGRA_PROJ(1, 2, 2) LOGRA_PROJ(1, 4, 2)
@@ -1030,8 +1108,15 @@ bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   LOGRA_PROJ(8, 1, 2) LOGRA_PROJ(8, 2, 2)
   LOGRA_PROJ(16, 1, 1) LOGRA_PROJ(16, 2, 1) LOGRA_PROJ(16, 1, 2) LOGRA_PROJ(16, 2, 2)
   LOGRA_PROJ(16, 1, 4) LOGRA_PROJ(16, 2, 4) LOGRA_PROJ(8, 1, 4) LOGRA_PROJ(8, 2, 4)
+  LOGRA_PROJ8(8, 2, 2) LOGRA_PROJ8(8, 2, 4) LOGRA_PROJ8(16, 2, 2) LOGRA_PROJ8(16, 2, 4)
+#undef LOGRA_PROJ8
 #undef LOGRA_PROJ
   return false;
+}
+
+void reduce_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s) {
+  const int64_t n = p.d * ((p.r + 3) / 4);
+  hipLaunchKernelGGL(sketch_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, pl.n_ts);
 }
 
 bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s) {
