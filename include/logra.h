@@ -151,7 +151,9 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v,
 logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out,
                          hipStream_t stream);
 
-/* Bytes of per-stream scratch logra_sketch_accumulate needs for T tokens at rank r. */
+/* Upper bound on the per-stream scratch logra_sketch_accumulate allocates for
+ * T tokens at rank r, over layer shapes up to 2^20 x 2^20 (P as a bf16 hi/lo
+ * pair, column-split and token-split partial sums, a 4 KB head of counters). */
 size_t logra_workspace_bytes(int64_t T, int32_t r);
 
 /* Static text for a status code. */

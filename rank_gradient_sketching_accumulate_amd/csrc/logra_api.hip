@@ -139,6 +139,7 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
     cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
     cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
+    cp.ts_major = env_int("LOGRA_CON_TSMAJOR", 0);
     if (pl.use_part) {
       cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
       cp.part_split = d * 16 * pl.NB;
@@ -245,12 +246,15 @@ logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out, hipSt
 
 size_t logra_workspace_bytes(int64_t T, int32_t r) {
   if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
-  // The largest plan over k and d for this T and r.
+  // The largest plan over k and d (powers of two up to 2^20) for this T and
+  // r.  The contraction's partial tiles grow with d only until the token
+  // splits shrink, so the maximum is reached inside this range.
   size_t best = 0;
-  for (int64_t k = 256; k <= ((int64_t)1 << 20); k *= 2) {
-    const SketchPlan pl = plan_sketch(T, k, 1 << 20, r);
-    if (pl.total > best) best = pl.total;
-  }
+  for (int64_t k = 256; k <= ((int64_t)1 << 20); k *= 2)
+    for (int64_t d = 256; d <= ((int64_t)1 << 20); d *= 2) {
+      const SketchPlan pl = plan_sketch(T, k, d, r);
+      if (pl.total > best) best = pl.total;
+    }
   return best;
 }
 

@@ -40,6 +40,7 @@ struct ContractParams {
   int n_dt, n_ts;  // d tiles, token splits
   int64_t ksp;     // 32-token steps per token split
   int atomic_out;  // 1 when several workgroups add into the same S tile
+  int ts_major;     // tile kernel: token split is the slow index of the grid
   float* part;      // non-null: token split ts stores its tile at part + ts*part_split instead
   int64_t part_split;  // floats per split (d x 16*NB, row stride 16*NB)
 };
@@ -53,6 +54,7 @@ struct SketchPlan {
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)
   int WM;                 // contraction row groups per workgroup (cvar 5)
+  int few_ts;             // tall S: at most one round of workgroups, few token splits
   int n_dt, n_ts;
   int64_t ksp;
   int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce

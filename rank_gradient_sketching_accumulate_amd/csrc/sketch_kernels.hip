@@ -786,8 +786,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   static_assert(WT * WM * WN == NW, "wave arrangement");
   __shared__ float red[WT > 1 ? NW * CH : 4];
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int dt = lin / p.n_ts;
-  const int ts = lin - dt * p.n_ts;
+  // Token splits slowest: an XCD's workgroups share one token window, so the
+  // P rows they all read stay in its L2 (P of a whole microbatch need not).
+  const int ts = p.ts_major ? lin / p.n_dt : lin % p.n_ts;
+  const int dt = p.ts_major ? lin - ts * p.n_dt : lin / p.n_ts;
+  if (ts >= p.n_ts) return;
   if (dt >= p.n_dt) return;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -999,9 +1002,13 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     // Token-lane tiles (64 rows per workgroup, few token splits) unless the
     // rank is 256 and the microbatch long: there every 64-row tile would read
     // eight times the dY bytes in P, and the 256 x 256 tiles win.
-    const int tile = env_int("LOGRA_CON_TILE", (pl.NB == 8 || T <= 8192) ? 1 : 0);
-    const int big = env_int("LOGRA_CON_BIG", -1);
     const int64_t bd8 = pl.NB == 8 ? 8 * 16 * kDC : 4 * 16 * kDC;
+    // Large d: the 512 x 128 / 256 x 256 tiles read P from L2 only d/bd8
+    // times and, with at least 36 row tiles, need only a few token splits.
+    const bool tall = (d + bd8 - 1) / bd8 >= 36;
+    pl.few_ts = tall ? 1 : 0;
+    const int tile = env_int("LOGRA_CON_TILE", tall ? 0 : ((pl.NB == 8 || T <= 8192) ? 1 : 0));
+    const int big = env_int("LOGRA_CON_BIG", tall ? 1 : -1);
     const bool use_big = big >= 0 ? big != 0 : ((d + bd8 - 1) / bd8) * (nks / 16) >= 256;
     if (tile) {
       // NB = 8: 2 column groups; NB = 16: 4 column groups; WM row groups.
@@ -1027,7 +1034,11 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   int64_t n_ts = (384 + pl.n_dt - 1) / pl.n_dt;
   int64_t max_ts = nks / min_steps;
   if (max_ts < 1) max_ts = 1;
-  if (pl.cvar >= 3) {
+  if (pl.cvar >= 3 && pl.few_ts) {
+    n_ts = 256 / pl.n_dt;  // one round of 256 eight-wave workgroups at most
+    if (n_ts < 1) n_ts = 1;
+    if (n_ts > 8) n_ts = 8;
+  } else if (pl.cvar >= 3) {
     // One eight-wave workgroup per CU (256 on MI355X): fill whole rounds of
     // the chip, preferring fewer token splits (less atomic traffic into S).
     double best = 0.0;
@@ -1061,7 +1072,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
-  pl.use_part = env_int("LOGRA_CON_PART", ((pl.cvar == 3 || pl.cvar == 4) && pl.n_ts >= 4) ? 1 : 0) && pl.n_ts > 1 &&
+  pl.use_part = env_int("LOGRA_CON_PART", ((pl.cvar == 3 || pl.cvar == 4) && pl.n_ts >= 3) ? 1 : 0) && pl.n_ts > 1 &&
                 pl.cvar >= 1;
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
