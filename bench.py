@@ -300,6 +300,40 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     t_merge = ev0.elapsed_time(ev1) / n_merges * 1e-3
+
+    # Streaming ceilings measured on this machine for the same bytes: the sketch
+    # call's two input streams read as two launches (X, then dY) over the same
+    # rotating inputs, and as one launch over windows of one buffer larger than
+    # the MALL; the merge's W as an in-place read-modify-write over the copies.
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev0.record(stream)
+    for i in range(n_calls):
+        X, dY = sets[(i // M) % nsets][i % M]
+        lg.stream_read(X, sink)
+        lg.stream_read(dY, sink)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_read2 = ev0.elapsed_time(ev1) / n_calls * 1e-3
+    win = (2 * T * (k + d) + 15) // 16 * 16
+    n_win = max(4, math.ceil(2.5 * MALL_BYTES / win))
+    buf = torch.zeros(n_win * win, dtype=torch.uint8, device=dev)
+    for j in range(n_win):
+        lg.stream_read(buf[j * win:(j + 1) * win], sink)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(n_calls):
+        j = i % n_win
+        lg.stream_read(buf[j * win:(j + 1) * win], sink)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_read1 = ev0.elapsed_time(ev1) / n_calls * 1e-3
+    del buf
+    ev0.record(stream)
+    for i in range(n_merges):
+        Ws[i % n_w].mul_(1.0)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_rmw = ev0.elapsed_time(ev1) / n_merges * 1e-3
     del Ws
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
@@ -354,6 +388,15 @@ def main():
             "avg_us": t_merge * 1e6,
             "merges_timed": n_merges,
             "weight_copies_rotated": n_w,
+        },
+        "ceiling": {
+            "what": "streaming reads/writes of the same bytes on this box (logra_stream_read; torch in-place mul for W)",
+            "sketch_bytes_one_read_us": t_read1 * 1e6,
+            "sketch_bytes_two_reads_us": t_read2 * 1e6,
+            "sketch_frac_of_one_read": t_read1 / t_call,
+            "sketch_frac_of_two_reads": t_read2 / t_call,
+            "merge_w_rmw_us": t_rmw * 1e6,
+            "merge_frac_of_rmw": t_rmw / t_merge,
         },
         "kernel_source_sha": kernel_source_sha(),
     }

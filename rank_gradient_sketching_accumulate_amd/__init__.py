@@ -29,6 +29,7 @@ __all__ = [
     "rowadam_scale",
     "signs",
     "workspace_bytes",
+    "stream_read",
     "abi_version",
     "EXPORTED_SYMBOLS",
 ]
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "logra_merge_update",
     "logra_rowadam_scale",
     "logra_signs",
+    "logra_stream_read",
     "logra_workspace_bytes",
     "logra_status_string",
     "logra_last_error",
@@ -70,6 +72,8 @@ def _declare(lib):
     lib.logra_rowadam_scale.restype = ctypes.c_int
     lib.logra_signs.argtypes = [c_u64, c_i32, c_i64, c_vp, c_vp]
     lib.logra_signs.restype = ctypes.c_int
+    lib.logra_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_vp, c_vp]
+    lib.logra_stream_read.restype = ctypes.c_int
     lib.logra_workspace_bytes.argtypes = [c_i64, c_i32]
     lib.logra_workspace_bytes.restype = ctypes.c_size_t
     lib.logra_status_string.argtypes = [ctypes.c_int]
@@ -209,6 +213,21 @@ def signs(seed: int, r: int, k: int, device="cuda"):
     _check(lib.logra_signs(ctypes.c_uint64(seed & (2**64 - 1)), r, k, out.data_ptr() if k else None,
                            _stream_handle(out)))
     return out
+
+
+def stream_read(t, sink):
+    """Stream the bytes of the contiguous device tensor t (a measurement aid:
+    the read ceiling for those bytes); sink is a one-element int32 device
+    tensor that receives nothing in practice."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("t must be a contiguous device tensor")
+    if not isinstance(sink, torch.Tensor) or sink.dtype != torch.int32 or not sink.is_cuda:
+        raise TypeError("sink must be an int32 device tensor")
+    nbytes = t.numel() * t.element_size()
+    _check(load_library().logra_stream_read(t.data_ptr() if nbytes else None, nbytes, sink.data_ptr(),
+                                            _stream_handle(t)))
 
 
 def workspace_bytes(T: int, r: int) -> int:

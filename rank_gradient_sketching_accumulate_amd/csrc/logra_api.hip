@@ -244,6 +244,19 @@ logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out, hipSt
   return LOGRA_OK;
 }
 
+logra_status logra_stream_read(const void* ptr, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  g_last_error.clear();
+  if (bytes == 0) return LOGRA_OK;
+  if (!ptr || !sink) return fail(LOGRA_ERR_NULL, "ptr and sink must be non-null");
+  if (((uintptr_t)ptr & 15) || (bytes & 15) || ((uintptr_t)sink & 3))
+    return fail(LOGRA_ERR_ALIGN, "ptr must be 16-byte aligned, bytes a multiple of 16, sink 4-byte aligned");
+  if (bytes / 16 / 1024 >= ((size_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "bytes too large for one launch");
+  stream_read_launch(ptr, (int64_t)(bytes / 16), sink, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return LOGRA_OK;
+}
+
 size_t logra_workspace_bytes(int64_t T, int32_t r) {
   if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
   // The largest plan over k and d (powers of two up to 2^20) for this T and

@@ -101,6 +101,7 @@ constexpr int kRowAdamBlocks = 256;
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias,
                     float eps_rel, float* root, float* ssq, double* partial, double* scal, hipStream_t s);
 void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s);
+void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_t s);
 
 int env_int(const char* name, int dflt);
 

@@ -131,4 +131,29 @@ void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s) {
   hipLaunchKernelGGL(signs_kernel, dim3(grid), dim3(256), 0, s, seed, r, k, out);
 }
 
+// Streaming read of n16 16-byte words (a measurement aid: the read ceiling
+// for the same bytes a sketch call streams).  Four words per thread are in
+// flight; the xor of everything reaches *sink only for one value, so no load
+// can be dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                          uint32_t* sink) {
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t idx = base + 256 * u;
+    v[u] = idx < n16 ? src[idx] : u32x4{0u, 0u, 0u, 0u};
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  if (acc == 0x9E3779B9u) *sink = acc;
+}
+
+void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_t s) {
+  const int64_t grid = (n16 + 1023) / 1024;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const u32x4*>(ptr), n16, sink);
+}
+
 }  // namespace logra

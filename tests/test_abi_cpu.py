@@ -130,6 +130,15 @@ def test_signs_validation(lib):
     assert lib.logra_signs(0, 4, 0, None, None) == OK
 
 
+def test_stream_read_validation(lib):
+    assert lib.logra_stream_read(None, 0, None, None) == 0  # empty: no-op
+    assert lib.logra_stream_read(None, 16, FAKE, None) == 1
+    assert lib.logra_stream_read(FAKE, 16, None, None) == 1
+    assert lib.logra_stream_read(FAKE + 8, 16, FAKE, None) == 3  # misaligned base
+    assert lib.logra_stream_read(FAKE, 24, FAKE, None) == 3  # not a multiple of 16 bytes
+    assert lib.logra_stream_read(FAKE, 16, FAKE + 2, None) == 3  # misaligned sink
+
+
 def test_python_wrapper_type_checks(lib):
     import torch
 

@@ -487,6 +487,17 @@ def test_full_step_tiny_with_rowadam():
 # ---------------------------------------------------------------------------
 # Error paths with real device buffers
 # ---------------------------------------------------------------------------
+def test_stream_read_leaves_buffers_alone():
+    """The streaming-read measurement aid reads and discards: neither the
+    buffer nor (except for one xor value in 2^32) the sink changes."""
+    t = wl.random_tensor((3, 1000), 5, device=DEV)  # 12000 bytes, a ragged last thread block
+    t0 = t.clone()
+    sink = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    lg.stream_read(t, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(t, t0) and int(sink.item()) == -7
+
+
 def test_errors_on_device_buffers():
     X, dY = _ragged_inputs(64, 256, 64, 1)
     S = torch.zeros((64, 16), dtype=torch.float32, device=DEV)
