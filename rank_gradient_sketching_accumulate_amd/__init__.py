@@ -113,10 +113,20 @@ def _check(status: int):
         raise LograError(f"logra status {status} ({name}): {detail}", status)
 
 
-def _stream_handle(tensor) -> int:
-    import torch
+_raw_stream = None
 
-    return int(torch.cuda.current_stream(tensor.device).cuda_stream)
+
+def _stream_handle(tensor) -> int:
+    """The raw handle of torch's current HIP stream on the tensor's device."""
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+
+        # torch's own raw accessor avoids building a Stream object per call.
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = raw if raw is not None else (
+            lambda dev: int(torch.cuda.current_stream(dev).cuda_stream))
+    return int(_raw_stream(tensor.get_device()))
 
 
 def _need(t, dtype, name, ndim=2):

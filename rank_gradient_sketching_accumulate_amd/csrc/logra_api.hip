@@ -3,10 +3,12 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#include <unistd.h>
 
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 #include "../../include/logra.h"
@@ -80,6 +82,40 @@ logra_status arena_get(int kind, hipStream_t stream, size_t need, void** out) {
   return LOGRA_OK;
 }
 
+// Launch plans depend only on the shape, unless a LOGRA_ variable in the
+// environment overrides a choice (tuning and tests): then the plan is worked
+// out afresh on every call.  Otherwise each thread keeps the plans it has
+// made, so a call costs one scan of the environment, not one lookup per knob.
+bool plan_overrides_present() {
+  for (char** e = environ; e && *e; ++e)
+    if (strncmp(*e, "LOGRA_", 6) == 0) return true;
+  return false;
+}
+
+SketchPlan sketch_plan_for(int64_t T, int64_t k, int64_t d, int r) {
+  if (plan_overrides_present()) return plan_sketch(T, k, d, r);
+  thread_local std::map<std::tuple<int64_t, int64_t, int64_t, int>, SketchPlan> plans;
+  const auto key = std::make_tuple(T, k, d, r);
+  auto it = plans.find(key);
+  if (it != plans.end()) return it->second;
+  if (plans.size() >= 1024) plans.clear();
+  const SketchPlan pl = plan_sketch(T, k, d, r);
+  plans.emplace(key, pl);
+  return pl;
+}
+
+MergePlan merge_plan_for(int64_t d, int64_t k, int r) {
+  if (plan_overrides_present()) return plan_merge(d, k, r);
+  thread_local std::map<std::tuple<int64_t, int64_t, int>, MergePlan> plans;
+  const auto key = std::make_tuple(d, k, r);
+  auto it = plans.find(key);
+  if (it != plans.end()) return it->second;
+  if (plans.size() >= 1024) plans.clear();
+  const MergePlan pl = plan_merge(d, k, r);
+  plans.emplace(key, pl);
+  return pl;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,7 +141,7 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     if (T > ((int64_t)1 << 31) || k > ((int64_t)1 << 31) || d > ((int64_t)1 << 31))
       return fail(LOGRA_ERR_SHAPE, "T, k and d must be below 2^31");
 
-    const SketchPlan pl = plan_sketch(T, k, d, r);
+    const SketchPlan pl = sketch_plan_for(T, k, d, r);
     // Kernels address X and dY through buffer descriptors with 32-bit byte
     // offsets (rows past T read as zero): each operand must span < 4 GiB.
     const uint64_t lim = ((uint64_t)1 << 32) - 4096;
@@ -117,6 +153,7 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     logra_status st = arena_get(kArenaSketch, stream, pl.total, &ws);
     if (st != LOGRA_OK) return st;
     char* base = static_cast<char*>(ws);
+    const float inv_sqrt_r = (float)(1.0 / sqrt((double)r));
 
     ProjParams pp{};
     pp.X = static_cast<const uint16_t*>(X);
@@ -136,10 +173,10 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     cp.lddy = lddy; cp.T = T; cp.d = d;
     cp.Phi = pp.Phi; cp.Plo = pp.Plo; cp.NB = pl.NB;
     cp.S = S; cp.lds = lds; cp.r = r;
-    cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
+    cp.inv_sqrt_r = inv_sqrt_r;
     cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
     cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
-    cp.ts_major = env_int("LOGRA_CON_TSMAJOR", 0);
+    cp.ts_major = pl.ts_major;
     if (pl.use_part) {
       cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
       cp.part_split = d * 16 * pl.NB;
@@ -178,7 +215,7 @@ logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ld
     if ((uint64_t)d * (uint64_t)ldw * 2 >= ((uint64_t)1 << 32) - 4096 ||
         (uint64_t)d * (uint64_t)ldu * 4 >= ((uint64_t)1 << 32) - 4096)
       return fail(LOGRA_ERR_SHAPE, "W or U spans 4 GiB or more; merge the rows in several calls");
-    const MergePlan pl = plan_merge(d, k, r);
+    const MergePlan pl = merge_plan_for(d, k, r);
     MergeParams mp{};
     mp.W = static_cast<uint16_t*>(W);
     mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;

@@ -58,6 +58,7 @@ struct SketchPlan {
   int n_dt, n_ts;
   int64_t ksp;
   int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce
+  int ts_major;           // contract_tile grid order (token split slowest)
   size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };
 

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
   constexpr int NW = 8;
   constexpr int TT = 16 * MBW;
   constexpr int SROW = 9;
-  extern __shared__ uint32_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
 
   const int tt = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -140,26 +140,26 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
       for (int mb = 0; mb < MBW; ++mb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Eight-way sum of the column partials, one 16-token block at a time:
-  // every wave parks its partial in LDS, then each thread sums four
-  // consecutive tokens of one column and writes their hi/lo pair.
-  constexpr int CH = NB * 256;
-  float* red = reinterpret_cast<float*>(lds);
+  // every wave parks its accumulators in LDS as whole float4s (1 KB
+  // contiguous per column block), then each thread sums one float4 item
+  // (four consecutive tokens of one column) over the eight waves and writes
+  // their hi/lo pair.
+  constexpr int ITEMS = NB * 64;
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
   for (int mb = 0; mb < MBW; ++mb) {
     __syncthreads();
-    float* mine = red + w * CH;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[mb][nb][e];
+    for (int nb = 0; nb < NB; ++nb) red[w * ITEMS + nb * 64 + lane] = acc[mb][nb];
     __syncthreads();
-    for (int v = threadIdx.x; v < CH / 4; v += NW * 64) {
+    for (int v = threadIdx.x; v < ITEMS; v += NW * 64) {
       const int ln = v & 63, nb = v >> 6;  // lane (g, i) of wave 0's layout, column block
-      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sum = red[v];
 #pragma unroll
-      for (int q = 0; q < NW; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum[e] += red[q * CH + (nb * 4 + e) * 64 + ln];
+      for (int q = 1; q < NW; ++q) {
+        const f32x4 o = red[q * ITEMS + v];
+        sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+      }
       const int gg = ln >> 4, ii = ln & 15;
       const int64_t e0 = pk_index(t0 + 16 * mb + 4 * gg, 16 * nb + ii, NB);
       uint32_t h0, l0, h1, l1;
@@ -481,8 +481,10 @@ __device__ __forceinline__ void put_s(const ContractParams& p, int ts, int64_t r
 template <int NB, int DEPTH>
 __global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
   constexpr int NW = 8;
-  constexpr int CH = NB * 256;  // floats of one 16-row block of the tile
-  __shared__ float red[NW * CH];
+  // 16-row blocks of the tile reduced per LDS round (64 KB of partials).
+  constexpr int CPR = (kDC * NB * 256 * NW * 4 <= 65536) ? kDC : 65536 / (NB * 256 * NW * 4);
+  constexpr int ITEMS = CPR * NB * 64;  // float4 items per wave and round
+  __shared__ f32x4 red[NW * ITEMS];
   // Token splits vary fastest among consecutive logical ids, so the
   // workgroups that add into the same S tile share an XCD (and its L2).
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
@@ -548,35 +550,45 @@ __global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
     }
   }
 
-  // Eight-way sum through LDS, one 16-row block (c) at a time: every wave
-  // parks its partial, then each wave sums and stores one eighth of the block.
+  // Eight-way sum through LDS, CPR 16-row blocks per round: every wave parks
+  // its accumulators as whole float4s (one 1 KB contiguous write per block
+  // and column block), then each thread sums one float4 item of all eight
+  // waves (contiguous 16-byte reads) and adds its four rows into S.
+  static_assert(kDC % CPR == 0, "rounds must cover the tile");
 #pragma unroll
-  for (int c = 0; c < kDC; ++c) {
-    float* mine = red + wt * CH;
+  for (int c0 = 0; c0 < kDC; c0 += CPR) {
+    if (c0) __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int cr = 0; cr < CPR; ++cr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[c][nb][e];
+      for (int nb = 0; nb < NB; ++nb) red[wt * ITEMS + (cr * NB + nb) * 64 + lane] = acc[c0 + cr][nb];
     __syncthreads();
-    for (int v = threadIdx.x; v < CH; v += NW * 64) {
-      float sum = 0.f;
+    for (int v = threadIdx.x; v < ITEMS; v += NW * 64) {
+      f32x4 sum = red[v];
 #pragma unroll
-      for (int q = 0; q < NW; ++q) sum += red[q * CH + v];
-      const int ln = v & 63, ne = v >> 6;  // lane and (nb*4 + e) of the element
-      const int nb = ne >> 2, e = ne & 3;
+      for (int q = 1; q < NW; ++q) {
+        const f32x4 o = red[q * ITEMS + v];
+        sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+      }
+      const int ln = v & 63, cn = v >> 6;  // lane of the item, (cr, nb) of the item
+      const int cr = cn / NB, nb = cn - cr * NB;
       const int gg = ln >> 4, ii = ln & 15;
       const int cc = 16 * nb + ii;
-      const int64_t row = d0w + (int64_t)kDC * (4 * gg + e) + c;
-      if (cc < p.r && row < p.d) {
-        float* dst = p.S + row * p.lds + cc;
-        const float val = sum * p.inv_sqrt_r;
-        if (p.atomic_out)
-          atomicAdd(dst, val);
-        else
-          *dst += val;
+      if (cc < p.r) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t row = d0w + (int64_t)kDC * (4 * gg + e) + c0 + cr;
+          if (row < p.d) {
+            float* dst = p.S + row * p.lds + cc;
+            const float val = sum[e] * p.inv_sqrt_r;
+            if (p.atomic_out)
+              atomicAdd(dst, val);
+            else
+              *dst += val;
+          }
+        }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -1077,6 +1089,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
+  pl.ts_major = env_int("LOGRA_CON_TSMAJOR", 0);
   return pl;
 }
 
