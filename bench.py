@@ -10,7 +10,8 @@ its inputs from HBM.
 Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
   roofline     the sketch-accumulate call (projection + contraction kernels)
                against MI355X's 8 TB/s HBM peak: HIP events on the kernels'
-               stream around M*K back-to-back calls over the rotating inputs;
+               stream around M*K back-to-back calls over the rotating inputs,
+               queued behind a sleep kernel so that they measure GPU time;
   merge        the fused merge against the same peak;
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
@@ -68,6 +69,33 @@ def load_traffic(workload: str):
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
     return t.get("sketch_call_bytes")
+
+
+def gpu_time_per_call(torch, stream, fn, n):
+    """(GPU seconds, host seconds) per call of fn(i), i < n, issued back to
+    back.  The loop runs once untimed (which also measures how fast the host
+    issues it), then again behind a sleep kernel long enough for the host to
+    queue every call before the first timed launch, so the HIP events on
+    `stream` see GPU time only."""
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    host = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is not None:
+        sleep(int(min(2.4e9, max(2.4e6, 3.0 * host * 2.4e9))))  # cycles at about 2.4 GHz
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    h0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    host = time.perf_counter() - h0
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n * 1e-3, host / n
 
 
 def cpu_baseline(w, layer, r, seed, budget_s: float):
@@ -138,35 +166,18 @@ def sweep(steps: int):
                 ins = [wl.layer_inputs(w, li, m, device=dev) for m in range(ns)]
                 S = torch.zeros((d, r), dtype=torch.float32, device=dev)
                 seed = wl.sign_seed(li)
-                for X, dY in ins:
-                    lg.sketch_accumulate(X, dY, seed, r, S)
-                torch.cuda.synchronize()
                 n = max(steps, 2 * ns)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for j in range(n):
-                    X, dY = ins[j % ns]
-                    lg.sketch_accumulate(X, dY, seed, r, S)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                t_call = e0.elapsed_time(e1) / n * 1e-3
+                t_call, _ = gpu_time_per_call(
+                    torch, stream, lambda j: lg.sketch_accumulate(ins[j % ns][0], ins[j % ns][1], seed, r, S), n)
                 del ins
                 torch.cuda.empty_cache()
                 n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
                 Ws = [wl.layer_weight(w, li, device=dev) for _ in range(min(n_w, 4))]
                 while len(Ws) < n_w:
                     Ws.append(Ws[len(Ws) % 4].clone())
-                for Wc in Ws:
-                    lg.merge_update(Wc, S, seed, r, w.scales[-1])
-                torch.cuda.synchronize()
                 nm = max(steps, 2 * n_w)
-                e0.record(stream)
-                for j in range(nm):
-                    lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1])
-                e1.record(stream)
-                torch.cuda.synchronize()
-                t_merge = e0.elapsed_time(e1) / nm * 1e-3
+                t_merge, _ = gpu_time_per_call(
+                    torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]), nm)
                 del Ws, S
                 torch.cuda.empty_cache()
                 sb, mb = sketch_bytes(T, k, d, r), merge_bytes(d, k, r)
@@ -274,66 +285,49 @@ def main():
     wall = time.perf_counter() - t_wall
     step_ms = e0.elapsed_time(e1) / args.steps
 
-    # Per-launch durations, live, with events on the kernels' stream: M*K
-    # back-to-back sketch calls over the same rotating inputs, then merges
-    # over enough copies of W to exceed the MALL (in a step, W was last
-    # touched a whole step earlier).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # Per-launch durations, live, with events on the kernels' stream.  Each
+    # loop is issued twice: once untimed (which also measures how fast the
+    # host issues the calls), then behind a sleep kernel long enough for the
+    # host to queue the whole loop before the first timed launch, so the
+    # events see GPU time only (one Python call takes several microseconds,
+    # about as long as a small kernel).
+    def gpu_time(fn, n):
+        return gpu_time_per_call(torch, stream, fn, n)
+
+    # Sketch: M*K back-to-back calls over the same rotating inputs.
     n_calls = args.steps * M
-    ev0.record(stream)
-    for i in range(n_calls):
+
+    def sketch_call(i):
         X, dY = sets[(i // M) % nsets][i % M]
         lg.sketch_accumulate(X, dY, seed, r, S)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_call = ev0.elapsed_time(ev1) / n_calls * 1e-3
+
+    t_call, h_call = gpu_time(sketch_call, n_calls)
+    # Merge: over enough copies of W to exceed the MALL (in a step, W was
+    # last touched a whole step earlier).
     n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
     Ws = [W.clone() for _ in range(n_w)]
-    for Wc in Ws:
-        lg.merge_update(Wc, S, seed, r, scale)
-    torch.cuda.synchronize()
     n_merges = max(args.steps, 2 * n_w)
-    ev0.record(stream)
-    for i in range(n_merges):
-        lg.merge_update(Ws[i % n_w], S, seed, r, scale)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_merge = ev0.elapsed_time(ev1) / n_merges * 1e-3
+    t_merge, h_merge = gpu_time(lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale), n_merges)
 
-    # Streaming ceilings measured on this machine for the same bytes: the sketch
-    # call's two input streams read as two launches (X, then dY) over the same
-    # rotating inputs, and as one launch over windows of one buffer larger than
-    # the MALL; the merge's W as an in-place read-modify-write over the copies.
+    # Streaming ceilings measured on this machine for the same bytes, timed the
+    # same way: the sketch call's two input streams read as two launches (X,
+    # then dY) over the same rotating inputs, and as one launch over windows of
+    # one buffer larger than the MALL; the merge's W as an in-place
+    # read-modify-write over the copies.
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    ev0.record(stream)
-    for i in range(n_calls):
+
+    def read_two(i):
         X, dY = sets[(i // M) % nsets][i % M]
         lg.stream_read(X, sink)
         lg.stream_read(dY, sink)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_read2 = ev0.elapsed_time(ev1) / n_calls * 1e-3
+
+    t_read2, _ = gpu_time(read_two, n_calls)
     win = (2 * T * (k + d) + 15) // 16 * 16
     n_win = max(4, math.ceil(2.5 * MALL_BYTES / win))
     buf = torch.zeros(n_win * win, dtype=torch.uint8, device=dev)
-    for j in range(n_win):
-        lg.stream_read(buf[j * win:(j + 1) * win], sink)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for i in range(n_calls):
-        j = i % n_win
-        lg.stream_read(buf[j * win:(j + 1) * win], sink)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_read1 = ev0.elapsed_time(ev1) / n_calls * 1e-3
+    t_read1, _ = gpu_time(lambda i: lg.stream_read(buf[(i % n_win) * win:(i % n_win + 1) * win], sink), n_calls)
     del buf
-    ev0.record(stream)
-    for i in range(n_merges):
-        Ws[i % n_w].mul_(1.0)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_rmw = ev0.elapsed_time(ev1) / n_merges * 1e-3
+    t_rmw, _ = gpu_time(lambda i: Ws[i % n_w].mul_(1.0), n_merges)
     del Ws
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
@@ -376,6 +370,7 @@ def main():
             "algorithmic_bytes_per_call": sb,
             "avg_call_us": t_call * 1e6,
             "calls_timed": n_calls,
+            "host_us_per_call": h_call * 1e6,
         },
         "merge": {
             "kernel": "merge_kernel",
@@ -387,6 +382,7 @@ def main():
             "algorithmic_bytes": mb,
             "avg_us": t_merge * 1e6,
             "merges_timed": n_merges,
+            "host_us_per_call": h_merge * 1e6,
             "weight_copies_rotated": n_w,
         },
         "ceiling": {

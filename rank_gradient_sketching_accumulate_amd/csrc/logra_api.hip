@@ -176,7 +176,7 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     cp.inv_sqrt_r = inv_sqrt_r;
     cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
     cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
-    cp.ts_major = pl.ts_major;
+    cp.bands = pl.cbands;
     if (pl.use_part) {
       cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
       cp.part_split = d * 16 * pl.NB;

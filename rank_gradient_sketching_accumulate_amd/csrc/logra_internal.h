@@ -40,9 +40,9 @@ struct ContractParams {
   int n_dt, n_ts;  // d tiles, token splits
   int64_t ksp;     // 32-token steps per token split
   int atomic_out;  // 1 when several workgroups add into the same S tile
-  int ts_major;     // tile kernel: token split is the slow index of the grid
   float* part;      // non-null: token split ts stores its tile at part + ts*part_split instead
   int64_t part_split;  // floats per split (d x 16*NB, row stride 16*NB)
+  int bands;        // stream-K kernels: token bands, 1 or 8 (one per XCD; grid a multiple of 8)
 };
 
 struct SketchPlan {
@@ -58,7 +58,8 @@ struct SketchPlan {
   int n_dt, n_ts;
   int64_t ksp;
   int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce
-  int ts_major;           // contract_tile grid order (token split slowest)
+  int cgrid;              // contract_small / contract_tile: workgroups sharing the step units
+  int cbands;             // token bands of that split (1, or 8 = one per XCD)
   size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };
 

@@ -238,24 +238,22 @@ size_t align_up_m(size_t x, size_t a) { return (x + a - 1) / a * a; }
 MergePlan plan_merge(int64_t d, int64_t k, int r) {
   MergePlan pl{};
   pl.NK = r <= 32 ? 1 : (r <= 64 ? 2 : (r <= 128 ? 4 : 8));
-  // Tile per wave and chunk, chosen so that two waves fit per SIMD: two
-  // 16-row blocks x 64 columns (each expanded sign operand feeds both row
-  // blocks), except one 16-row block x 128 columns for r in (64, 128].
-  int NBW = pl.NK == 4 ? 1 : 2, CB = pl.NK == 4 ? 8 : 4;
-  auto units = [&](int nbw, int cb) {
-    return ((d + 64 * nbw - 1) / (64 * nbw)) * ((k + 16 * cb - 1) / (16 * cb));
-  };
-  if (NBW == 2 && units(2, CB) < 512) NBW = 1;
+  // Tile per wave and chunk (two waves fit per SIMD): one 16-row block x 64
+  // columns up to r = 128 with about 2048 workgroups; at r = 256, where the
+  // U operands and sign expansion cost more, two 16-row blocks (each expanded
+  // sign operand feeds both) with about 512 longer column ranges.  Measured
+  // with GPU-only timing over layers from 1536 x 1536 to 18944 x 3584.
+  int NBW = pl.NK == 8 ? 2 : 1, CB = 4;
   NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
   CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
   if (NBW == 2 && CB == 8 && pl.NK >= 4) CB = 4;  // would not fit two waves per SIMD
   pl.NBW = NBW;
   pl.CB = CB;
   pl.n_rb = (int)((d + 64 * NBW - 1) / (64 * NBW));
-  // Column ranges: as long as possible while about 1024 workgroups remain.
+  // Column ranges: as long as possible while about `target` workgroups remain.
   const int64_t CW = 16 * CB;
   const int64_t chunks = (k + CW - 1) / CW;
-  int64_t target = env_int("LOGRA_MERGE_WGS", 1024);
+  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK == 8 ? 512 : 2048);
   if (target < 1) target = 1;
   int64_t n_cr = (target + pl.n_rb - 1) / pl.n_rb;
   if (n_cr > chunks) n_cr = chunks;

@@ -472,10 +472,43 @@ __device__ __forceinline__ void put_s(const ContractParams& p, int ts, int64_t r
   }
 }
 
+// Stream-K split of a contraction: units are (row tile, 32-token step) pairs;
+// the grid takes them in equal contiguous runs, tile-major.  With p.bands = 8
+// the steps are first cut into eight token bands, one per XCD (workgroup ids
+// are dealt round-robin to the eight XCDs), and an XCD's workgroups share the
+// units of its band, so that its L2 holds only that band's rows of P.
+struct StreamK {
+  int64_t kb0, blen, u_beg, u_end;
+  __device__ __forceinline__ StreamK(const ContractParams& p, int64_t nks) {
+    const int B = p.bands;
+    const int band = B == 8 ? (int)(blockIdx.x & 7) : 0;
+    const int64_t gx = B == 8 ? gridDim.x >> 3 : gridDim.x;  // workgroups sharing the band
+    const int64_t jx = B == 8 ? blockIdx.x >> 3 : blockIdx.x;
+    kb0 = nks * band / B;
+    blen = nks * (band + 1) / B - kb0;
+    const int64_t units = (int64_t)p.n_dt * blen;
+    u_beg = units * jx / gx;
+    u_end = units * (jx + 1) / gx;
+  }
+  // The segment of the run that starts at unit u0 (one row tile, a range of
+  // steps); advances u0 past it.
+  __device__ __forceinline__ void segment(int64_t& u0, int& dt, int64_t& ks_beg, int64_t& ks_end) const {
+    dt = (int)(u0 / blen);
+    ks_beg = kb0 + (u0 - (int64_t)dt * blen);
+    ks_end = min(kb0 + blen, ks_beg + (u_end - u0));
+    u0 += ks_end - ks_beg;
+  }
+};
+
 // Small ranks (NB <= 4): eight waves share 64 rows of S and take every
-// eighth 32-token step of the workgroup's token range.  A step's dY rows and
-// P words travel together in one ring slot (DEPTH steps in flight), so waiting
-// for one step never waits for a later one.  dY comes through a buffer
+// eighth 32-token step, with the work split stream-K style (StreamK), so that
+// every workgroup does the same number of steps however the tiles divide
+// among the CUs.  A run crosses a few tile boundaries at most; the workgroup
+// keeps the tile's sums in registers over its part of the run and adds them
+// into S whenever the tile changes (atomically, unless the segment is the
+// whole tile).  A step's dY rows and P words
+// travel together in one ring slot (DEPTH steps in flight), so waiting for
+// one step never waits for a later one.  dY comes through a buffer
 // descriptor: token rows past T read as zero; columns past d only feed rows
 // of S that are not stored.
 template <int NB, int DEPTH>
@@ -485,106 +518,108 @@ __global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
   constexpr int CPR = (kDC * NB * 256 * NW * 4 <= 65536) ? kDC : 65536 / (NB * 256 * NW * 4);
   constexpr int ITEMS = CPR * NB * 64;  // float4 items per wave and round
   __shared__ f32x4 red[NW * ITEMS];
-  // Token splits vary fastest among consecutive logical ids, so the
-  // workgroups that add into the same S tile share an XCD (and its L2).
-  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int dt = lin / p.n_ts;
-  const int ts = lin - dt * p.n_ts;
-  if (dt >= p.n_dt) return;
 
-  const int lane = threadIdx.x & 63, wt = threadIdx.x >> 6;
+  // The wave index is uniform over the wave: keep it (and all derived
+  // addressing) in scalar registers.
+  const int lane = threadIdx.x & 63, wt = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, i = lane & 15;
-  const int64_t d0w = (int64_t)dt * 16 * kDC;
-  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
   const int64_t nks = (p.T + 31) >> 5;
-  const int64_t ks_beg = ts * p.ksp;
-  const int64_t ks_end = min(nks, ks_beg + p.ksp);
-  const int64_t ks0 = ks_beg + wt;
-  const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + NW - 1) / NW) : 0;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
   const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+  const StreamK sk(p, nks);
 
-  f32x4 acc[kDC][NB];
-#pragma unroll
-  for (int c = 0; c < kDC; ++c)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t u0 = sk.u_beg; u0 < sk.u_end;) {
+    int dt;
+    int64_t ks_beg, ks_end;
+    sk.segment(u0, dt, ks_beg, ks_end);
+    const bool whole = ks_beg == 0 && ks_end == nks;  // no other workgroup adds into this tile
 
-  u32x2 y[DEPTH][8];
-  u32x4 bh[DEPTH][NB], bl[DEPTH][NB];
-  auto issue = [&](int slot_y, int m) {
-    if (m >= nsteps) return;
-    const int64_t ks = ks0 + (int64_t)NW * m;
-    uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
+    const int64_t d0w = (int64_t)dt * 16 * kDC;
+    const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+    const int64_t ks0 = ks_beg + wt;
+    const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + NW - 1) / NW) : 0;
+
+    f32x4 acc[kDC][NB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[slot_y][e] = buf_load8(ry, off);
-      off += rowstep;
-    }
+    for (int c = 0; c < kDC; ++c)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int64_t o = ((ks * p.NB + nb) * 64 + lane) * 8;
-      bh[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
-      bl[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
-    }
-  };
+      for (int nb = 0; nb < NB; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x2 y[DEPTH][8];
+    u32x4 bh[DEPTH][NB], bl[DEPTH][NB];
+    auto issue = [&](int slot_y, int m) {
+      if (m >= nsteps) return;
+      const int64_t ks = ks0 + (int64_t)NW * m;
+      uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[slot_y][e] = buf_load8(ry, off);
+        off += rowstep;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t o = ((ks * p.NB + nb) * 64 + lane) * 8;
+        bh[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
+        bl[slot_y][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
+      }
+    };
 
 #pragma unroll
-  for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
-  for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
+    for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
+    for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) {
-      const int m = m0 + u;
-      if (m < nsteps) {
-        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
-        u32x4 a[kDC];
-        transpose_dy(y[u], a);
+      for (int u = 0; u < DEPTH; ++u) {
+        const int m = m0 + u;
+        if (m < nsteps) {
+          issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
+          u32x4 a[kDC];
+          transpose_dy(y[u], a);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int c = 0; c < kDC; ++c) {
-            acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
-            acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
-          }
+            for (int c = 0; c < kDC; ++c) {
+              acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
+              acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
+            }
+        }
       }
     }
-  }
 
-  // Eight-way sum through LDS, CPR 16-row blocks per round: every wave parks
-  // its accumulators as whole float4s (one 1 KB contiguous write per block
-  // and column block), then each thread sums one float4 item of all eight
-  // waves (contiguous 16-byte reads) and adds its four rows into S.
-  static_assert(kDC % CPR == 0, "rounds must cover the tile");
+    // Eight-way sum through LDS, CPR 16-row blocks per round: every wave
+    // parks its accumulators as whole float4s (one 1 KB contiguous write per
+    // block and column block), then each thread sums one float4 item of all
+    // eight waves (contiguous 16-byte reads) and adds its four rows into S.
+    static_assert(kDC % CPR == 0, "rounds must cover the tile");
 #pragma unroll
-  for (int c0 = 0; c0 < kDC; c0 += CPR) {
-    if (c0) __syncthreads();
+    for (int c0 = 0; c0 < kDC; c0 += CPR) {
+      __syncthreads();  // the previous round's (or segment's) readers are done
 #pragma unroll
-    for (int cr = 0; cr < CPR; ++cr)
+      for (int cr = 0; cr < CPR; ++cr)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) red[wt * ITEMS + (cr * NB + nb) * 64 + lane] = acc[c0 + cr][nb];
-    __syncthreads();
-    for (int v = threadIdx.x; v < ITEMS; v += NW * 64) {
-      f32x4 sum = red[v];
+        for (int nb = 0; nb < NB; ++nb) red[wt * ITEMS + (cr * NB + nb) * 64 + lane] = acc[c0 + cr][nb];
+      __syncthreads();
+      for (int v = threadIdx.x; v < ITEMS; v += NW * 64) {
+        f32x4 sum = red[v];
 #pragma unroll
-      for (int q = 1; q < NW; ++q) {
-        const f32x4 o = red[q * ITEMS + v];
-        sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
-      }
-      const int ln = v & 63, cn = v >> 6;  // lane of the item, (cr, nb) of the item
-      const int cr = cn / NB, nb = cn - cr * NB;
-      const int gg = ln >> 4, ii = ln & 15;
-      const int cc = 16 * nb + ii;
-      if (cc < p.r) {
+        for (int q = 1; q < NW; ++q) {
+          const f32x4 o = red[q * ITEMS + v];
+          sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+        }
+        const int ln = v & 63, cn = v >> 6;  // lane of the item, (cr, nb) of the item
+        const int cr = cn / NB, nb = cn - cr * NB;
+        const int gg = ln >> 4, ii = ln & 15;
+        const int cc = 16 * nb + ii;
+        if (cc < p.r) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t row = d0w + (int64_t)kDC * (4 * gg + e) + c0 + cr;
-          if (row < p.d) {
-            float* dst = p.S + row * p.lds + cc;
-            const float val = sum[e] * p.inv_sqrt_r;
-            if (p.atomic_out)
-              atomicAdd(dst, val);
-            else
-              *dst += val;
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = d0w + (int64_t)kDC * (4 * gg + e) + c0 + cr;
+            if (row < p.d) {
+              float* dst = p.S + row * p.lds + cc;
+              if (whole)
+                *dst += sum[e] * p.inv_sqrt_r;
+              else
+                atomicAdd(dst, sum[e] * p.inv_sqrt_r);
+            }
           }
         }
       }
@@ -794,102 +829,121 @@ template <int NB, int WM, int WN, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void contract_tile_kernel(ContractParams p) {
   constexpr int WT = NW / (WM * WN);
   constexpr int NBW = NB / WN;
-  constexpr int CH = NBW * 256;  // floats of one 16-row block of one wave's tile
   static_assert(WT * WM * WN == NW, "wave arrangement");
-  __shared__ float red[WT > 1 ? NW * CH : 4];
-  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  // Token splits slowest: an XCD's workgroups share one token window, so the
-  // P rows they all read stay in its L2 (P of a whole microbatch need not).
-  const int ts = p.ts_major ? lin / p.n_dt : lin % p.n_ts;
-  const int dt = p.ts_major ? lin - ts * p.n_dt : lin / p.n_ts;
-  if (ts >= p.n_ts) return;
-  if (dt >= p.n_dt) return;
+  // LDS rounds of CPR 16-row blocks: every wave parks CPR x NBW float4 items
+  // per lane (64 KB in all).
+  constexpr int CPR = (kDC * NBW * 64 * NW * 16 <= 65536) ? kDC : 65536 / (NBW * 64 * NW * 16);
+  constexpr int ITEMS = CPR * NBW * 64;  // float4 items per wave and round
+  static_assert(CPR >= 1 && kDC % CPR == 0, "rounds must cover the tile");
+  __shared__ f32x4 red[WT > 1 ? NW * ITEMS : 1];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, i = lane & 15;
   const int wt = w % WT, wn = (w / WT) % WN, wm = w / (WT * WN);
-  const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
-  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
   const int64_t nks = (p.T + 31) >> 5;
-  const int64_t ks_beg = ts * p.ksp;
-  const int64_t ks_end = min(nks, ks_beg + p.ksp);
-  const int64_t ks0 = ks_beg + wt;
-  const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + WT - 1) / WT) : 0;
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
   const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+  const StreamK sk(p, nks);
 
-  f32x4 acc[kDC][NBW];
-#pragma unroll
-  for (int c = 0; c < kDC; ++c)
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t u0 = sk.u_beg; u0 < sk.u_end;) {
+    int dt;
+    int64_t ks_beg, ks_end;
+    sk.segment(u0, dt, ks_beg, ks_end);
+    const bool whole = ks_beg == 0 && ks_end == nks;  // no other workgroup adds into this tile
 
-  u32x2 y[DEPTH][8];
-  u32x4 bh[DEPTH][NBW], bl[DEPTH][NBW];
-  auto issue = [&](int slot, int m) {
-    if (m >= nsteps) return;
-    const int64_t ks = ks0 + (int64_t)WT * m;
-    uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
+    const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
+    const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+    const int64_t ks0 = ks_beg + wt;
+    const int nsteps = ks_end > ks0 ? (int)((ks_end - ks0 + WT - 1) / WT) : 0;
+
+    f32x4 acc[kDC][NBW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[slot][e] = buf_load8(ry, off);
-      off += rowstep;
+    for (int c = 0; c < kDC; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x2 y[DEPTH][8];
+    u32x4 bh[DEPTH][NBW], bl[DEPTH][NBW];
+    auto issue = [&](int slot, int m) {
+      if (m >= nsteps) return;
+      const int64_t ks = ks0 + (int64_t)WT * m;
+      uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[slot][e] = buf_load8(ry, off);
+        off += rowstep;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int64_t o = ((ks * p.NB + wn * NBW + nb) * 64 + lane) * 8;
+        bh[slot][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
+        bl[slot][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
+      }
+    };
+
+#pragma unroll
+    for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
+    for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int m = m0 + u;
+        if (m < nsteps) {
+          issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
+          u32x4 a[kDC];
+          transpose_dy(y[u], a);
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) {
+              acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
+              acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
+            }
+        }
+      }
     }
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int64_t o = ((ks * p.NB + wn * NBW + nb) * 64 + lane) * 8;
-      bh[slot][nb] = *reinterpret_cast<const u32x4*>(p.Phi + o);
-      bl[slot][nb] = *reinterpret_cast<const u32x4*>(p.Plo + o);
-    }
-  };
 
+    if constexpr (WT == 1) {
+      if (whole) store_s_tile_mode<NBW, 2>(p, acc, d0w, wn * NBW, g, i, 0, d0w + 16 * kDC <= p.d && 16 * (wn + 1) * NBW <= p.r);
+      else store_s_tile_mode<NBW, 1>(p, acc, d0w, wn * NBW, g, i, 0, d0w + 16 * kDC <= p.d && 16 * (wn + 1) * NBW <= p.r);
+    } else {
+      // Sum the WT token lanes of every (row group, column group) through
+      // LDS, CPR 16-row blocks per round, as whole float4s (contiguous 1 KB
+      // writes and reads).
 #pragma unroll
-  for (int q = 0; q < DEPTH - 1; ++q) issue(q, q);
-  for (int m0 = 0; m0 < nsteps; m0 += DEPTH) {
+      for (int c0 = 0; c0 < kDC; c0 += CPR) {
+        __syncthreads();  // the previous round's (or segment's) readers are done
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) {
-      const int m = m0 + u;
-      if (m < nsteps) {
-        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
-        u32x4 a[kDC];
-        transpose_dy(y[u], a);
+        for (int cr = 0; cr < CPR; ++cr)
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+          for (int nb = 0; nb < NBW; ++nb) red[w * ITEMS + (cr * NBW + nb) * 64 + lane] = acc[c0 + cr][nb];
+        __syncthreads();
+        for (int v = threadIdx.x; v < (NW / WT) * ITEMS; v += NW * 64) {
+          const int gm = v / ITEMS, rest = v - gm * ITEMS;  // gm = wm * WN + wn
+          f32x4 sum = red[(gm * WT) * ITEMS + rest];
 #pragma unroll
-          for (int c = 0; c < kDC; ++c) {
-            acc[c][nb] = mfma_16x16x32(a[c], bh[u][nb], acc[c][nb]);
-            acc[c][nb] = mfma_16x16x32(a[c], bl[u][nb], acc[c][nb]);
+          for (int q = 1; q < WT; ++q) {
+            const f32x4 o = red[(gm * WT + q) * ITEMS + rest];
+            sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
           }
+          const int ln = rest & 63, cn = rest >> 6;  // lane, (cr, nb) of the item
+          const int cr = cn / NBW, nb = cn - cr * NBW;
+          const int gg = ln >> 4, ii = ln & 15;
+          const int cc = 16 * ((gm % WN) * NBW + nb) + ii;
+          if (cc < p.r) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t row = ((int64_t)dt * WM + gm / WN) * 16 * kDC + (int64_t)kDC * (4 * gg + e) + c0 + cr;
+              if (row < p.d) {
+                float* dst = p.S + row * p.lds + cc;
+                if (whole)
+                  *dst += sum[e] * p.inv_sqrt_r;
+                else
+                  atomicAdd(dst, sum[e] * p.inv_sqrt_r);
+              }
+            }
+          }
+        }
       }
-    }
-  }
-
-  if constexpr (WT == 1) {
-    store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
-  } else {
-    // Sum the WT token lanes of every (row group, column group) through LDS,
-    // one 16-row block (c) at a time.
-#pragma unroll
-    for (int c = 0; c < kDC; ++c) {
-      float* mine = red + w * CH;
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mine[(nb * 4 + e) * 64 + lane] = acc[c][nb][e];
-      __syncthreads();
-      for (int v = threadIdx.x; v < (NW / WT) * CH; v += NW * 64) {
-        const int gm = v / CH, rest = v - gm * CH;  // gm = wm * WN + wn
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < WT; ++q) sum += red[(gm * WT + q) * CH + rest];
-        const int ln = rest & 63, ne = rest >> 6;  // lane and (nb*4 + e) of the element
-        const int nb = ne >> 2, e = ne & 3;
-        const int gg = ln >> 4, ii = ln & 15;
-        const int cc = 16 * ((gm % WN) * NBW + nb) + ii;
-        const int64_t row = ((int64_t)dt * WM + gm / WN) * 16 * kDC + (int64_t)kDC * (4 * gg + e) + c;
-        if (cc < p.r && row < p.d) put_s(p, ts, row, cc, sum * p.inv_sqrt_r);
-      }
-      __syncthreads();
     }
   }
 }
@@ -1005,7 +1059,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   const int64_t nks = T32 / 32;
   int64_t BD, min_steps;
   if (pl.NB <= 4) {
-    pl.cvar = 0;  // eight waves on every eighth step of 64 rows
+    pl.cvar = 0;  // eight waves on every eighth step of 64 rows, stream-K over steps
     BD = 16 * kDC;
     min_steps = 16;
   } else {
@@ -1071,6 +1125,25 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   pl.ksp = (nks + n_ts - 1) / n_ts;
   pl.n_ts = (int)((nks + pl.ksp - 1) / pl.ksp);
   if (pl.n_ts < 1) pl.n_ts = 1;
+  if (pl.cvar == 0 || pl.cvar == 5) {
+    // Stream-K with one eight-wave workgroup per CU at most.  When eight
+    // token bands of at least 16 steps times the row tiles fit in one round
+    // (n_dt * 8 <= 256), every workgroup takes exactly one (tile, band) pair
+    // and each XCD's L2 holds only its band's eighth of P; otherwise one band
+    // over 256 workgroups (runs that straddle tiles cost one more set of
+    // atomic adds each, and many tiles per band would cut every run up).
+    const int64_t units = (int64_t)pl.n_dt * nks;
+    pl.cbands = env_int("LOGRA_CON_BANDS", (nks >= 128 && pl.n_dt * 8 <= 256) ? 8 : 1) == 8 ? 8 : 1;
+    int64_t grid = pl.cbands == 8 ? 8 * (int64_t)pl.n_dt : 256;
+    grid = env_int("LOGRA_CON_GRID", (int)grid);
+    if (grid > units / 8) grid = units / 8;
+    if (pl.cbands == 8) grid = grid / 8 * 8;
+    if (grid < 1) {
+      grid = 1;
+      pl.cbands = 1;
+    }
+    pl.cgrid = (int)grid;
+  }
 
   size_t off = 0;
   pl.off_counters = off;
@@ -1084,12 +1157,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
-  pl.use_part = env_int("LOGRA_CON_PART", ((pl.cvar == 3 || pl.cvar == 4) && pl.n_ts >= 3) ? 1 : 0) && pl.n_ts > 1 &&
-                pl.cvar >= 1;
+  pl.use_part = env_int("LOGRA_CON_PART", pl.n_ts >= 3 ? 1 : 0) && pl.n_ts > 1 && (pl.cvar == 3 || pl.cvar == 4);
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
-  pl.ts_major = env_int("LOGRA_CON_TSMAJOR", 0);
   return pl;
 }
 
@@ -1147,9 +1218,9 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
   const int grid = (int)align_up((size_t)pl.n_dt * pl.n_ts, 8);
   switch (pl.cvar) {
     case 0:
-      if (pl.NB == 1) hipLaunchKernelGGL((contract_small_kernel<1, 3>), dim3(grid), dim3(512), 0, s, p);
-      else if (pl.NB == 2) hipLaunchKernelGGL((contract_small_kernel<2, 3>), dim3(grid), dim3(512), 0, s, p);
-      else hipLaunchKernelGGL((contract_small_kernel<4, 2>), dim3(grid), dim3(512), 0, s, p);
+      if (pl.NB == 1) hipLaunchKernelGGL((contract_small_kernel<1, 3>), dim3(pl.cgrid), dim3(512), 0, s, p);
+      else if (pl.NB == 2) hipLaunchKernelGGL((contract_small_kernel<2, 3>), dim3(pl.cgrid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((contract_small_kernel<4, 2>), dim3(pl.cgrid), dim3(512), 0, s, p);
       return true;
     case 1:
       hipLaunchKernelGGL((contract_lds_kernel<8, 1>), dim3(grid), dim3(256), 0, s, p);
@@ -1166,7 +1237,7 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
     case 5: {
 #define LOGRA_CT(nb, wm, wn)                                                                          \
       if (pl.NB == nb && pl.WM == wm) {                                                               \
-        hipLaunchKernelGGL((contract_tile_kernel<nb, wm, wn, 8, 2>), dim3(grid), dim3(512), 0, s, p);   \
+        hipLaunchKernelGGL((contract_tile_kernel<nb, wm, wn, 8, 2>), dim3(pl.cgrid), dim3(512), 0, s, p); \
         return true;                                                                                  \
       }
       LOGRA_CT(8, 1, 2) LOGRA_CT(8, 2, 2) LOGRA_CT(8, 4, 2) LOGRA_CT(16, 1, 4) LOGRA_CT(16, 2, 4)

@@ -201,8 +201,10 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_PART": 0, "LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_TS": 5},
     {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 4},
     {"LOGRA_PROJ_SMALL": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_NK": 3},
-    {"LOGRA_CON_TSMAJOR": 1, "LOGRA_CON_TS": 4},
-    {"LOGRA_CON_TSMAJOR": 1, "LOGRA_CON_TS": 5, "LOGRA_CON_PART": 1},
+    {"LOGRA_CON_GRID": 7},
+    {"LOGRA_CON_GRID": 3},
+    {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 16},
+    {"LOGRA_CON_BANDS": 1, "LOGRA_CON_GRID": 5},
 ]
 
 
