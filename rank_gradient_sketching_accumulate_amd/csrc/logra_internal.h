@@ -60,6 +60,7 @@ struct SketchPlan {
   int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce
   int cgrid;              // contract_small / contract_tile: workgroups sharing the step units
   int cbands;             // token bands of that split (1, or 8 = one per XCD)
+  int bigdp;              // contract_big: steps between requesting a step's operands and using them
   size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };
 

@@ -723,7 +723,7 @@ __global__ __launch_bounds__(256) void contract_lds_kernel(ContractParams p) {
 // groups x WN column groups give a 512 x 128 (r <= 128) or 256 x 256 tile.
 // The step's P tile sits in a double-buffered LDS stage shared by all waves;
 // every wave loads the dY rows of its row group itself.
-template <int NB, int WN>
+template <int NB, int WN, int DP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void contract_big_kernel(ContractParams p) {
   constexpr int NBW = NB / WN;           // column blocks per wave
   constexpr int WM = 8 / WN;             // row groups
@@ -737,7 +737,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
   const int ts = lin - dt * p.n_ts;
   if (dt >= p.n_dt) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, i = lane & 15;
   const int wn = wave % WN, wm = wave / WN;
   const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
@@ -755,9 +755,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x2 y[2][8];
-  u32x4 stg[PER];
+  // Prefetch distance DP: the loads of step m + DP are issued while step m is
+  // multiplied, and P of step m + 1 goes from registers into the other LDS
+  // half at the end of step m, DP - 1 steps after it was requested.
+  u32x2 y[DP + 1][8];
+  u32x4 stg[DP][PER];
   auto load_y = [&](u32x2 (&slot)[8], int m) {
+    if (m >= nsteps) return;
     uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -766,39 +770,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
     }
   };
   // Thread q moves words q, q + 512, ... of the step's [hi | lo] tile.
-  auto load_p = [&](int m) {
+  auto load_p = [&](u32x4 (&sl)[PER], int m) {
+    if (m >= nsteps) return;
     const int64_t base = (ks_beg + m) * (int64_t)PV;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int w = threadIdx.x + 512 * j;
       const uint16_t* src = (w < PV) ? p.Phi + (base + w) * 8 : p.Plo + (base + w - PV) * 8;
-      stg[j] = *reinterpret_cast<const u32x4*>(src);
+      sl[j] = *reinterpret_cast<const u32x4*>(src);
     }
   };
-  auto store_p = [&](int buf) {
+  auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) pt[buf][threadIdx.x + 512 * j] = stg[j];
+    for (int j = 0; j < PER; ++j) pt[buf][threadIdx.x + 512 * j] = sl[j];
   };
 
-  if (nsteps > 0) {
-    load_p(0);
-    load_y(y[0], 0);
-    store_p(0);
-  }
-  __syncthreads();
-  for (int m0 = 0; m0 < nsteps; m0 += 2) {
+  // Steps 0 .. DP - 1 in flight; step 0 staged.  P of step m lives in
+  // stg[m % DP] until it is staged, dY of step m in y[m % (DP + 1)]; the loop
+  // body covers DP * (DP + 1) steps so that both indices are constants.
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+  for (int q = 0; q < DP; ++q) {
+    load_p(stg[q], q);
+    load_y(y[q], q);
+  }
+  if (nsteps > 0) store_p(stg[0], 0);
+  __syncthreads();
+  constexpr int L = DP * (DP + 1);
+  for (int m0 = 0; m0 < nsteps; m0 += L) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
       const int m = m0 + u;
       if (m < nsteps) {
-        const bool more = m + 1 < nsteps;
-        if (more) {
-          load_p(m + 1);
-          load_y(y[u ^ 1], m + 1);
-        }
+        load_p(stg[u % DP], m + DP);  // stg[m % DP] was staged at the end of step m - 1
+        load_y(y[(u + DP) % (DP + 1)], m + DP);
         u32x4 a[kDC];
-        transpose_dy(y[u], a);
-        const u32x4* ph = &pt[u][0];
+        transpose_dy(y[u % (DP + 1)], a);
+        const u32x4* ph = &pt[u & 1][0];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           const u32x4 bh = ph[(wn * NBW + nb) * 64 + lane];
@@ -809,7 +816,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
             acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
           }
         }
-        if (more) store_p(u ^ 1);
+        if (m + 1 < nsteps) store_p(stg[(u + 1) % DP], (u + 1) & 1);
         __syncthreads();
       }
     }
@@ -1158,6 +1165,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
   pl.use_part = env_int("LOGRA_CON_PART", pl.n_ts >= 3 ? 1 : 0) && pl.n_ts > 1 && (pl.cvar == 3 || pl.cvar == 4);
+  pl.bigdp = env_int("LOGRA_CON_BIGDP", 2) == 1 ? 1 : 2;
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
@@ -1229,10 +1237,12 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
       hipLaunchKernelGGL((contract_lds_kernel<16, 2>), dim3(grid), dim3(256), 0, s, p);
       return true;
     case 3:
-      hipLaunchKernelGGL((contract_big_kernel<8, 1>), dim3(grid), dim3(512), 0, s, p);
+      if (pl.bigdp == 2) hipLaunchKernelGGL((contract_big_kernel<8, 1, 2>), dim3(grid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((contract_big_kernel<8, 1, 1>), dim3(grid), dim3(512), 0, s, p);
       return true;
     case 4:
-      hipLaunchKernelGGL((contract_big_kernel<16, 2>), dim3(grid), dim3(512), 0, s, p);
+      if (pl.bigdp == 2) hipLaunchKernelGGL((contract_big_kernel<16, 2, 2>), dim3(grid), dim3(512), 0, s, p);
+      else hipLaunchKernelGGL((contract_big_kernel<16, 2, 1>), dim3(grid), dim3(512), 0, s, p);
       return true;
     case 5: {
 #define LOGRA_CT(nb, wm, wn)                                                                          \
