@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const int cr = lin - rb * p.n_cr;
   if (rb >= p.n_rb) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, i = lane & 15;
   const int64_t rw = (int64_t)rb * 4 * RW + (int64_t)wave * RW;  // first row of this wave
   const int64_t c_begin = (int64_t)cr * p.cr_cols;
@@ -241,8 +241,8 @@ MergePlan plan_merge(int64_t d, int64_t k, int r) {
   // Tile per wave and chunk (two waves fit per SIMD): one 16-row block x 64
   // columns up to r = 128 with about 2048 workgroups; at r = 256, where the
   // U operands and sign expansion cost more, two 16-row blocks (each expanded
-  // sign operand feeds both) with about 512 longer column ranges.  Measured
-  // with GPU-only timing over layers from 1536 x 1536 to 18944 x 3584.
+  // sign operand feeds both) with about 1024 longer column ranges.  Measured
+  // with GPU-only timing over layers from 1536 x 1536 to 17408 x 5120.
   int NBW = pl.NK == 8 ? 2 : 1, CB = 4;
   NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
   CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
@@ -253,7 +253,7 @@ MergePlan plan_merge(int64_t d, int64_t k, int r) {
   // Column ranges: as long as possible while about `target` workgroups remain.
   const int64_t CW = 16 * CB;
   const int64_t chunks = (k + CW - 1) / CW;
-  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK == 8 ? 512 : 2048);
+  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK == 8 ? 1024 : 2048);
   if (target < 1) target = 1;
   int64_t n_cr = (target + pl.n_rb - 1) / pl.n_rb;
   if (n_cr > chunks) n_cr = chunks;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
 
   const int tt = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, i = lane & 15;
   const int64_t t0 = (int64_t)tt * TT;
   const int nks = (int)((p.k + 31) >> 5);
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int ksp = lin - tt * p.n_k;
   if (tt >= p.n_tt) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 4, i = lane & 15;
   const int wt = wave % WT, wk = wave / WT;
   const int64_t t0 = (int64_t)tt * TT;
