@@ -94,6 +94,53 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
                                      hipStream_t stream);
 
 /*
+ * Split sketch accumulation: project at forward time, contract at backward
+ * time.  The paper counts cached projections among the memory the method
+ * keeps (section 2.2, "Memory and synchronization") and projects the inputs
+ * before the backward derivatives multiply them (section 2.1, after
+ * equation 2):
+ *
+ *     logra_project  :  P  = X[T x k] * s^T[k x r]              (forward)
+ *     logra_contract :  S += (1/sqrt(r)) * dY^T[d x T] * P       (backward)
+ *
+ * Together they add exactly what one logra_sketch_accumulate call adds (the
+ * same kernels run); between the two calls the caller keeps P instead of X:
+ * 4 * roundup(T, 256) * R bytes against 2 * T * k.
+ *
+ * The projection cache P is a caller-owned device buffer of at least
+ * logra_projection_bytes(T, r) bytes, 16-byte aligned.  Its layout: R = 16 *
+ * (the smallest power of two >= ceil(r / 16)) columns, Tc = roundup(T, 256)
+ * tokens; a plane of bf16 high parts at byte 0 and a plane of bf16 low parts
+ * at byte 2 * Tc * R, each Tc * R entries; entry (t, c) of a plane sits at
+ * index ((((t / 32) * (R / 16) + c / 16) * 64 + ((t % 32) / 8) * 16 + c % 16) * 8
+ * + t % 8), the order in which the contraction feeds its matrix cores.  For
+ * t < T and c < r, high + low equals P[t][c] = sum_j X[t][j] s[c][j] to about
+ * 2^-16 relative (fp32 accumulation, then a bf16 high part and a bf16 low
+ * part of the remainder); tokens T <= t < roundup(T, 32) hold zeros; other
+ * entries are unspecified.  A cache is valid for the T and r it was made
+ * with and is read, not written, by logra_contract.
+ *
+ *   logra_project:  X as in logra_sketch_accumulate; T, k >= 0 (T == 0 is a
+ *                   no-op; k == 0 fills P with zeros); P must not overlap X;
+ *                   the whole cache is rewritten.
+ *   logra_contract: dY and S as in logra_sketch_accumulate; T, d >= 0 (0 is a
+ *                   no-op); S must not overlap dY or P.  The same seed and r
+ *                   as the projection are implied by P.
+ * Both keep their other scratch (column- and token-split partial sums) per
+ * (device, stream) like logra_sketch_accumulate, and return
+ * LOGRA_ERR_SHAPE when P_bytes < logra_projection_bytes(T, r).
+ */
+size_t logra_projection_bytes(int64_t T, int32_t r);
+
+logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k,
+                           uint64_t seed, int32_t r,
+                           void* P, size_t P_bytes, hipStream_t stream);
+
+logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d,
+                            const void* P, size_t P_bytes, int32_t r,
+                            float* S, int64_t lds, hipStream_t stream);
+
+/*
  * Fused expand-and-merge (paper section 2.1, equations 3 and 4; Algorithm 1's
  * trainer update):
  *

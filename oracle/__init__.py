@@ -25,6 +25,7 @@ from .logra_oracle import (  # noqa: F401
     f64_to_bf16_bits,
     dense_gradient,
     sketch_from_gradient,
+    project_inputs,
     sketch_accumulate,
     low_rank_expand,
     merge_update,

@@ -178,6 +178,14 @@ def sketch_from_gradient(G, A) -> np.ndarray:
     return np.asarray(G, dtype=np.float64) @ np.asarray(A, dtype=np.float64).T
 
 
+def project_inputs(X, A) -> np.ndarray:
+    """P = X A^T (T x r, float64): the layer inputs projected before the
+    backward derivatives multiply them (LoGRA section 2.1, the paragraph after
+    equation 2), the quantity kept as "cached projections" (section 2.2,
+    "Memory and synchronization").  dY^T P is then this microbatch's G A^T."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(A, dtype=np.float64).T
+
+
 def sketch_accumulate(S0, X_list, dY_list, A, rows=None) -> np.ndarray:
     """S = S0 + (sum_m dY_m^T X_m) A^T.
 

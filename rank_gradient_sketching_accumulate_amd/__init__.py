@@ -25,6 +25,9 @@ __all__ = [
     "load_library",
     "library_loaded",
     "sketch_accumulate",
+    "projection_bytes",
+    "project",
+    "contract",
     "merge_update",
     "rowadam_scale",
     "signs",
@@ -40,6 +43,9 @@ MAX_RANK = 256
 # Every symbol include/logra.h declares.
 EXPORTED_SYMBOLS = (
     "logra_sketch_accumulate",
+    "logra_projection_bytes",
+    "logra_project",
+    "logra_contract",
     "logra_merge_update",
     "logra_rowadam_scale",
     "logra_signs",
@@ -66,6 +72,12 @@ def _declare(lib):
     c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
     lib.logra_sketch_accumulate.restype = ctypes.c_int
+    lib.logra_projection_bytes.argtypes = [c_i64, c_i32]
+    lib.logra_projection_bytes.restype = ctypes.c_size_t
+    lib.logra_project.argtypes = [c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, ctypes.c_size_t, c_vp]
+    lib.logra_project.restype = ctypes.c_int
+    lib.logra_contract.argtypes = [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_size_t, c_i32, c_vp, c_i64, c_vp]
+    lib.logra_contract.restype = ctypes.c_int
     lib.logra_merge_update.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_f, c_vp]
     lib.logra_merge_update.restype = ctypes.c_int
     lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
@@ -172,6 +184,60 @@ def sketch_accumulate(X, dY, seed: int, r: int, S):
         lib.logra_sketch_accumulate(
             X.data_ptr(), _ld(X), dY.data_ptr(), _ld(dY), T, k, d,
             ctypes.c_uint64(seed & (2**64 - 1)), r, S.data_ptr(), _ld(S), _stream_handle(S),
+        )
+    )
+    return S
+
+
+def projection_bytes(T: int, r: int) -> int:
+    """Bytes of the projection cache for T tokens at rank r (0 if T <= 0)."""
+    return int(load_library().logra_projection_bytes(T, r))
+
+
+def project(X, seed: int, r: int, P=None):
+    """Forward half of the split sketch: P = X s^T into a projection cache.
+
+    X: (T, k) bf16.  P: a uint8 device tensor of at least projection_bytes(T, r)
+    bytes (allocated when None); its layout is the one include/logra.h states.
+    Returns P.
+    """
+    import torch
+
+    lib = load_library()
+    _need(X, torch.bfloat16, "X")
+    T, k = X.shape
+    nbytes = projection_bytes(T, r)
+    if P is None:
+        P = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+    _need(P, torch.uint8, "P", ndim=1)
+    _check(
+        lib.logra_project(
+            X.data_ptr() if X.numel() else None, _ld(X) if k else 0, T, k,
+            ctypes.c_uint64(seed & (2**64 - 1)), r, P.data_ptr(), P.numel(), _stream_handle(P),
+        )
+    )
+    return P
+
+
+def contract(dY, P, r: int, S):
+    """Backward half of the split sketch: S += (1/sqrt(r)) dY^T P; returns S.
+
+    dY: (T, d) bf16, P: the cache logra_project filled for the same T and r,
+    S: (d, r) float32 (updated in place).
+    """
+    import torch
+
+    lib = load_library()
+    _need(dY, torch.bfloat16, "dY")
+    _need(P, torch.uint8, "P", ndim=1)
+    _need(S, torch.float32, "S")
+    T, d = dY.shape
+    if tuple(S.shape) != (d, r):
+        raise ValueError(f"S must be ({d}, {r}), got {tuple(S.shape)}")
+    _check(
+        lib.logra_contract(
+            dY.data_ptr(), _ld(dY), T, d, P.data_ptr(), P.numel(), r, S.data_ptr(), _ld(S),
+            _stream_handle(S),
         )
     )
     return S

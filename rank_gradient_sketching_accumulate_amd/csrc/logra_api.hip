@@ -116,6 +116,85 @@ MergePlan merge_plan_for(int64_t d, int64_t k, int r) {
   return pl;
 }
 
+// Checks shared by the calls that read X.
+logra_status check_x(const void* X, int64_t ldx, int64_t T, int64_t k) {
+  if (ldx < k) return fail(LOGRA_ERR_SHAPE, "ldx must be >= k");
+  if (((uintptr_t)X & 15) || (ldx & 7))
+    return fail(LOGRA_ERR_ALIGN, "X needs a 16-byte aligned base and a row stride that is a multiple of 8");
+  if (T > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "T and k must be below 2^31");
+  return LOGRA_OK;
+}
+
+// Checks shared by the calls that read dY and add into S.
+logra_status check_dy_s(const void* dY, int64_t lddy, int64_t T, int64_t d, const float* S, int64_t lds, int r) {
+  if (lddy < d) return fail(LOGRA_ERR_SHAPE, "lddy must be >= d");
+  if (((uintptr_t)dY & 15) || (lddy & 7))
+    return fail(LOGRA_ERR_ALIGN, "dY needs a 16-byte aligned base and a row stride that is a multiple of 8");
+  if ((uintptr_t)S & 3) return fail(LOGRA_ERR_ALIGN, "S must be 4-byte aligned");
+  if (overlaps(S, span_bytes(d, r, lds, 4), dY, span_bytes(T, d, lddy, 2)))
+    return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
+  if (T > ((int64_t)1 << 31) || d > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "T and d must be below 2^31");
+  return LOGRA_OK;
+}
+
+// Kernels address X and dY through buffer descriptors with 32-bit byte
+// offsets (rows past T read as zero): each operand must span < 4 GiB.
+logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t lddy) {
+  const uint64_t lim = ((uint64_t)1 << 32) - 4096;
+  if ((uint64_t)(pl.Tpad + 32) * (uint64_t)ldx * 2 >= lim || (uint64_t)(pl.Tpad + 32) * (uint64_t)lddy * 2 >= lim)
+    return fail(LOGRA_ERR_SHAPE, "X or dY spans 4 GiB or more; split the microbatch into several calls");
+  if ((size_t)pl.n_k * pl.Tpad * 16 * pl.NB * 4 > ((size_t)1 << 32) - 64)
+    return fail(LOGRA_ERR_SHAPE, "T too large for one call at this rank; split the microbatch");
+  (void)T;
+  return LOGRA_OK;
+}
+
+// P = X s^T into the hi/lo planes (Pk order); tokens in [T, Tpad) get zeros.
+logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X, int64_t ldx, int64_t T, int64_t k,
+                                uint64_t seed, int r, uint16_t* Phi, uint16_t* Plo, hipStream_t stream) {
+  ProjParams pp{};
+  pp.X = static_cast<const uint16_t*>(X);
+  pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
+  pp.n_tt = pl.n_tt; pp.n_k = pl.n_k; pp.cbs_per = pl.cbs_per; pp.ncb = pl.ncb;
+  pp.Phi = Phi;
+  pp.Plo = Plo;
+  pp.Ppart = reinterpret_cast<float*>(base + pl.off_part);
+  pp.part_stride = pl.Tpad * 16 * pl.NB;
+  pp.counters = reinterpret_cast<unsigned*>(base + pl.off_counters);
+  if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return LOGRA_OK;
+}
+
+// S += (1/sqrt r) dY^T P from the hi/lo planes.
+logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* dY, int64_t lddy, int64_t T, int64_t d,
+                                 const uint16_t* Phi, const uint16_t* Plo, int r, float* S, int64_t lds,
+                                 hipStream_t stream) {
+  ContractParams cp{};
+  cp.dY = static_cast<const uint16_t*>(dY);
+  cp.lddy = lddy; cp.T = T; cp.d = d;
+  cp.Phi = Phi; cp.Plo = Plo; cp.NB = pl.NB;
+  cp.S = S; cp.lds = lds; cp.r = r;
+  cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
+  cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
+  cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
+  cp.bands = pl.cbands;
+  if (pl.use_part) {
+    cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
+    cp.part_split = d * 16 * pl.NB;
+  }
+  if (!contract_launch(pl, cp, stream)) return fail(LOGRA_ERR_RANGE, "no contraction kernel for this tile");
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "contraction launch");
+  if (pl.use_part) {
+    reduce_launch(pl, cp, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
+  }
+  return LOGRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,66 +209,100 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
     if (T == 0 || k == 0 || d == 0) return LOGRA_OK;
     if (!X || !dY || !S) return fail(LOGRA_ERR_NULL, "X, dY and S must be non-null");
-    if (ldx < k) return fail(LOGRA_ERR_SHAPE, "ldx must be >= k");
-    if (lddy < d) return fail(LOGRA_ERR_SHAPE, "lddy must be >= d");
-    if (((uintptr_t)X & 15) || ((uintptr_t)dY & 15) || (ldx & 7) || (lddy & 7))
-      return fail(LOGRA_ERR_ALIGN, "X and dY need 16-byte aligned bases and row strides that are multiples of 8");
-    if ((uintptr_t)S & 3) return fail(LOGRA_ERR_ALIGN, "S must be 4-byte aligned");
-    const size_t sb = span_bytes(d, r, lds, 4);
-    if (overlaps(S, sb, X, span_bytes(T, k, ldx, 2)) || overlaps(S, sb, dY, span_bytes(T, d, lddy, 2)))
+    logra_status st = check_x(X, ldx, T, k);
+    if (st != LOGRA_OK) return st;
+    st = check_dy_s(dY, lddy, T, d, S, lds, r);
+    if (st != LOGRA_OK) return st;
+    if (overlaps(S, span_bytes(d, r, lds, 4), X, span_bytes(T, k, ldx, 2)))
       return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
-    if (T > ((int64_t)1 << 31) || k > ((int64_t)1 << 31) || d > ((int64_t)1 << 31))
-      return fail(LOGRA_ERR_SHAPE, "T, k and d must be below 2^31");
 
     const SketchPlan pl = sketch_plan_for(T, k, d, r);
-    // Kernels address X and dY through buffer descriptors with 32-bit byte
-    // offsets (rows past T read as zero): each operand must span < 4 GiB.
-    const uint64_t lim = ((uint64_t)1 << 32) - 4096;
-    if ((uint64_t)(pl.Tpad + 32) * (uint64_t)ldx * 2 >= lim || (uint64_t)(pl.Tpad + 32) * (uint64_t)lddy * 2 >= lim)
-      return fail(LOGRA_ERR_SHAPE, "X or dY spans 4 GiB or more; split the microbatch into several calls");
-    if ((size_t)pl.n_k * pl.Tpad * 16 * pl.NB * 4 > ((size_t)1 << 32) - 64)
-      return fail(LOGRA_ERR_SHAPE, "T too large for one call at this rank; split the microbatch");
+    st = check_plan(pl, T, ldx, lddy);
+    if (st != LOGRA_OK) return st;
     void* ws = nullptr;
-    logra_status st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    st = arena_get(kArenaSketch, stream, pl.total, &ws);
     if (st != LOGRA_OK) return st;
     char* base = static_cast<char*>(ws);
-    const float inv_sqrt_r = (float)(1.0 / sqrt((double)r));
+    uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
+    uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
+    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, stream);
+    if (st != LOGRA_OK) return st;
+    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, stream);
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
 
-    ProjParams pp{};
-    pp.X = static_cast<const uint16_t*>(X);
-    pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
-    pp.n_tt = pl.n_tt; pp.n_k = pl.n_k; pp.cbs_per = pl.cbs_per; pp.ncb = pl.ncb;
-    pp.Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
-    pp.Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
-    pp.Ppart = reinterpret_cast<float*>(base + pl.off_part);
-    pp.part_stride = pl.Tpad * 16 * pl.NB;
-    pp.counters = reinterpret_cast<unsigned*>(base + pl.off_counters);
-    if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "projection launch");
+size_t logra_projection_bytes(int64_t T, int32_t r) {
+  if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
+  return projection_cache_bytes(T, r);
+}
 
-    ContractParams cp{};
-    cp.dY = static_cast<const uint16_t*>(dY);
-    cp.lddy = lddy; cp.T = T; cp.d = d;
-    cp.Phi = pp.Phi; cp.Plo = pp.Plo; cp.NB = pl.NB;
-    cp.S = S; cp.lds = lds; cp.r = r;
-    cp.inv_sqrt_r = inv_sqrt_r;
-    cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
-    cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
-    cp.bands = pl.cbands;
-    if (pl.use_part) {
-      cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
-      cp.part_split = d * 16 * pl.NB;
+logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uint64_t seed, int32_t r, void* P,
+                           size_t P_bytes, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (T < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "T and k must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (T == 0) return LOGRA_OK;
+    if (!P) return fail(LOGRA_ERR_NULL, "P must be non-null");
+    const size_t need = projection_cache_bytes(T, r);
+    if (P_bytes < need) return fail(LOGRA_ERR_SHAPE, "P_bytes is smaller than logra_projection_bytes(T, r)");
+    if ((uintptr_t)P & 15) return fail(LOGRA_ERR_ALIGN, "P must be 16-byte aligned");
+    if (k == 0) {
+      // X has no columns: P = X s^T is zero.
+      hipError_t e = hipMemsetAsync(P, 0, need, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+      return LOGRA_OK;
     }
-    if (!contract_launch(pl, cp, stream)) return fail(LOGRA_ERR_RANGE, "no contraction kernel for this tile");
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "contraction launch");
-    if (pl.use_part) {
-      reduce_launch(pl, cp, stream);
-      e = hipGetLastError();
-      if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
-    }
-    return LOGRA_OK;
+    if (!X) return fail(LOGRA_ERR_NULL, "X must be non-null");
+    logra_status st = check_x(X, ldx, T, k);
+    if (st != LOGRA_OK) return st;
+    if (overlaps(P, need, X, span_bytes(T, k, ldx, 2))) return fail(LOGRA_ERR_ALIAS, "P overlaps X");
+
+    SketchPlan pl = sketch_plan_for(T, k, 1, r);
+    st = check_plan(pl, T, ldx, 8);
+    if (st != LOGRA_OK) return st;
+    if (pl.Tpad > cache_tokens(T)) return fail(LOGRA_ERR_RANGE, "projection tile does not fit the cache");
+    scratch_layout(pl, 1, true, false);
+    void* ws = nullptr;
+    st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    if (st != LOGRA_OK) return st;
+    uint16_t* Phi = static_cast<uint16_t*>(P);
+    uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
+    return enqueue_projection(pl, static_cast<char*>(ws), X, ldx, T, k, seed, r, Phi, Plo, stream);
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d, const void* P, size_t P_bytes,
+                            int32_t r, float* S, int64_t lds, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (T < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T and d must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
+    if (T == 0 || d == 0) return LOGRA_OK;
+    if (!dY || !P || !S) return fail(LOGRA_ERR_NULL, "dY, P and S must be non-null");
+    const size_t need = projection_cache_bytes(T, r);
+    if (P_bytes < need) return fail(LOGRA_ERR_SHAPE, "P_bytes is smaller than logra_projection_bytes(T, r)");
+    if ((uintptr_t)P & 15) return fail(LOGRA_ERR_ALIGN, "P must be 16-byte aligned");
+    logra_status st = check_dy_s(dY, lddy, T, d, S, lds, r);
+    if (st != LOGRA_OK) return st;
+    if (overlaps(S, span_bytes(d, r, lds, 4), P, need)) return fail(LOGRA_ERR_ALIAS, "S overlaps P");
+
+    // The contraction's tiling does not depend on k; 256 stands in for it.
+    SketchPlan pl = sketch_plan_for(T, 256, d, r);
+    st = check_plan(pl, T, 8, lddy);
+    if (st != LOGRA_OK) return st;
+    scratch_layout(pl, d, false, true);
+    void* ws = nullptr;
+    st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    if (st != LOGRA_OK) return st;
+    const uint16_t* Phi = static_cast<const uint16_t*>(P);
+    const uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
+    return enqueue_contraction(pl, static_cast<char*>(ws), dY, lddy, T, d, Phi, Plo, r, S, lds, stream);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }

@@ -65,6 +65,16 @@ struct SketchPlan {
 };
 
 SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r);
+// Caller-held projection cache of the split project / contract calls: a high
+// plane then a low plane, each cache_tokens(T) x 16*NB bf16 entries in Pk
+// order.  Every projection tiling's padded token count fits in it (token
+// tiles are powers of two of at most 256 tokens).
+inline int64_t cache_tokens(int64_t T) { return (T + 255) / 256 * 256; }
+size_t projection_cache_bytes(int64_t T, int r);
+// Re-lays the library scratch of a plan without the P planes (they live in
+// the caller's cache), keeping the projection's column-split partials and/or
+// the contraction's token-split partials.
+void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part);
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s);
 bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s);
 // S += sum over token splits of the stored partial tiles (use_part plans).

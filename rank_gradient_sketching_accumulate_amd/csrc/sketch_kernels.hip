@@ -995,6 +995,23 @@ int pow2_blocks(int r) {
 }
 }  // namespace
 
+size_t projection_cache_bytes(int64_t T, int r) {
+  return (size_t)cache_tokens(T) * 16 * pow2_blocks(r) * 4;
+}
+
+void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part) {
+  const size_t RP = 16 * (size_t)pl.NB;
+  size_t off = 0;
+  pl.off_counters = off;
+  off += align_up((size_t)pl.n_tt * sizeof(unsigned), 256);
+  pl.off_phi = pl.off_plo = 0;
+  pl.off_part = off;
+  if (proj_part && pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
+  pl.off_cpart = off;
+  if (con_part && pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
+  pl.total = off;
+}
+
 int env_int(const char* name, int dflt) {
   const char* s = getenv(name);
   return (s && *s) ? atoi(s) : dflt;

@@ -89,6 +89,54 @@ def test_sketch_validation(lib):
     assert _sketch(lib, d=0) == OK
 
 
+def test_projection_bytes(lib):
+    assert lib.logra_projection_bytes(0, 16) == 0
+    assert lib.logra_projection_bytes(16, 0) == 0
+    assert lib.logra_projection_bytes(16, 257) == 0
+    # two bf16 planes of roundup(T, 256) tokens x (16 * next power of two of ceil(r / 16)) columns
+    assert lib.logra_projection_bytes(1, 1) == 4 * 256 * 16
+    assert lib.logra_projection_bytes(4096, 64) == 4 * 4096 * 64
+    assert lib.logra_projection_bytes(4097, 48) == 4 * 4352 * 64
+    assert lib.logra_projection_bytes(16384, 256) == 4 * 16384 * 256
+
+
+PB = 4 * 256 * 16  # logra_projection_bytes(16, 16)
+
+
+def _project(lib, X=FAKE, ldx=512, T=16, k=512, r=16, P=FAKE * 64, nbytes=PB):
+    return lib.logra_project(X, ldx, T, k, 0, r, P, nbytes, None)
+
+
+def _contract(lib, dY=FAKE, lddy=256, T=16, d=256, P=FAKE * 64, nbytes=PB, r=16, S=FAKE * 4096, lds=16):
+    return lib.logra_contract(dY, lddy, T, d, P, nbytes, r, S, lds, None)
+
+
+def test_split_validation(lib):
+    assert _project(lib, r=0) == ERR_RANGE
+    assert _project(lib, T=-1) == ERR_SHAPE
+    assert _project(lib, T=0, X=None, P=None) == OK
+    assert _project(lib, P=None) == ERR_NULL
+    assert _project(lib, X=None) == ERR_NULL
+    assert _project(lib, nbytes=PB - 1) == ERR_SHAPE
+    assert b"logra_projection_bytes" in lib.logra_last_error()
+    assert _project(lib, P=FAKE * 64 + 8) == ERR_ALIGN
+    assert _project(lib, X=FAKE + 2) == ERR_ALIGN
+    assert _project(lib, ldx=500) == ERR_SHAPE
+    assert _project(lib, P=FAKE + 4096) == ERR_ALIAS  # inside X's 16 KiB span
+    assert _contract(lib, r=300) == ERR_RANGE
+    assert _contract(lib, lds=8) == ERR_SHAPE
+    assert _contract(lib, T=0, dY=None, P=None, S=None) == OK
+    assert _contract(lib, d=0) == OK
+    assert _contract(lib, P=None) == ERR_NULL
+    assert _contract(lib, nbytes=100) == ERR_SHAPE
+    assert _contract(lib, P=FAKE * 64 + 4) == ERR_ALIGN
+    assert _contract(lib, lddy=250) == ERR_SHAPE
+    assert _contract(lib, S=FAKE + 2048) == ERR_ALIAS  # S inside dY's span
+    assert _contract(lib, S=FAKE * 64 + 64) == ERR_ALIAS  # S inside P
+    # a cache made for more tokens or a larger rank is large enough
+    assert lib.logra_projection_bytes(16, 16) <= lib.logra_projection_bytes(300, 16)
+
+
 def _merge(lib, W=FAKE, ldw=512, U=FAKE * 64, ldu=16, d=256, k=512, r=16, scale=1e-3):
     return lib.logra_merge_update(W, ldw, U, ldu, d, k, 0, r, ctypes.c_float(scale), None)
 

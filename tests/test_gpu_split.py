@@ -1,0 +1,182 @@
+"""GPU parity of the split sketch (logra_project at forward time, then
+logra_contract at backward time) against the float64 oracle.
+
+The cache P that logra_project writes is decoded on the host with the layout
+include/logra.h states and compared with the oracle's projected inputs
+X A^T (times sqrt(r), since the cache holds X s^T); S after the contractions
+is compared with the oracle's sketch, as for the fused call.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests._util import assert_sketch_close, f64, padded_ld, rel_frob
+
+torch = pytest.importorskip("torch")
+lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _cache_cols(r):
+    nb = (r + 15) // 16
+    q = 1
+    while q < nb:
+        q *= 2
+    return 16 * q
+
+
+def decode_cache(P, T, r):
+    """(T, r) float64 values hi + lo read from a projection cache, and the
+    (roundup(T, 32) - T, r) block of padding tokens, per the documented layout."""
+    R = _cache_cols(r)
+    Tc = (T + 255) // 256 * 256
+    raw = P.cpu().numpy()[: 4 * Tc * R].view(np.uint16)
+    T32 = (T + 31) // 32 * 32
+    t = np.arange(T32)[:, None]
+    c = np.arange(r)[None, :]
+    idx = ((((t // 32) * (R // 16) + c // 16) * 64 + ((t % 32) // 8) * 16 + c % 16) * 8 + t % 8)
+    # only the specified entries are read (the rest may hold any bit pattern)
+    vals = oracle.bf16_bits_to_f64(raw[idx]) + oracle.bf16_bits_to_f64(raw[Tc * R + idx])
+    return vals[:T], vals[T:]
+
+
+def _inputs(T, k, d, seed):
+    X = wl.gaussian_bf16((T, k), 1.0, seed, device=DEV, ld=padded_ld(k))
+    dY = wl.gaussian_bf16((T, d), 1e-2, seed + 1, device=DEV, ld=padded_ld(d))
+    return X, dY
+
+
+SHAPES = [
+    (1, 8, 1, 1),
+    (37, 300, 200, 16),
+    (255, 520, 130, 40),
+    (512, 512, 256, 16),
+    (1000, 700, 900, 128),
+    (300, 1100, 513, 256),
+    (4096, 1536, 1536, 64),
+    (2000, 8960, 64, 128),
+]
+
+
+@pytest.mark.parametrize("T,k,d,r", SHAPES)
+def test_project_cache_matches_oracle(T, k, d, r):
+    _say("project", T, k, d, r)
+    seed = 77 + T + k + r
+    X, _ = _inputs(T, k, d, seed)
+    P = lg.project(X, seed, r)
+    assert P.numel() >= lg.projection_bytes(T, r)
+    got, pad = decode_cache(P, T, r)
+    Xh = f64(X)
+    ref = oracle.project_inputs(Xh, oracle.rademacher_projection(seed, r, k)) * math.sqrt(r)
+    # hi + lo carries about 16 significant bits (<= 2^-16 relative here), and
+    # k products accumulate in fp32 (|error| <= k 2^-24 sum_j |X_tj|).
+    bound = 2.0**-16 * np.abs(ref) + k * 2.0**-24 * np.abs(Xh).sum(axis=1, keepdims=True)
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"max excess {float((err - bound).max()):.3e}"
+    assert rel_frob(got, ref) <= 2e-5
+    np.testing.assert_array_equal(pad, np.zeros_like(pad))
+
+
+@pytest.mark.parametrize("T,k,d,r", SHAPES)
+def test_split_sketch_matches_oracle_and_fused(T, k, d, r):
+    """Forward for every microbatch first (caches live together), then the
+    backward contractions in reverse order, as a training step would."""
+    _say("split sketch", T, k, d, r)
+    M = 3
+    seed = 500 + T + d + r
+    S0 = wl.random_tensor((d, r), seed + 9, device=DEV)
+    S = S0.clone()
+    Sf = S0.clone()
+    Xs, dYs, caches = [], [], []
+    for m in range(M):
+        X, dY = _inputs(T, k, d, seed + 10 * m)
+        Xs.append(X)
+        dYs.append(dY)
+        caches.append(lg.project(X, seed, r))
+    for m in reversed(range(M)):
+        lg.contract(dYs[m], caches[m], r, S)
+        lg.sketch_accumulate(Xs[m], dYs[m], seed, r, Sf)
+    A = oracle.rademacher_projection(seed, r, k)
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(x) for x in Xs], [f64(y) for y in dYs], A)
+    inc = f64(S) - f64(S0)
+    e = assert_sketch_close(inc, ref, what="split S")
+    ef = assert_sketch_close(f64(Sf) - f64(S0), ref, what="fused S")
+    _say("split / fused S rel err", e, ef)
+
+
+def test_split_attn1536_workload():
+    """The 1.5B-class attention workload (8 x 4096 tokens, r = 64) through the
+    split calls, one cache per microbatch."""
+    w = wl.WORKLOADS["attn1536"]
+    L = w.layers[0]
+    r = w.ranks[0]
+    seed = wl.sign_seed(0)
+    _say("split attn1536", L, r)
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    G = np.zeros((L.d, L.k))
+    caches, dYs = [], []
+    for m in range(w.M):
+        X, dY = wl.layer_inputs(w, 0, m, device=DEV)
+        caches.append(lg.project(X, seed, r))
+        dYs.append(dY)
+        G += f64(dY).T @ f64(X)
+        del X
+    for m in range(w.M):
+        lg.contract(dYs[m], caches[m], r, S)
+    ref = oracle.sketch_from_gradient(G, oracle.rademacher_projection(seed, r, L.k))
+    e = assert_sketch_close(f64(S), ref)
+    _say("split attn1536 S rel err", e)
+
+
+def test_split_edge_cases():
+    _say("split edge cases")
+    r, d = 16, 40
+    # k == 0: the cache is zero and a contraction adds nothing
+    X = torch.empty((70, 0), dtype=torch.bfloat16, device=DEV)
+    P = torch.full((lg.projection_bytes(70, r),), 0xAB, dtype=torch.uint8, device=DEV)
+    lg.project(X, 3, r, P)
+    assert int(P.count_nonzero()) == 0
+    dY = wl.gaussian_bf16((70, d), 1.0, 5, device=DEV, ld=padded_ld(d))
+    S = wl.random_tensor((d, r), 6, device=DEV)
+    S0 = S.clone()
+    lg.contract(dY, P, r, S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    # T == 0 is a no-op for both calls
+    Xe = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    lg.project(Xe, 3, r, P)
+    lg.contract(torch.empty((0, d), dtype=torch.bfloat16, device=DEV), P, r, S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    # a larger cache than needed is accepted; one that is too small is refused
+    X, dY = _inputs(100, 264, d, 8)
+    big = torch.zeros((lg.projection_bytes(1000, r) + 4096,), dtype=torch.uint8, device=DEV)
+    lg.project(X, 4, r, big)
+    lg.contract(dY, big, r, S)
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(4, r, 264))
+    assert_sketch_close(f64(S) - f64(S0), ref)
+    small = torch.zeros((lg.projection_bytes(100, r) - 16,), dtype=torch.uint8, device=DEV)
+    with pytest.raises(lg.LograError):
+        lg.project(X, 4, r, small)
+    with pytest.raises(lg.LograError):
+        lg.contract(dY, small, r, S)

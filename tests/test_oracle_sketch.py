@@ -8,7 +8,10 @@ What ties the oracle to the pages and to mathematics rather than to itself:
   * rank(S A) <= r (section 2.1);
   * the reconstruction cosine for isotropic gradients, which reproduces the
     values the paper prints for the 1.5B model (section 3.4.1);
-  * the accumulator-size arithmetic the paper prints (section 2.2).
+  * the accumulator-size arithmetic the paper prints (section 2.2);
+  * the projection-first path dY^T (X A^T) (section 2.1, after equation 2)
+    equals the dense-gradient path, and projecting a unit row returns the
+    matching column of A.
 """
 
 import json
@@ -21,6 +24,7 @@ import pytest
 from oracle import (
     dense_gradient,
     low_rank_expand,
+    project_inputs,
     rademacher_projection,
     reconstruction_cosine,
     sketch_accumulate,
@@ -168,3 +172,33 @@ def test_empty_inputs(shape):
     S0 = np.ones((d, 4))
     S = sketch_accumulate(S0, [np.zeros((T, k))], [np.zeros((T, d))], A)
     np.testing.assert_array_equal(S, S0)
+
+
+def test_projection_first_equals_gradient_path():
+    # Projecting the inputs first and contracting with dY gives exactly the
+    # sketch of the dense gradient (associativity), microbatch by microbatch.
+    M, T, d, k, r = 3, 37, 11, 70, 16
+    Xs, dYs = _tiny(5, M, T, d, k)
+    A = rademacher_projection(3, r, k)
+    S = sum(dY.T @ project_inputs(X, A) for X, dY in zip(Xs, dYs))
+    ref = sketch_accumulate(np.zeros((d, r)), Xs, dYs, A)
+    np.testing.assert_allclose(S, ref, rtol=1e-12, atol=1e-10)
+
+
+def test_projection_of_unit_rows_is_columns_of_A():
+    # Row t of X equal to the unit vector e_j projects to column j of A; a
+    # zero row projects to zero; the projection is linear in X.
+    k, r = 300, 8
+    A = rademacher_projection(11, r, k)
+    cols = [0, 1, 255, 256, 299]
+    X = np.zeros((len(cols) + 1, k))
+    for t, j in enumerate(cols):
+        X[t, j] = 1.0
+    P = project_inputs(X, A)
+    for t, j in enumerate(cols):
+        np.testing.assert_array_equal(P[t], A[:, j])
+    np.testing.assert_array_equal(P[-1], np.zeros(r))
+    Y = np.random.default_rng(0).standard_normal((4, k))
+    np.testing.assert_allclose(project_inputs(2.0 * Y - X[:4], A), 2.0 * project_inputs(Y, A) - P[:4], atol=1e-12)
+    # every entry of A has magnitude 1/sqrt(r), so |P[t, c]| <= sum_j |X[t, j]| / sqrt(r)
+    assert np.all(np.abs(project_inputs(Y, A)) <= np.abs(Y).sum(axis=1, keepdims=True) / math.sqrt(r) + 1e-12)
