@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY.  Nothing in the product package may import this
 package.  The only callers are ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  It shares no code with the HIP library:
-the sign generator, the sketch, RowAdam and the merge are all written again
-here, in float64, from the definitions on the pages.
+the sign generator, the sketch, RowAdam, the merge and the predicted-KL
+step size are all written again here, in float64, from the definitions on the pages.
 
 Source pages (cited by title and section / equation only):
   [LoGRA]  "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
@@ -31,4 +31,13 @@ from .logra_oracle import (  # noqa: F401
     merge_update,
     rowadam_scale,
     reconstruction_cosine,
+)
+from .predicted_kl import (  # noqa: F401
+    token_probabilities,
+    score_rate_variance,
+    predicted_kl,
+    policy_kl_along,
+    kl_step_scale,
+    kl_budget,
+    effective_budget,
 )
