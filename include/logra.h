@@ -191,6 +191,61 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v,
                                  hipStream_t stream);
 
 /*
+ * Predicted KL of a proposed update (paper section 2.3, equation 6; derived in
+ * appendix A.1):
+ *
+ *     q = 1 / (2 n T^2) * sum_{s < n} Var_{v ~ p(s)}[ zdot[s][v] ],
+ *     p(s) = softmax(z[s][.] / T) over the V vocabulary entries,
+ *
+ * where row s of z holds the logits at one examined context and row s of
+ * zdot their rates of change along the proposed update D (evaluated before
+ * the update is applied; the caller computes them, e.g. with a forward-mode
+ * pass through the factors -eta U A, appendix A.1).  Var is the
+ * p-weighted variance.  One streaming pass over both arrays; per-row states
+ * are merged in a fixed order, so the result is deterministic.
+ *
+ *   z, zdot  n x V, row strides ldz, ldzd >= V (elements); dtype
+ *            LOGRA_DTYPE_F32 (float) or LOGRA_DTYPE_BF16 (bfloat16), the same
+ *            for both.  16-byte aligned bases; with n > 1 every row must
+ *            start on a 16-byte boundary (ld a multiple of 4 floats or 8 bf16).  A row
+ *            spans less than 2 GiB.
+ *   temperature  T > 0, finite (the sampling temperature of p).
+ *   row_var  optional (NULL to skip): n floats receiving Var per row.
+ *   q        one float receiving q.  n == 0 writes q = 0.
+ * A row whose logits are all -inf has no distribution: its Var, and q, are
+ * NaN.  NaN inputs propagate.  Neither output may overlap z, zdot or the
+ * other output.  V == 0 with n > 0 is LOGRA_ERR_SHAPE.  Scratch (32 bytes per
+ * row and column range) is held per (device, stream).
+ */
+#define LOGRA_DTYPE_F32 0
+#define LOGRA_DTYPE_BF16 1
+logra_status logra_predicted_kl(const void* z, int64_t ldz,
+                                const void* zdot, int64_t ldzd,
+                                int64_t n, int64_t V, int32_t dtype,
+                                float temperature,
+                                float* row_var, float* q,
+                                hipStream_t stream);
+
+/*
+ * Host helpers of the KL-budget step rule (no device work).
+ *
+ * logra_kl_step_scale: alpha = min(alpha_max, sqrt(delta / q)) (section 2.3,
+ *   equation 7; appendix A.2).  q == 0 gives alpha_max, q == +inf gives 0;
+ *   NaN for q < 0, NaN q, delta <= 0 or alpha_max <= 0.
+ * logra_kl_budget: delta_u = delta_min + (delta_max - delta_min) / 2 *
+ *   (1 + cos(pi (u - 1) / (H - 1))) for update u = 1..H (appendix D.1,
+ *   equation 16); u is clamped to [1, H] (the budget stays at delta_min after
+ *   the schedule); H < 2 gives delta_min.
+ * logra_kl_effective_budget: max(delta - kappa, delta / 2) (appendix D.1,
+ *   equation 17), kappa the smoothed rollout-minus-trainer log-probability
+ *   mismatch, clamped below at zero; NaN kappa (no valid measurement) gives
+ *   delta unchanged.
+ */
+double logra_kl_step_scale(double q, double delta, double alpha_max);
+double logra_kl_budget(int64_t u, int64_t H, double delta_max, double delta_min);
+double logra_kl_effective_budget(double delta, double kappa);
+
+/*
  * Materialise the signs s (r x k) as int8 (+1 / -1), row-major, row stride k,
  * into `out` (device).  A test and debugging aid: the hot path never stores
  * the signs.

@@ -30,6 +30,10 @@ __all__ = [
     "contract",
     "merge_update",
     "rowadam_scale",
+    "predicted_kl",
+    "kl_step_scale",
+    "kl_budget",
+    "kl_effective_budget",
     "signs",
     "workspace_bytes",
     "stream_read",
@@ -48,6 +52,10 @@ EXPORTED_SYMBOLS = (
     "logra_contract",
     "logra_merge_update",
     "logra_rowadam_scale",
+    "logra_predicted_kl",
+    "logra_kl_step_scale",
+    "logra_kl_budget",
+    "logra_kl_effective_budget",
     "logra_signs",
     "logra_stream_read",
     "logra_workspace_bytes",
@@ -82,6 +90,15 @@ def _declare(lib):
     lib.logra_merge_update.restype = ctypes.c_int
     lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
     lib.logra_rowadam_scale.restype = ctypes.c_int
+    lib.logra_predicted_kl.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_vp, c_vp, c_vp]
+    lib.logra_predicted_kl.restype = ctypes.c_int
+    c_d = ctypes.c_double
+    lib.logra_kl_step_scale.argtypes = [c_d, c_d, c_d]
+    lib.logra_kl_step_scale.restype = c_d
+    lib.logra_kl_budget.argtypes = [c_i64, c_i64, c_d, c_d]
+    lib.logra_kl_budget.restype = c_d
+    lib.logra_kl_effective_budget.argtypes = [c_d, c_d]
+    lib.logra_kl_effective_budget.restype = c_d
     lib.logra_signs.argtypes = [c_u64, c_i32, c_i64, c_vp, c_vp]
     lib.logra_signs.restype = ctypes.c_int
     lib.logra_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_vp, c_vp]
@@ -278,6 +295,60 @@ def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):
     _check(lib.logra_rowadam_scale(S.data_ptr(), _ld(S), v.data_ptr(), d, r, int(step),
                                    float(beta2), float(eps_rel), _stream_handle(S)))
     return S
+
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def predicted_kl(z, zdot, temperature: float, row_var=None, q=None):
+    """q = 1/(2 n T^2) sum_s Var_{v ~ softmax(z_s/T)}[zdot_s,v] on the device.
+
+    z, zdot: (n, V) float32 or bfloat16 (the same dtype), unit column stride.
+    row_var: optional (n,) float32 output of the per-row variances.
+    q: optional (1,) float32 output; allocated when None.  Returns q.
+    """
+    import torch
+
+    lib = load_library()
+    if z.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("z must be float32 or bfloat16")
+    _need(z, z.dtype, "z")
+    _need(zdot, z.dtype, "zdot")
+    if zdot.shape != z.shape:
+        raise ValueError("z and zdot must have the same shape")
+    n, V = z.shape
+    if q is None:
+        q = torch.empty(1, dtype=torch.float32, device=z.device)
+    _need(q, torch.float32, "q", ndim=1)
+    if row_var is not None:
+        _need(row_var, torch.float32, "row_var", ndim=1)
+        if row_var.numel() != n:
+            raise ValueError("row_var must have one entry per row")
+    dt = DTYPE_BF16 if z.dtype == torch.bfloat16 else DTYPE_F32
+    _check(
+        lib.logra_predicted_kl(
+            z.data_ptr() if n else None, _ld(z) if n else 0, zdot.data_ptr() if n else None,
+            _ld(zdot) if n else 0, n, V, dt, float(temperature),
+            row_var.data_ptr() if row_var is not None and n else None, q.data_ptr(), _stream_handle(q),
+        )
+    )
+    return q
+
+
+def kl_step_scale(q: float, delta: float, alpha_max: float) -> float:
+    """alpha = min(alpha_max, sqrt(delta / q)) (host; NaN for invalid input)."""
+    return float(load_library().logra_kl_step_scale(float(q), float(delta), float(alpha_max)))
+
+
+def kl_budget(u: int, H: int, delta_max: float, delta_min: float) -> float:
+    """Cosine-annealed KL budget of update u (host)."""
+    return float(load_library().logra_kl_budget(int(u), int(H), float(delta_max), float(delta_min)))
+
+
+def kl_effective_budget(delta: float, kappa: float) -> float:
+    """max(delta - kappa, delta / 2); NaN kappa leaves delta unchanged (host)."""
+    return float(load_library().logra_kl_effective_budget(float(delta), float(kappa)))
 
 
 def signs(seed: int, r: int, k: int, device="cuda"):

@@ -43,7 +43,7 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
 // it grows the stream is synchronised, so no queued kernel still uses the old
 // buffer.  New memory is zeroed (the sketch path keeps counters there that
 // must start at zero; its kernels leave them at zero).
-enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1 };
+enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaKL = 2 };
 struct Arena {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -380,6 +380,81 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+logra_status logra_predicted_kl(const void* z, int64_t ldz, const void* zdot, int64_t ldzd, int64_t n, int64_t V,
+                                int32_t dtype, float temperature, float* row_var, float* q, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (n < 0 || V < 0) return fail(LOGRA_ERR_SHAPE, "n and V must be >= 0");
+    if (dtype != LOGRA_DTYPE_F32 && dtype != LOGRA_DTYPE_BF16)
+      return fail(LOGRA_ERR_RANGE, "dtype must be LOGRA_DTYPE_F32 or LOGRA_DTYPE_BF16");
+    if (!(temperature > 0.0f) || !isfinite(temperature))
+      return fail(LOGRA_ERR_RANGE, "temperature must be finite and > 0");
+    if (!q) return fail(LOGRA_ERR_NULL, "q must be non-null");
+    if ((uintptr_t)q & 3) return fail(LOGRA_ERR_ALIGN, "q must be 4-byte aligned");
+    const size_t esz = dtype == LOGRA_DTYPE_BF16 ? 2 : 4;
+    if (n > 0) {
+      if (V == 0) return fail(LOGRA_ERR_SHAPE, "V must be >= 1 when n > 0 (softmax over an empty vocabulary)");
+      if (!z || !zdot) return fail(LOGRA_ERR_NULL, "z and zdot must be non-null");
+      if (ldz < V || ldzd < V) return fail(LOGRA_ERR_SHAPE, "ldz and ldzd must be >= V");
+      if (((uintptr_t)z & 15) || ((uintptr_t)zdot & 15) ||
+          (n > 1 && (((size_t)ldz * esz) % 16 || ((size_t)ldzd * esz) % 16)))
+        return fail(LOGRA_ERR_ALIGN, "z and zdot need 16-byte aligned bases and rows that start on 16-byte boundaries");
+      if (row_var && ((uintptr_t)row_var & 3)) return fail(LOGRA_ERR_ALIGN, "row_var must be 4-byte aligned");
+      if ((uint64_t)V * esz >= ((uint64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "a row must span less than 2 GiB");
+      const size_t zb = span_bytes(n, V, ldz, esz), db = span_bytes(n, V, ldzd, esz);
+      if (overlaps(q, 4, z, zb) || overlaps(q, 4, zdot, db))
+        return fail(LOGRA_ERR_ALIAS, "q overlaps z or zdot");
+      if (row_var && (overlaps(row_var, (size_t)n * 4, z, zb) || overlaps(row_var, (size_t)n * 4, zdot, db) ||
+                      overlaps(row_var, (size_t)n * 4, q, 4)))
+        return fail(LOGRA_ERR_ALIAS, "row_var overlaps z, zdot or q");
+    }
+    const KLPlan pl = plan_kl(n, V);
+    if ((uint64_t)n * (uint64_t)pl.n_split >= ((uint64_t)1 << 31))
+      return fail(LOGRA_ERR_SHAPE, "too many rows for one call; split them");
+    void* ws = nullptr;
+    if (n > 0) {
+      logra_status st = arena_get(kArenaKL, stream, pl.part_bytes, &ws);
+      if (st != LOGRA_OK) return st;
+    }
+    KLParams kp{};
+    kp.z = z; kp.ldz = ldz; kp.zd = zdot; kp.ldzd = ldzd; kp.n = n; kp.V = V;
+    kp.scale = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    kp.n_split = pl.n_split;
+    kp.span = pl.span;
+    kp.part = static_cast<double*>(ws);
+    const double t = (double)temperature;
+    const double inv_2nt2 = n > 0 ? 1.0 / (2.0 * (double)n * t * t) : 0.0;
+    kl_launch(pl, kp, dtype == LOGRA_DTYPE_BF16 ? 1 : 0, row_var, q, inv_2nt2, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "predicted-KL launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+double logra_kl_step_scale(double q, double delta, double alpha_max) {
+  if (!(delta > 0.0) || !(alpha_max > 0.0) || !(q >= 0.0)) return NAN;
+  if (q == 0.0) return alpha_max;
+  const double a = sqrt(delta / q);
+  return a < alpha_max ? a : alpha_max;
+}
+
+double logra_kl_budget(int64_t u, int64_t H, double delta_max, double delta_min) {
+  if (H < 2) return delta_min;
+  if (u < 1) u = 1;
+  if (u > H) u = H;
+  const double pi = 3.14159265358979323846;
+  return delta_min + 0.5 * (delta_max - delta_min) * (1.0 + cos(pi * (double)(u - 1) / (double)(H - 1)));
+}
+
+double logra_kl_effective_budget(double delta, double kappa) {
+  if (isnan(kappa)) return delta;
+  const double k = kappa > 0.0 ? kappa : 0.0;
+  const double a = delta - k, b = 0.5 * delta;
+  return a > b ? a : b;
 }
 
 logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out, hipStream_t stream) {

@@ -108,6 +108,32 @@ MergePlan plan_merge(int64_t d, int64_t k, int r);
 bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Predicted KL (equation 6): per-row softmax-weighted variance of the score
+// rates, then q.
+// ---------------------------------------------------------------------------
+struct KLParams {
+  const void* z;
+  int64_t ldz;
+  const void* zd;
+  int64_t ldzd;
+  int64_t n, V;
+  float scale;      // log2(e) / temperature
+  int n_split;      // workgroups per row
+  int64_t span;     // columns per workgroup (a multiple of 256 * 16)
+  double* part;     // n * n_split states (m, W, mu, M2)
+};
+
+struct KLPlan {
+  int n_split;
+  int64_t span;
+  size_t part_bytes;
+};
+
+KLPlan plan_kl(int64_t n, int64_t V);
+void kl_launch(const KLPlan& pl, const KLParams& p, int bf16, float* row_var, float* q, double inv_2nt2,
+               hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // RowAdam and the sign dump.
 // ---------------------------------------------------------------------------
 constexpr int kRowAdamBlocks = 256;

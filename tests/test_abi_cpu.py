@@ -137,6 +137,51 @@ def test_split_validation(lib):
     assert lib.logra_projection_bytes(16, 16) <= lib.logra_projection_bytes(300, 16)
 
 
+def _kl(lib, z=FAKE, ldz=1024, zd=FAKE * 64, ldzd=1024, n=16, V=1000, dtype=0, T=1.0, rv=FAKE * 4096, q=FAKE * 8192):
+    return lib.logra_predicted_kl(z, ldz, zd, ldzd, n, V, dtype, ctypes.c_float(T), rv, q, None)
+
+
+def test_predicted_kl_validation(lib):
+    assert _kl(lib, dtype=2) == ERR_RANGE
+    assert _kl(lib, T=0.0) == ERR_RANGE
+    assert _kl(lib, T=float("inf")) == ERR_RANGE
+    assert _kl(lib, T=float("nan")) == ERR_RANGE
+    assert _kl(lib, n=-1) == ERR_SHAPE
+    assert _kl(lib, q=None) == ERR_NULL
+    assert _kl(lib, z=None) == ERR_NULL
+    assert _kl(lib, V=0) == ERR_SHAPE
+    assert _kl(lib, ldz=999) == ERR_SHAPE
+    assert _kl(lib, ldz=1002) == ERR_ALIGN  # fp32 rows must start on 16-byte boundaries
+    assert _kl(lib, dtype=1, ldz=1004, ldzd=1008) == ERR_ALIGN  # bf16: multiples of 8 elements
+    assert _kl(lib, z=FAKE + 4) == ERR_ALIGN
+    assert _kl(lib, n=1, ldz=1001, ldzd=1003, q=None) == ERR_NULL  # one row: any stride passes the checks
+    assert _kl(lib, q=FAKE * 8192 + 2) == ERR_ALIGN
+    assert _kl(lib, rv=FAKE * 4096 + 1) == ERR_ALIGN
+    assert _kl(lib, q=FAKE + 64) == ERR_ALIAS  # q inside z
+    assert _kl(lib, rv=FAKE * 64 + 64) == ERR_ALIAS  # row_var inside zdot
+    assert _kl(lib, rv=FAKE * 8192 - 8) == ERR_ALIAS  # row_var runs into q
+
+
+def test_kl_host_helpers_match_oracle(lib):
+    import math
+
+    import oracle
+
+    for q, delta, amax in [(8e-4, 2e-4, 10.0), (5e-5, 2e-4, 10.0), (5e-5, 2e-4, 1.5), (0.0, 1e-4, 3.0),
+                           (math.inf, 1e-4, 3.0), (1.234e-7, 3e-5, 100.0)]:
+        assert lib.logra_kl_step_scale(q, delta, amax) == oracle.kl_step_scale(q, delta, amax)
+    for bad in [(-1.0, 1e-4, 1.0), (math.nan, 1e-4, 1.0), (1e-4, 0.0, 1.0), (1e-4, 1e-4, 0.0)]:
+        assert math.isnan(lib.logra_kl_step_scale(*bad))
+    for u in (-3, 0, 1, 2, 150, 299, 300, 301, 1000):
+        for H in (1, 2, 300, 1000):
+            got = lib.logra_kl_budget(u, H, 2e-4, 2e-5)
+            assert got == pytest.approx(oracle.kl_budget(u, H, 2e-4, 2e-5), rel=1e-14, abs=1e-20)
+    for delta, kappa in [(1e-4, 3e-5), (1e-4, 9e-5), (1e-4, -2e-5), (1e-4, 0.0), (2e-5, 1.0)]:
+        assert lib.logra_kl_effective_budget(delta, kappa) == pytest.approx(oracle.effective_budget(delta, kappa),
+                                                                             rel=1e-15)
+    assert lib.logra_kl_effective_budget(1e-4, math.nan) == 1e-4
+
+
 def _merge(lib, W=FAKE, ldw=512, U=FAKE * 64, ldu=16, d=256, k=512, r=16, scale=1e-3):
     return lib.logra_merge_update(W, ldw, U, ldu, d, k, 0, r, ctypes.c_float(scale), None)
 

@@ -161,3 +161,33 @@ def random_tensor(shape, seed: int, device="cuda", dtype=None, std: float = 1.0)
 
     t = torch.randn(shape, generator=_gen(device, seed), device=device, dtype=torch.float32) * std
     return t if dtype is None else t.to(dtype)
+
+
+# Predicted-KL probe inputs: logits and score-change rates over a
+# Qwen2.5-class vocabulary at a set of examined contexts.
+KL_VOCAB = 151936
+KL_CONTEXTS = 2048
+
+
+def kl_inputs(n: int, V: int, seed: int, device="cuda", dtype=None, ld: int | None = None,
+              z_std: float = 2.0, peak: float = 12.0, zdot_std: float = 1e-2):
+    """(z, zdot), each (n, V): z ~ N(0, z_std^2) with one seeded token per row
+    raised by `peak` (a peaked next-token distribution, as language-model
+    logits are), zdot ~ N(0, zdot_std^2).  Drawn in float32, then cast to
+    `dtype` (float32 by default).  With ``ld`` the rows live in a wider
+    buffer and the returned tensors are the left (n, V) views."""
+    import torch
+
+    dtype = torch.float32 if dtype is None else dtype
+    width = V if ld is None else ld
+    z = torch.randn((n, width), generator=_gen(device, seed), device=device, dtype=torch.float32)
+    z.mul_(z_std)
+    if n and V:
+        top = torch.randint(0, V, (n,), generator=_gen(device, seed + 2), device=device)
+        z[torch.arange(n, device=device), top] += peak
+    zd = torch.randn((n, width), generator=_gen(device, seed + 1), device=device, dtype=torch.float32)
+    zd.mul_(zdot_std)
+    z, zd = z.to(dtype), zd.to(dtype)
+    if width != V:
+        z, zd = z[:, :V], zd[:, :V]
+    return z, zd
