@@ -13,6 +13,8 @@ Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
                stream around M*K back-to-back calls over the rotating inputs,
                queued behind a sleep kernel so that they measure GPU time;
   merge        the fused merge against the same peak;
+  split        the forward/backward halves of a sketch call (project, contract);
+  predicted_kl the predicted-KL reduction over a 2048 x 151,936 probe;
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn1536]
@@ -96,6 +98,53 @@ def gpu_time_per_call(torch, stream, fn, n):
     ev1.record(stream)
     torch.cuda.synchronize()
     return ev0.elapsed_time(ev1) / n * 1e-3, host / n
+
+
+def proj_cols(r):
+    """Columns of the projection cache: 16 times the next power of two of ceil(r / 16)."""
+    nb, q = (r + 15) // 16, 1
+    while q < nb:
+        q *= 2
+    return 16 * q
+
+
+def split_bytes(T, k, d, r):
+    """Algorithmic HBM bytes of the split calls: the projection reads X and
+    writes the cache (a bf16 hi/lo pair per entry); the contraction reads dY
+    and the cache and reads and writes S."""
+    R = proj_cols(r)
+    return 2 * T * k + 4 * T * R, 2 * T * d + 4 * T * R + 8 * d * r
+
+
+def kl_bytes(n, V, esz):
+    """Algorithmic HBM bytes of one predicted-KL call: z and zdot read once,
+    one float per row and q written."""
+    return 2 * n * V * esz + 4 * n + 4
+
+
+def predicted_kl_timing(torch, lg, wl, stream, dev, calls: int):
+    """Predicted KL over the probe workload (2048 contexts x 151,936 tokens),
+    fp32 and bf16, timed like the sketch calls."""
+    out = {}
+    n, V = wl.KL_CONTEXTS, wl.KL_VOCAB
+    for name, dt, esz in (("fp32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        per = 2 * n * V * esz
+        ncopy = max(1, math.ceil(2.5 * MALL_BYTES / per))
+        ins = [wl.kl_inputs(n, V, 500 + c, device=dev, dtype=dt) for c in range(ncopy)]
+        rv = torch.empty(n, dtype=torch.float32, device=dev)
+        q = torch.empty(1, dtype=torch.float32, device=dev)
+        t, h = gpu_time_per_call(torch, stream, lambda i: lg.predicted_kl(ins[i % ncopy][0], ins[i % ncopy][1], 1.0,
+                                                                          row_var=rv, q=q), calls)
+        b = kl_bytes(n, V, esz)
+        out[name] = {"avg_us": t * 1e6, "achieved": b / t / 1e9, "frac": b / t / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": b, "host_us_per_call": h * 1e6}
+        del ins
+        torch.cuda.empty_cache()
+    return {
+        "kernel": "kl_rows_kernel + kl_finalize_kernel",
+        "workload": f"predicted-KL probe: {n} contexts x {V}-token vocabulary, logits and score rates",
+        "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", **out,
+    }
 
 
 def cpu_baseline(w, layer, r, seed, budget_s: float):
@@ -201,6 +250,7 @@ def main():
     ap.add_argument("--rank", type=int, default=0, help="rank r (default: the workload's first)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kl", action="store_true", help="skip the predicted-KL probe timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -329,6 +379,17 @@ def main():
     del buf
     t_rmw, _ = gpu_time(lambda i: Ws[i % n_w].mul_(1.0), n_merges)
     del Ws
+
+    # Split calls: the projection of every microbatch into its own cache (as
+    # at forward time), then the contractions from the caches (backward).
+    caches = [[lg.project(X, seed, r) for X, _ in mbs] for mbs in sets]
+    t_proj, _ = gpu_time(lambda i: lg.project(sets[(i // M) % nsets][i % M][0], seed, r,
+                                              caches[(i // M) % nsets][i % M]), n_calls)
+    t_con, _ = gpu_time(lambda i: lg.contract(sets[(i // M) % nsets][i % M][1], caches[(i // M) % nsets][i % M],
+                                              r, S), n_calls)
+    del caches
+    pb, cb = split_bytes(T, k, d, r)
+    kl = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps)) if not args.no_kl else None
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
     sk_gbs = sb / t_call / 1e9
@@ -394,6 +455,17 @@ def main():
             "merge_w_rmw_us": t_rmw * 1e6,
             "merge_frac_of_rmw": t_rmw / t_merge,
         },
+        "split": {
+            "what": "logra_project (forward, X -> cache) and logra_contract (backward, dY and cache -> S), per call",
+            "project_us": t_proj * 1e6,
+            "project_GBps": pb / t_proj / 1e9,
+            "project_frac": pb / t_proj / 1e9 / HBM_PEAK_GBS,
+            "contract_us": t_con * 1e6,
+            "contract_GBps": cb / t_con / 1e9,
+            "contract_frac": cb / t_con / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": [pb, cb],
+        },
+        "predicted_kl": kl,
         "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:
