@@ -135,9 +135,14 @@ def predicted_kl_timing(torch, lg, wl, stream, dev, calls: int):
         q = torch.empty(1, dtype=torch.float32, device=dev)
         t, h = gpu_time_per_call(torch, stream, lambda i: lg.predicted_kl(ins[i % ncopy][0], ins[i % ncopy][1], 1.0,
                                                                           row_var=rv, q=q), calls)
+        # the box's streaming-read time for the same two arrays (two launches)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        t_rd, _ = gpu_time_per_call(torch, stream, lambda i: (lg.stream_read(ins[i % ncopy][0], sink),
+                                                              lg.stream_read(ins[i % ncopy][1], sink)), calls)
         b = kl_bytes(n, V, esz)
         out[name] = {"avg_us": t * 1e6, "achieved": b / t / 1e9, "frac": b / t / 1e9 / HBM_PEAK_GBS,
-                     "algorithmic_bytes": b, "host_us_per_call": h * 1e6}
+                     "algorithmic_bytes": b, "host_us_per_call": h * 1e6,
+                     "read_ceiling_us": t_rd * 1e6, "frac_of_read_ceiling": t_rd / t}
         del ins
         torch.cuda.empty_cache()
     return {

@@ -165,6 +165,36 @@ logra_status logra_merge_update(void* W, int64_t ldw,
                                 hipStream_t stream);
 
 /*
+ * Grouped merge: the merge above applied to several matrices of one rank in
+ * one launch (Algorithm 1's trainer update for every sketched matrix of a
+ * layer, and the rollout side's policy synchronisation, where the engine
+ * regenerates each A from its seed and applies the received alpha eta U,
+ * section 2.2 "Memory and synchronization").  Item j is
+ *
+ *     W_j <- RNE_bf16( W_j - scale_j * (1/sqrt(r)) * U_j * s(seed_j) )
+ *
+ * with each item's arguments and rules exactly those of logra_merge_update;
+ * every W_j ends bitwise equal to what logra_merge_update gives for the same
+ * item (each matrix keeps its own tiling).  The items array is host memory,
+ * read during the call.  All items are validated before anything is
+ * enqueued; an item's W may not overlap another item's W or U
+ * (LOGRA_ERR_ALIAS).  Items with d == 0, k == 0 or scale == 0 are skipped.
+ * Sixteen matrices go to one launch; more are split over several launches.
+ */
+typedef struct {
+  void* W;          /* bf16, d x k, row stride ldw (read and written)  */
+  int64_t ldw;
+  const float* U;   /* fp32, d x r, row stride ldu                      */
+  int64_t ldu;
+  int64_t d, k;
+  uint64_t seed;
+  float scale;      /* alpha * eta for this matrix                      */
+} logra_merge_item;
+
+logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t count,
+                                        int32_t r, hipStream_t stream);
+
+/*
  * RowAdam row scaling (paper appendix B, equation 15), S -> U in place:
  *
  *     m_i   = (1/r) sum_j S_ij^2

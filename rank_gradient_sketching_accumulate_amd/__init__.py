@@ -29,6 +29,7 @@ __all__ = [
     "project",
     "contract",
     "merge_update",
+    "merge_update_grouped",
     "rowadam_scale",
     "predicted_kl",
     "kl_step_scale",
@@ -51,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "logra_project",
     "logra_contract",
     "logra_merge_update",
+    "logra_merge_update_grouped",
     "logra_rowadam_scale",
     "logra_predicted_kl",
     "logra_kl_step_scale",
@@ -76,6 +78,17 @@ class LograError(RuntimeError):
 _lib = None
 
 
+class MergeItem(ctypes.Structure):
+    """One matrix of a grouped merge (the C struct logra_merge_item)."""
+
+    _fields_ = [
+        ("W", ctypes.c_void_p), ("ldw", ctypes.c_int64),
+        ("U", ctypes.c_void_p), ("ldu", ctypes.c_int64),
+        ("d", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("seed", ctypes.c_uint64), ("scale", ctypes.c_float),
+    ]
+
+
 def _declare(lib):
     c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
@@ -88,6 +101,8 @@ def _declare(lib):
     lib.logra_contract.restype = ctypes.c_int
     lib.logra_merge_update.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_f, c_vp]
     lib.logra_merge_update.restype = ctypes.c_int
+    lib.logra_merge_update_grouped.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32, c_vp]
+    lib.logra_merge_update_grouped.restype = ctypes.c_int
     lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
     lib.logra_rowadam_scale.restype = ctypes.c_int
     lib.logra_predicted_kl.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_vp, c_vp, c_vp]
@@ -280,6 +295,27 @@ def merge_update(W, U, seed: int, r: int, scale: float):
         )
     )
     return W
+
+
+def merge_update_grouped(items, r: int):
+    """Grouped merge: items is a sequence of (W, U, seed, scale) with W (d, k)
+    bf16 and U (d, r) float32; every W is updated in place as
+    merge_update(W, U, seed, r, scale) would, in one launch.  Returns None."""
+    import torch
+
+    lib = load_library()
+    arr = (MergeItem * max(1, len(items)))()
+    stream = None
+    for j, (W, U, seed, scale) in enumerate(items):
+        _need(W, torch.bfloat16, "W")
+        _need(U, torch.float32, "U")
+        d, k = W.shape
+        if tuple(U.shape) != (d, r):
+            raise ValueError(f"item {j}: U must be ({d}, {r}), got {tuple(U.shape)}")
+        arr[j] = MergeItem(W.data_ptr(), _ld(W), U.data_ptr(), _ld(U), d, k, seed & (2**64 - 1), float(scale))
+        if stream is None:
+            stream = _stream_handle(W)
+    _check(lib.logra_merge_update_grouped(arr, len(items), r, stream))
 
 
 def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):

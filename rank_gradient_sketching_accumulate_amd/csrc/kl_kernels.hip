@@ -27,6 +27,8 @@
 // fixed order (deterministic), writes Var = M2 / W per row and q.
 #include <math.h>
 
+#include <type_traits>
+
 #include "logra_device.h"
 #include "logra_internal.h"
 
@@ -47,7 +49,9 @@ __device__ __forceinline__ KLState kl_merge(const KLState& a, const KLState& b) 
   if (b.w == 0.0) return a;
   if (a.w == 0.0) return b;
   const double m = fmax(a.m, b.m);
-  const double fa = exp2(a.m - m), fb = exp2(b.m - m);
+  // (the maxima are fp32 values: their difference rounded to fp32 and the
+  // hardware exp2 keep the rescale within a few fp32 ulps)
+  const double fa = __builtin_amdgcn_exp2f((float)(a.m - m)), fb = __builtin_amdgcn_exp2f((float)(b.m - m));
   const double wa = a.w * fa, wb = b.w * fb;
   const double w = wa + wb;
   const double dl = b.mu - a.mu;
@@ -131,14 +135,16 @@ __global__ __launch_bounds__(kKLThreads) void kl_rows_kernel(KLParams p) {
       b[u] = buf_load16(rd, off);
     }
   };
-  if (beg < end) load(cz, cd, beg);
-  for (int64_t e0 = beg; e0 < end; e0 += BLK) {
-    const bool more = e0 + BLK < end;
-    if (more) load(nz, nd, e0 + BLK);
-    float zs[kKLStep], zv[kKLStep];
+  // One step: 16 entries per thread.  Interior steps (every entry inside the
+  // range, the common case) skip the masking; the scale 1/T is folded into
+  // the exponent's fma, and the step's maximum is taken on the raw logits
+  // (scaling by log2(e)/T > 0 keeps the order).
+  auto step = [&](int64_t e0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    float zr[kKLStep], zv[kKLStep];
 #pragma unroll
     for (int u = 0; u < L; ++u) {
-      kl_unpack<BF16>(cz[u], zs + u * EPL);
+      kl_unpack<BF16>(cz[u], zr + u * EPL);
       kl_unpack<BF16>(cd[u], zv + u * EPL);
     }
     float cm = -INFINITY;
@@ -147,22 +153,28 @@ __global__ __launch_bounds__(kKLThreads) void kl_rows_kernel(KLParams p) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = u * EPL + i;
-        const bool valid = e0 + (int64_t)(u * kKLThreads + tid) * EPL + i < end;
-        zs[e] = valid ? zs[e] * scale : -INFINITY;
-        zv[e] = valid ? zv[e] - zref : 0.f;
-        cm = fmaxf(cm, zs[e]);
+        if constexpr (MASKED) {
+          const bool valid = e0 + (int64_t)(u * kKLThreads + tid) * EPL + i < end;
+          zr[e] = valid ? zr[e] : -INFINITY;
+          zv[e] = valid ? zv[e] - zref : 0.f;
+        } else {
+          zv[e] -= zref;
+        }
+        cm = fmaxf(cm, zr[e]);
       }
-    if (cm > m) {
-      const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - cm);
+    const float cms = cm * scale;
+    if (cms > m) {
+      const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - cms);
       W *= f;
       M2 *= f;
-      m = cm;
+      m = cms;
     }
-    if (cm != -INFINITY) {
+    if (cms != -INFINITY) {
+      const float nm = -m;
       float w[kKLStep], Wc = 0.f, S1 = 0.f;
 #pragma unroll
       for (int e = 0; e < kKLStep; ++e) {
-        w[e] = __builtin_amdgcn_exp2f(zs[e] - m);
+        w[e] = __builtin_amdgcn_exp2f(__fmaf_rn(zr[e], scale, nm));
         Wc += w[e];
         S1 = __fmaf_rn(w[e], zv[e], S1);
       }
@@ -182,6 +194,16 @@ __global__ __launch_bounds__(kKLThreads) void kl_rows_kernel(KLParams p) {
         W = Wn;
       }
     }
+  };
+
+  if (beg < end) load(cz, cd, beg);
+  for (int64_t e0 = beg; e0 < end; e0 += BLK) {
+    const bool more = e0 + BLK < end;
+    if (more) load(nz, nd, e0 + BLK);
+    if (e0 + BLK <= end)
+      step(e0, std::false_type{});
+    else
+      step(e0, std::true_type{});
     if (more) {
 #pragma unroll
       for (int u = 0; u < L; ++u) {
@@ -242,10 +264,12 @@ __global__ __launch_bounds__(256) void kl_finalize_kernel(const double* part, in
 KLPlan plan_kl(int64_t n, int64_t V) {
   KLPlan pl{};
   const int64_t blk = (int64_t)kKLThreads * kKLStep;
-  // About eight workgroups per CU over the chip, each with at least four
-  // steps of its row.
+  // Column ranges only when there are fewer than ~2048 rows: on the
+  // 2048 x 151,936 probe one range per row ran at 0.92 of the box's
+  // streaming-read time for the same bytes, and 4, 8 or 16 ranges per row
+  // were 3-10 % slower.  Each range keeps at least two steps of its row.
   int64_t want = n > 0 ? (2048 + n - 1) / n : 1;
-  const int64_t most = V > 0 ? (V + 4 * blk - 1) / (4 * blk) : 1;
+  const int64_t most = V > 0 ? (V + 2 * blk - 1) / (2 * blk) : 1;
   if (want > most) want = most;
   if (want < 1) want = 1;
   want = env_int("LOGRA_KL_SPLIT", (int)want);

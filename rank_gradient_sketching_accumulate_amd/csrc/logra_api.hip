@@ -10,6 +10,8 @@
 #include <string>
 #include <tuple>
 #include <utility>
+#include <vector>
+#include <algorithm>
 
 #include "../../include/logra.h"
 #include "logra_internal.h"
@@ -195,6 +197,43 @@ logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* d
   return LOGRA_OK;
 }
 
+// Validation and launch parameters of one merge (shared by the single and
+// grouped calls).  skip: nothing to do (empty matrix or scale 0).
+logra_status prepare_merge(void* W, int64_t ldw, const float* U, int64_t ldu, int64_t d, int64_t k, uint64_t seed,
+                           int32_t r, float scale, MergeParams& mp, MergePlan& pl, bool& skip) {
+  skip = false;
+  if (d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "d and k must be >= 0");
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (ldu < r) return fail(LOGRA_ERR_SHAPE, "ldu must be >= r");
+  if (d == 0 || k == 0) {
+    skip = true;
+    return LOGRA_OK;
+  }
+  if (!W || !U) return fail(LOGRA_ERR_NULL, "W and U must be non-null");
+  if (ldw < k) return fail(LOGRA_ERR_SHAPE, "ldw must be >= k");
+  if (((uintptr_t)W & 7) || (ldw & 3)) return fail(LOGRA_ERR_ALIGN, "W needs an 8-byte aligned base and ldw a multiple of 4");
+  if ((uintptr_t)U & 3) return fail(LOGRA_ERR_ALIGN, "U must be 4-byte aligned");
+  if (!isfinite(scale)) return fail(LOGRA_ERR_RANGE, "scale must be finite");
+  if (overlaps(W, span_bytes(d, k, ldw, 2), U, span_bytes(d, r, ldu, 4))) return fail(LOGRA_ERR_ALIAS, "W overlaps U");
+  if (d > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "d and k must be below 2^31");
+  if ((uint64_t)d * (uint64_t)ldw * 2 >= ((uint64_t)1 << 32) - 4096 ||
+      (uint64_t)d * (uint64_t)ldu * 4 >= ((uint64_t)1 << 32) - 4096)
+    return fail(LOGRA_ERR_SHAPE, "W or U spans 4 GiB or more; merge the rows in several calls");
+  if (scale == 0.0f) {
+    skip = true;
+    return LOGRA_OK;
+  }
+  pl = merge_plan_for(d, k, r);
+  mp = MergeParams{};
+  mp.W = static_cast<uint16_t*>(W);
+  mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;
+  mp.u_vec = (((uintptr_t)U & 15) == 0 && (ldu & 3) == 0) ? 1 : 0;
+  mp.seed = seed;
+  mp.scale_eff = (float)((double)scale / sqrt((double)r));
+  mp.n_rb = pl.n_rb; mp.n_cr = pl.n_cr; mp.cr_cols = pl.cr_cols;
+  return LOGRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,33 +351,74 @@ logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ld
                                 uint64_t seed, int32_t r, float scale, hipStream_t stream) {
   try {
     g_last_error.clear();
-    if (d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "d and k must be >= 0");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
-    if (ldu < r) return fail(LOGRA_ERR_SHAPE, "ldu must be >= r");
-    if (d == 0 || k == 0) return LOGRA_OK;
-    if (!W || !U) return fail(LOGRA_ERR_NULL, "W and U must be non-null");
-    if (ldw < k) return fail(LOGRA_ERR_SHAPE, "ldw must be >= k");
-    if (((uintptr_t)W & 7) || (ldw & 3)) return fail(LOGRA_ERR_ALIGN, "W needs an 8-byte aligned base and ldw a multiple of 4");
-    if ((uintptr_t)U & 3) return fail(LOGRA_ERR_ALIGN, "U must be 4-byte aligned");
-    if (!isfinite(scale)) return fail(LOGRA_ERR_RANGE, "scale must be finite");
-    if (overlaps(W, span_bytes(d, k, ldw, 2), U, span_bytes(d, r, ldu, 4))) return fail(LOGRA_ERR_ALIAS, "W overlaps U");
-    if (d > ((int64_t)1 << 31) || k > ((int64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "d and k must be below 2^31");
-    if (scale == 0.0f) return LOGRA_OK;
-
-    if ((uint64_t)d * (uint64_t)ldw * 2 >= ((uint64_t)1 << 32) - 4096 ||
-        (uint64_t)d * (uint64_t)ldu * 4 >= ((uint64_t)1 << 32) - 4096)
-      return fail(LOGRA_ERR_SHAPE, "W or U spans 4 GiB or more; merge the rows in several calls");
-    const MergePlan pl = merge_plan_for(d, k, r);
     MergeParams mp{};
-    mp.W = static_cast<uint16_t*>(W);
-    mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;
-    mp.u_vec = (((uintptr_t)U & 15) == 0 && (ldu & 3) == 0) ? 1 : 0;
-    mp.seed = seed;
-    mp.scale_eff = (float)((double)scale / sqrt((double)r));
-    mp.n_rb = pl.n_rb; mp.n_cr = pl.n_cr; mp.cr_cols = pl.cr_cols;
+    MergePlan pl{};
+    bool skip = false;
+    logra_status st = prepare_merge(W, ldw, U, ldu, d, k, seed, r, scale, mp, pl, skip);
+    if (st != LOGRA_OK || skip) return st;
     if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t count, int32_t r,
+                                        hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (count < 0) return fail(LOGRA_ERR_SHAPE, "count must be >= 0");
+    if (count == 0) return LOGRA_OK;
+    if (!items) return fail(LOGRA_ERR_NULL, "items must be non-null");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    // Validate everything before anything is enqueued.
+    std::vector<MergeParams> mps;
+    MergePlan pl0{};
+    bool have = false;
+    for (int32_t j = 0; j < count; ++j) {
+      const logra_merge_item& it = items[j];
+      MergeParams mp{};
+      MergePlan pl{};
+      bool skip = false;
+      logra_status st = prepare_merge(it.W, it.ldw, it.U, it.ldu, it.d, it.k, it.seed, r, it.scale, mp, pl, skip);
+      if (st != LOGRA_OK)
+        return fail(st, "item " + std::to_string(j) + ": " + g_last_error);
+      const size_t wb = span_bytes(it.d, it.k, it.ldw, 2);
+      for (int32_t i = 0; i < j; ++i)
+        if (overlaps(it.W, wb, items[i].W, span_bytes(items[i].d, items[i].k, items[i].ldw, 2)) ||
+            overlaps(it.W, wb, items[i].U, span_bytes(items[i].d, r, items[i].ldu, 4)) ||
+            overlaps(items[i].W, span_bytes(items[i].d, items[i].k, items[i].ldw, 2), it.U,
+                     span_bytes(it.d, r, it.ldu, 4)))
+          return fail(LOGRA_ERR_ALIAS, "item " + std::to_string(j) + " overlaps the W or U of item " +
+                                           std::to_string(i) + " (a W written by one item is read or written by another)");
+      if (skip) continue;
+      if (!have) {
+        pl0 = pl;
+        have = true;
+      } else if (pl.NBW != pl0.NBW || pl.CB != pl0.CB || pl.NK != pl0.NK) {
+        return fail(LOGRA_ERR_RANGE, "items need the same tiling (set by r)");
+      }
+      mp.n_rb = pl.n_rb;
+      mp.n_cr = pl.n_cr;
+      mp.cr_cols = pl.cr_cols;
+      mps.push_back(mp);
+    }
+    for (size_t b = 0; b < mps.size(); b += kMaxMergeGroup) {
+      MergeGroup g{};
+      g.count = (int)std::min<size_t>(kMaxMergeGroup, mps.size() - b);
+      g.start[0] = 0;
+      for (int j = 0; j < g.count; ++j) {
+        g.p[j] = mps[b + j];
+        const int64_t next = (int64_t)g.start[j] + (int64_t)g.p[j].n_rb * g.p[j].n_cr;
+        if (next >= ((int64_t)1 << 31) - 8) return fail(LOGRA_ERR_SHAPE, "too many workgroups for one launch");
+        g.start[j + 1] = (int)next;
+      }
+      if (!merge_group_launch(pl0, g, stream)) return fail(LOGRA_ERR_RANGE, "no grouped merge kernel for this tile");
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "grouped merge launch");
+    }
     return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");

@@ -107,6 +107,16 @@ struct MergePlan {
 MergePlan plan_merge(int64_t d, int64_t k, int r);
 bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s);
 
+// Up to kMaxMergeGroup matrices of one rank merged by one launch; matrix j
+// owns logical workgroups [start[j], start[j+1]) (its own n_rb * n_cr tiles).
+constexpr int kMaxMergeGroup = 16;
+struct MergeGroup {
+  int count;
+  int start[kMaxMergeGroup + 1];
+  MergeParams p[kMaxMergeGroup];
+};
+bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Predicted KL (equation 6): per-row softmax-weighted variance of the score
 // rates, then q.

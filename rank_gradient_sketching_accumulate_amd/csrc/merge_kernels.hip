@@ -40,8 +40,10 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
   return x;
 }
 
+// The work of one workgroup: tile `lin` (row block lin / n_cr, column range
+// lin % n_cr) of the matrix p describes.
 template <int NBW, int CB, int NK, int PD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_kernel(MergeParams p) {
+__device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   constexpr int STR = 9;        // dwords per row (row-major bits) / per column (column-major bits)
   constexpr int CW = 16 * CB;   // columns per chunk
   constexpr int KR = 32 * NK;   // sign rows generated (U entries >= r are zero)
@@ -54,7 +56,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   __shared__ uint32_t colbits[256 * STR];
   __shared__ float tiles[4 * RW * TSTR];
 
-  const int lin = xcd_linear_id_m(blockIdx.x, gridDim.x);
   const int rb = lin / p.n_cr;
   const int cr = lin - rb * p.n_cr;
   if (rb >= p.n_rb) return;
@@ -231,6 +232,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   }
 }
 
+template <int NBW, int CB, int NK, int PD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_kernel(MergeParams p) {
+  merge_tile<NBW, CB, NK, PD>(p, xcd_linear_id_m(blockIdx.x, gridDim.x));
+}
+
+// Several matrices in one launch (same rank, so the same tiling): the
+// logical workgroup ids are dealt to the matrices by the prefix table
+// `start`; each matrix's tiles are exactly those of its own launch.
+template <int NBW, int CB, int NK, int PD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_group_kernel(MergeGroup grp) {
+  const int lin = xcd_linear_id_m(blockIdx.x, gridDim.x);
+  int j = 0;
+  while (j + 1 < grp.count && lin >= grp.start[j + 1]) ++j;
+  if (lin >= grp.start[grp.count]) return;
+  merge_tile<NBW, CB, NK, PD>(grp.p[j], lin - grp.start[j]);
+}
+
 namespace {
 size_t align_up_m(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
@@ -276,6 +294,25 @@ bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s) {
   LOGRA_MERGE(1, 4, 4) LOGRA_MERGE(1, 8, 4) LOGRA_MERGE(2, 4, 4)
   LOGRA_MERGE(1, 4, 8) LOGRA_MERGE(1, 8, 8) LOGRA_MERGE(2, 4, 8)
 #undef LOGRA_MERGE
+  return false;
+}
+
+}  // namespace logra
+
+namespace logra {
+
+bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s) {
+  const int grid = (int)align_up_m((size_t)g.start[g.count], 8);
+#define LOGRA_MERGE_G(nbw, cb, nk)                                                                \
+  if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                              \
+    hipLaunchKernelGGL((merge_group_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, g);     \
+    return true;                                                                                  \
+  }
+  LOGRA_MERGE_G(1, 4, 1) LOGRA_MERGE_G(1, 8, 1) LOGRA_MERGE_G(2, 4, 1) LOGRA_MERGE_G(2, 8, 1)
+  LOGRA_MERGE_G(1, 4, 2) LOGRA_MERGE_G(1, 8, 2) LOGRA_MERGE_G(2, 4, 2) LOGRA_MERGE_G(2, 8, 2)
+  LOGRA_MERGE_G(1, 4, 4) LOGRA_MERGE_G(1, 8, 4) LOGRA_MERGE_G(2, 4, 4)
+  LOGRA_MERGE_G(1, 4, 8) LOGRA_MERGE_G(1, 8, 8) LOGRA_MERGE_G(2, 4, 8)
+#undef LOGRA_MERGE_G
   return false;
 }
 

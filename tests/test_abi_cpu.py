@@ -201,6 +201,35 @@ def test_merge_validation(lib):
     assert _merge(lib, scale=0.0) == OK
 
 
+def _items(*specs):
+    arr = (lg.MergeItem * max(1, len(specs)))()
+    for j, sp in enumerate(specs):
+        base = dict(W=FAKE * (1 + 64 * j), ldw=512, U=FAKE * (2048 + 64 * j), ldu=16, d=256, k=512, seed=j, scale=1e-3)
+        base.update(sp)
+        arr[j] = lg.MergeItem(base["W"], base["ldw"], base["U"], base["ldu"], base["d"], base["k"], base["seed"],
+                              base["scale"])
+    return arr
+
+
+def test_grouped_merge_validation(lib):
+    assert lib.logra_merge_update_grouped(None, 0, 16, None) == OK
+    assert lib.logra_merge_update_grouped(None, 2, 16, None) == ERR_NULL
+    assert lib.logra_merge_update_grouped(_items({}), -1, 16, None) == ERR_SHAPE
+    assert lib.logra_merge_update_grouped(_items({}), 1, 0, None) == ERR_RANGE
+    # an invalid item names itself; nothing is enqueued
+    assert lib.logra_merge_update_grouped(_items({}, {"W": None}), 2, 16, None) == ERR_NULL
+    assert b"item 1" in lib.logra_last_error()
+    assert lib.logra_merge_update_grouped(_items({}, {}, {"ldu": 8}), 3, 16, None) == ERR_SHAPE
+    assert lib.logra_merge_update_grouped(_items({"scale": float("nan")}), 1, 16, None) == ERR_RANGE
+    assert lib.logra_merge_update_grouped(_items({"W": FAKE + 4}), 1, 16, None) == ERR_ALIGN
+    # item 1 writes a W that item 0 also writes, or reads as its U
+    assert lib.logra_merge_update_grouped(_items({}, {"W": FAKE + 4096}), 2, 16, None) == ERR_ALIAS
+    assert b"item 0" in lib.logra_last_error()
+    assert lib.logra_merge_update_grouped(_items({}, {"W": FAKE * 2048}), 2, 16, None) == ERR_ALIAS
+    # all items empty or with scale 0: nothing to do, no device work
+    assert lib.logra_merge_update_grouped(_items({"d": 0}, {"scale": 0.0}, {"k": 0}), 3, 16, None) == OK
+
+
 def _rowadam(lib, S=FAKE, lds=16, v=FAKE * 64, d=256, r=16, step=1, beta2=0.95, eps=1e-8):
     return lib.logra_rowadam_scale(S, lds, v, d, r, step, ctypes.c_float(beta2), ctypes.c_float(eps), None)
 
