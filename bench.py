@@ -14,6 +14,7 @@ Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
                queued behind a sleep kernel so that they measure GPU time;
   merge        the fused merge against the same peak;
   split        the forward/backward halves of a sketch call (project, contract);
+  grouped_merge a 1.5B-class layer's seven merges in one launch vs seven;
   predicted_kl the predicted-KL reduction over a 2048 x 151,936 probe;
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
@@ -149,6 +150,39 @@ def predicted_kl_timing(torch, lg, wl, stream, dev, calls: int):
         "kernel": "kl_rows_kernel + kl_finalize_kernel",
         "workload": f"predicted-KL probe: {n} contexts x {V}-token vocabulary, logits and score rates",
         "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", **out,
+    }
+
+
+def grouped_merge_timing(torch, lg, wl, stream, dev, calls: int, r: int = 128, scale: float = 1e-5):
+    """A 1.5B-class layer's seven sketched matrices (q, k, v, o: 1536 x 1536
+    and 256 x 1536; gate, up: 8960 x 1536; down: 1536 x 8960) merged by one
+    grouped launch and by seven separate merges, over enough copies of the
+    layer's weights to exceed the MALL."""
+    shapes = [(1536, 1536), (256, 1536), (256, 1536), (1536, 1536), (8960, 1536), (8960, 1536), (1536, 8960)]
+    per = sum(2 * d * k for d, k in shapes)
+    ncopy = max(2, math.ceil(2.5 * MALL_BYTES / per))
+    Us = [wl.random_tensor((d, r), 900 + j, device=dev) for j, (d, k) in enumerate(shapes)]
+    Ws = [[wl.gaussian_bf16((d, k), 0.02, 800 + j, device=dev) for j, (d, k) in enumerate(shapes)]]
+    for _ in range(ncopy - 1):
+        Ws.append([W.clone() for W in Ws[0]])
+    items = [[(Ws[c][j], Us[j], 100 + j, scale) for j in range(len(shapes))] for c in range(ncopy)]
+    t_g, _ = gpu_time_per_call(torch, stream, lambda i: lg.merge_update_grouped(items[i % ncopy], r), calls)
+
+    def separate(i):
+        for W, U, seed, sc in items[i % ncopy]:
+            lg.merge_update(W, U, seed, r, sc)
+
+    t_s, _ = gpu_time_per_call(torch, stream, separate, calls)
+    b = sum(merge_bytes(d, k, r) for d, k in shapes)
+    del Ws, items
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "merge_group_kernel",
+        "workload": f"1.5B-class layer, 7 matrices, r={r}",
+        "grouped_us": t_g * 1e6, "separate_us": t_s * 1e6,
+        "achieved": b / t_g / 1e9, "frac": b / t_g / 1e9 / HBM_PEAK_GBS,
+        "separate_frac": b / t_s / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": b,
+        "unit": "GB/s", "peak": HBM_PEAK_GBS, "weight_copies_rotated": ncopy,
     }
 
 
@@ -394,6 +428,7 @@ def main():
                                               r, S), n_calls)
     del caches
     pb, cb = split_bytes(T, k, d, r)
+    grouped = grouped_merge_timing(torch, lg, wl, stream, dev, max(10, args.steps))
     kl = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps)) if not args.no_kl else None
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
@@ -470,6 +505,7 @@ def main():
             "contract_frac": cb / t_con / 1e9 / HBM_PEAK_GBS,
             "algorithmic_bytes": [pb, cb],
         },
+        "grouped_merge": grouped,
         "predicted_kl": kl,
         "kernel_source_sha": kernel_source_sha(),
     }
