@@ -15,6 +15,7 @@ import pytest
 import oracle
 import workloads as wl
 from tests._util import assert_sketch_close, f64, padded_ld, rel_frob
+from tests.test_gpu_parity import PLAN_OVERRIDES, _plan_id
 
 torch = pytest.importorskip("torch")
 lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
@@ -180,3 +181,30 @@ def test_split_edge_cases():
         lg.project(X, 4, r, small)
     with pytest.raises(lg.LograError):
         lg.contract(dY, small, r, S)
+
+
+@pytest.mark.parametrize("r", [64, 128, 256])
+@pytest.mark.parametrize("env", PLAN_OVERRIDES, ids=_plan_id)
+def test_split_launch_plans(r, env, monkeypatch):
+    """The split calls keep the projection's column-split partials and the
+    contraction's token-split partials in library scratch laid out without
+    the P planes: every tiling the planner can pick gives the oracle's sketch
+    and a correct cache."""
+    if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
+        env = dict(env, LOGRA_PROJ_SMALL=0)
+    if r == 256 and env.get("LOGRA_PROJ_WK", 1) != 1:
+        pytest.skip("rank 256 runs with one wave column along k")
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    T, k, d = 700, 1300, 300
+    _say("split plans", r, env)
+    X, dY = _inputs(T, k, d, 4343)
+    P = lg.project(X, 12, r)
+    got, pad = decode_cache(P, T, r)
+    ref_p = oracle.project_inputs(f64(X), oracle.rademacher_projection(12, r, k)) * math.sqrt(r)
+    assert rel_frob(got, ref_p) <= 2e-5
+    np.testing.assert_array_equal(pad, np.zeros_like(pad))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    lg.contract(dY, P, r, S)
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(12, r, k))
+    assert_sketch_close(f64(S), ref)
