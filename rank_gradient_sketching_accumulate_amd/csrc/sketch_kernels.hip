@@ -1083,8 +1083,23 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   const int64_t nks = T32 / 32;
   int64_t BD, min_steps;
   if (pl.NB <= 4) {
-    pl.cvar = 0;  // eight waves on every eighth step of 64 rows, stream-K over steps
-    BD = 16 * kDC;
+    // Eight waves on every eighth step of 64 rows, stream-K over steps; at
+    // NB = 4 the token-lane tiles of 128 or 256 rows (WM = 2, 4) are the
+    // alternative: P is re-read from L2 half or a quarter as often, for more
+    // atomic adds into S per step.  They pay off only for tall S (18944 x
+    // 3584 at r = 64: 99.6 -> 93.1 us per 8192-token call; 1536- and
+    // 3584-row layers ran 0-35 % slower).
+    const int tile4 = pl.NB == 4 ? env_int("LOGRA_CON_TILE", d >= 8192 ? 1 : 0) : 0;
+    if (tile4) {
+      int wm = env_int("LOGRA_CON_WM", 2);
+      if (wm != 1 && wm != 2 && wm != 4) wm = 2;
+      pl.WM = wm;
+      pl.cvar = 5;
+      BD = 16 * kDC * wm;
+    } else {
+      pl.cvar = 0;
+      BD = 16 * kDC;
+    }
     min_steps = 16;
   } else {
     // Eight-wave tiles (512 x 128 or 256 x 256) where they still give a few
@@ -1267,6 +1282,7 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
         hipLaunchKernelGGL((contract_tile_kernel<nb, wm, wn, 8, 2>), dim3(pl.cgrid), dim3(512), 0, s, p); \
         return true;                                                                                  \
       }
+      LOGRA_CT(4, 1, 1) LOGRA_CT(4, 2, 1) LOGRA_CT(4, 4, 1)
       LOGRA_CT(8, 1, 2) LOGRA_CT(8, 2, 2) LOGRA_CT(8, 4, 2) LOGRA_CT(16, 1, 4) LOGRA_CT(16, 2, 4)
 #undef LOGRA_CT
       return false;

@@ -206,6 +206,10 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 16},
     {"LOGRA_CON_BANDS": 1, "LOGRA_CON_GRID": 5},
     {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_BIGDP": 1, "LOGRA_CON_TS": 3},
+    {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 1},
+    {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2},
+    {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 4},
+    {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2, "LOGRA_CON_BANDS": 1, "LOGRA_CON_GRID": 37},
 ]
 
 
