@@ -293,7 +293,9 @@ logra_status logra_stream_read(const void* ptr, size_t bytes, uint32_t* sink, hi
 
 /* Upper bound on the per-stream scratch logra_sketch_accumulate allocates for
  * T tokens at rank r, over layer shapes up to 2^20 x 2^20 (P as a bf16 hi/lo
- * pair, column-split and token-split partial sums, per-tile counters). */
+ * pair, column-split and token-split partial sums, per-tile counters).  It
+ * also bounds the scratch of logra_project and logra_contract, which keep
+ * the same partial sums but not P. */
 size_t logra_workspace_bytes(int64_t T, int32_t r);
 
 /* Static text for a status code. */
