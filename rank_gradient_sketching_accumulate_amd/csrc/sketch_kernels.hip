@@ -1054,8 +1054,12 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     MBW = env_int("LOGRA_PROJ_MB", MBW);
     WK = env_int("LOGRA_PROJ_WK", WK);
     // Eight-wave workgroups (two token rows) halve the sign generation per
-    // token at rank >= 128, where Philox costs more than the expansion.
-    int NW = env_int("LOGRA_PROJ_NW", k >= 8192 ? 8 : 4) == 8 ? 8 : 4;
+    // token at rank >= 128, where Philox costs more than the expansion: for
+    // long rows, and for long microbatches, where 64-token tiles still give
+    // 256 workgroups without column splits (16384 tokens x 5120 columns at
+    // r = 256: 79 -> 71 us; 8192-token microbatches of 3584 columns gained
+    // nothing).
+    int NW = env_int("LOGRA_PROJ_NW", (k >= 8192 || T32 >= 16384) ? 8 : 4) == 8 ? 8 : 4;
     if (NW == 8 && !(pl.NB >= 8 && MBW == 2 && WK >= 2)) NW = 4;
     pl.PNW = NW;
     pl.MBW = MBW;
