@@ -289,9 +289,10 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
     if (P_bytes < need) return fail(LOGRA_ERR_SHAPE, "P_bytes is smaller than logra_projection_bytes(T, r)");
     if ((uintptr_t)P & 15) return fail(LOGRA_ERR_ALIGN, "P must be 16-byte aligned");
     if (k == 0) {
-      // X has no columns: P = X s^T is zero.
-      hipError_t e = hipMemsetAsync(P, 0, need, stream);
-      if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+      // X has no columns: P = X s^T is zero (need is a multiple of 16 bytes).
+      zero_fill_launch(P, (int64_t)(need / 16), stream);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "zero fill launch");
       return LOGRA_OK;
     }
     if (!X) return fail(LOGRA_ERR_NULL, "X must be non-null");

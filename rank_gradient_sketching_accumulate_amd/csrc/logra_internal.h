@@ -151,6 +151,8 @@ void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float bet
                     float eps_rel, float* root, float* ssq, double* partial, double* scal, hipStream_t s);
 void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s);
 void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_t s);
+// dst[0 .. 16*n16) = 0 (dst 16-byte aligned).
+void zero_fill_launch(void* dst, int64_t n16, hipStream_t s);
 
 int env_int(const char* name, int dflt);
 

@@ -156,4 +156,18 @@ void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_
                      static_cast<const u32x4*>(ptr), n16, sink);
 }
 
+// Zero fill of n16 16-byte words (a kernel rather than a memset node, so that
+// a caller may capture the call in a HIP graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* __restrict__ dst, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    dst[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+void zero_fill_launch(void* dst, int64_t n16, hipStream_t s) {
+  int64_t grid = (n16 + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<u32x4*>(dst), n16);
+}
+
 }  // namespace logra

@@ -1,0 +1,114 @@
+"""HIP graph capture of the whole path (no library call allocates once its
+scratch has been sized): sketch calls, split calls, RowAdam, merges and the
+predicted-KL reduction captured on a side stream, then replayed several
+times with new inputs written eagerly between the replays.  Every replay is
+checked against eager calls on the same inputs: bitwise where the kernels
+are deterministic (merge, grouped merge, predicted KL, RowAdam from the same
+S), and to fp32 rounding where atomic adds make S order-dependent.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests._util import assert_sketch_close, f64, padded_ld, rel_frob
+
+torch = pytest.importorskip("torch")
+lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_graph_capture_and_replay():
+    print("[case] graph capture", flush=True)
+    T, k, d, r, seed, scale = 1000, 1536, 700, 64, 21, 1e-3
+    X = wl.gaussian_bf16((T, k), 1.0, 1, device=DEV, ld=padded_ld(k))
+    dY = wl.gaussian_bf16((T, d), 1e-2, 2, device=DEV, ld=padded_ld(d))
+    W0 = wl.gaussian_bf16((d, k), 0.02, 3, device=DEV)
+    z, zd = wl.kl_inputs(64, 5000, 4, device=DEV)
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    S2 = torch.zeros_like(S)
+    U = torch.zeros_like(S)
+    v = torch.zeros(d, dtype=torch.float32, device=DEV)
+    W = torch.empty_like(W0)
+    Wg = torch.empty_like(W0)
+    P = torch.empty(lg.projection_bytes(T, r), dtype=torch.uint8, device=DEV)
+    q = torch.empty(1, dtype=torch.float32, device=DEV)
+    rv = torch.empty(64, dtype=torch.float32, device=DEV)
+
+    def body():
+        S.zero_()
+        lg.sketch_accumulate(X, dY, seed, r, S)
+        lg.sketch_accumulate(X, dY, seed, r, S)
+        torch.mul(W0, 1.0, out=W)
+        lg.merge_update(W, S, seed, r, scale)
+        lg.project(X, seed, r, P)
+        S2.zero_()
+        lg.contract(dY, P, r, S2)
+        torch.mul(S, 1.0, out=U)
+        v.zero_()
+        lg.rowadam_scale(U, v, 1, 0.95, 1e-8)
+        torch.mul(W0, 1.0, out=Wg)
+        lg.merge_update_grouped([(Wg, U, seed + 1, scale)], r)
+        lg.predicted_kl(z, zd, 0.9, row_var=rv, q=q)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()  # sizes the library's scratch and fills its plan caches
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        body()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        # eager work between replays: new inputs
+        X.copy_(wl.gaussian_bf16((T, k), 1.0, 100 + rep, device=DEV, ld=padded_ld(k)))
+        dY.copy_(wl.gaussian_bf16((T, d), 1e-2, 200 + rep, device=DEV, ld=padded_ld(d)))
+        zn, zdn = wl.kl_inputs(64, 5000, 300 + rep, device=DEV)
+        z.copy_(zn)
+        zd.copy_(zdn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+
+        Se = torch.zeros_like(S)
+        lg.sketch_accumulate(X, dY, seed, r, Se)
+        lg.sketch_accumulate(X, dY, seed, r, Se)
+        assert rel_frob(f64(S), f64(Se)) <= 1e-6, f"replay {rep}: S"
+        assert rel_frob(f64(S2), 0.5 * f64(Se)) <= 1e-6, f"replay {rep}: split S"
+        We = W0.clone()
+        lg.merge_update(We, S, seed, r, scale)  # the replay's own S: bitwise the same W
+        assert torch.equal(W, We), f"replay {rep}: W"
+        Ue = S.clone()
+        ve = torch.zeros_like(v)
+        lg.rowadam_scale(Ue, ve, 1, 0.95, 1e-8)
+        assert torch.equal(U, Ue) and torch.equal(v, ve), f"replay {rep}: RowAdam"
+        Wge = W0.clone()
+        lg.merge_update(Wge, Ue, seed + 1, r, scale)
+        assert torch.equal(Wg, Wge), f"replay {rep}: grouped W"
+        qe = torch.empty_like(q)
+        rve = torch.empty_like(rv)
+        lg.predicted_kl(z, zd, 0.9, row_var=rve, q=qe)
+        assert torch.equal(q, qe) and torch.equal(rv, rve), f"replay {rep}: predicted KL"
+        torch.cuda.synchronize()
+
+    # the last replay against the oracle
+    A = oracle.rademacher_projection(seed, r, k)
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X), f64(X)], [f64(dY), f64(dY)], A)
+    assert_sketch_close(f64(S), ref)
+    assert float(q.item()) == pytest.approx(oracle.predicted_kl(f64(z), f64(zd), 0.9), rel=1e-4)
