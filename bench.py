@@ -13,6 +13,7 @@ Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
                stream around M*K back-to-back calls over the rotating inputs,
                queued behind a sleep kernel so that they measure GPU time;
   merge        the fused merge against the same peak;
+  rowadam      the optional RowAdam scaling of S (three small kernels);
   split        the forward/backward halves of a sketch call (project, contract);
   grouped_merge a 1.5B-class layer's seven merges in one launch vs seven;
   predicted_kl the predicted-KL reduction over a 2048 x 151,936 probe;
@@ -107,6 +108,25 @@ def proj_cols(r):
     while q < nb:
         q *= 2
     return 16 * q
+
+
+def rowadam_bytes(d, r):
+    """Algorithmic HBM bytes of RowAdam: S read twice and written once (fp32),
+    v read and written once."""
+    return 12 * d * r + 8 * d
+
+
+def rowadam_time(torch, lg, stream, S, calls: int):
+    """GPU time per RowAdam call over copies of S (each call rescales its copy
+    in place; the values stay finite because the rescale keeps the norm)."""
+    d, r = S.shape
+    n = max(2, math.ceil(2.5 * MALL_BYTES / (4 * d * r)))
+    Us = [S.clone() for _ in range(n)]
+    vs = [torch.zeros(d, dtype=torch.float32, device=S.device) for _ in range(n)]
+    t, h = gpu_time_per_call(torch, stream, lambda i: lg.rowadam_scale(Us[i % n], vs[i % n], 1 + i // n, 0.999, 1e-8),
+                             max(calls, 2 * n))
+    del Us, vs
+    return t, h
 
 
 def split_bytes(T, k, d, r):
@@ -266,6 +286,7 @@ def sweep(steps: int):
                 nm = max(steps, 2 * n_w)
                 t_merge, _ = gpu_time_per_call(
                     torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]), nm)
+                t_ra, _ = rowadam_time(torch, lg, stream, S, steps)
                 del Ws, S
                 torch.cuda.empty_cache()
                 sb, mb = sketch_bytes(T, k, d, r), merge_bytes(d, k, r)
@@ -275,6 +296,7 @@ def sweep(steps: int):
                     "sketch_GBps": sb / t_call / 1e9, "sketch_frac": sb / t_call / 1e9 / HBM_PEAK_GBS,
                     "merge_us": t_merge * 1e6, "merge_GBps": mb / t_merge / 1e9,
                     "merge_frac": mb / t_merge / 1e9 / HBM_PEAK_GBS,
+                    "rowadam_us": t_ra * 1e6, "rowadam_GBps": rowadam_bytes(d, r) / t_ra / 1e9,
                     "kernel_source_sha": kernel_source_sha(),
                 }), flush=True)
 
@@ -428,6 +450,7 @@ def main():
                                               r, S), n_calls)
     del caches
     pb, cb = split_bytes(T, k, d, r)
+    t_ra, h_ra = rowadam_time(torch, lg, stream, S, args.steps)
     grouped = grouped_merge_timing(torch, lg, wl, stream, dev, max(10, args.steps))
     kl = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps)) if not args.no_kl else None
     sb = sketch_bytes(T, k, d, r)
@@ -494,6 +517,14 @@ def main():
             "sketch_frac_of_two_reads": t_read2 / t_call,
             "merge_w_rmw_us": t_rmw * 1e6,
             "merge_frac_of_rmw": t_rmw / t_merge,
+        },
+        "rowadam": {
+            "kernel": "rowadam_rows_kernel + rowadam_norm_kernel + rowadam_apply_kernel",
+            "avg_us": t_ra * 1e6,
+            "achieved": rowadam_bytes(d, r) / t_ra / 1e9,
+            "frac": rowadam_bytes(d, r) / t_ra / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": rowadam_bytes(d, r),
+            "host_us_per_call": h_ra * 1e6,
         },
         "split": {
             "what": "logra_project (forward, X -> cache) and logra_contract (backward, dY and cache -> S), per call",

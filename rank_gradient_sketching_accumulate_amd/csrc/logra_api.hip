@@ -445,8 +445,8 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
     const size_t off_root = 0;
     const size_t off_ssq = up((size_t)d * 4);
     const size_t off_part = off_ssq + up((size_t)d * 4);
-    const size_t off_scal = off_part + up((size_t)2 * kRowAdamBlocks * 8);
-    const size_t total = off_scal + 256;
+    const size_t off_part2 = off_part + up((size_t)2 * kRowAdamBlocks * 8);
+    const size_t total = off_part2 + up((size_t)kRowAdamBlocks * 8);
     void* ws = nullptr;
     logra_status st = arena_get(kArenaRowAdam, stream, total, &ws);
     if (st != LOGRA_OK) return st;
@@ -454,7 +454,7 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
     const double inv_bias = 1.0 / (1.0 - pow((double)beta2, (double)step));
     rowadam_launch(S, lds, v, d, r, beta2, inv_bias, eps_rel, reinterpret_cast<float*>(base + off_root),
                    reinterpret_cast<float*>(base + off_ssq), reinterpret_cast<double*>(base + off_part),
-                   reinterpret_cast<double*>(base + off_scal), stream);
+                   reinterpret_cast<double*>(base + off_part2), stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "rowadam launch");
     return LOGRA_OK;

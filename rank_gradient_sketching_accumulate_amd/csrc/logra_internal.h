@@ -146,9 +146,11 @@ void kl_launch(const KLPlan& pl, const KLParams& p, int bf16, float* row_var, fl
 // ---------------------------------------------------------------------------
 // RowAdam and the sign dump.
 // ---------------------------------------------------------------------------
-constexpr int kRowAdamBlocks = 256;
+// RowAdam: at most kRowAdamBlocks blocks per kernel; partial holds
+// 2 * kRowAdamBlocks doubles, partial2 kRowAdamBlocks.
+constexpr int kRowAdamBlocks = 512;
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias,
-                    float eps_rel, float* root, float* ssq, double* partial, double* scal, hipStream_t s);
+                    float eps_rel, float* root, float* ssq, double* partial, double* partial2, hipStream_t s);
 void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s);
 void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_t s);
 // dst[0 .. 16*n16) = 0 (dst 16-byte aligned).

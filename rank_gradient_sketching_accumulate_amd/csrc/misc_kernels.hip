@@ -12,43 +12,20 @@
 
 namespace logra {
 
-// One wave per row: m_i, the v_i update and sqrt(vh_i); per-workgroup fp64
-// sums of sqrt(vh) and of ||S_i||^2 into partial[2*block .. 2*block+1].
-__global__ __launch_bounds__(256) void rowadam_rows_kernel(const float* S, int64_t lds, float* v, int64_t d,
-                                                          int r, float beta2, double inv_bias, float* root,
-                                                          float* ssq, double* partial) {
-  __shared__ double sh[2][4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double sum_root = 0.0, sum_ssq = 0.0;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < d; row += (int64_t)gridDim.x * 4) {
-    float q = 0.f;
-    for (int j = lane; j < r; j += 64) {
-      const float x = S[row * lds + j];
-      q = __fmaf_rn(x, x, q);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off, 64);
-    if (lane == 0) {
-      const float m = q / (float)r;
-      const float vn = beta2 * v[row] + (1.f - beta2) * m;
-      const float rt = (float)sqrt((double)vn * inv_bias);
-      v[row] = vn;
-      root[row] = rt;
-      ssq[row] = q;
-      sum_root += (double)rt;
-      sum_ssq += (double)q;
-    }
-  }
-  if (lane == 0) {
-    sh[0][wave] = sum_root;
-    sh[1][wave] = sum_ssq;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    partial[2 * blockIdx.x] = sh[0][0] + sh[0][1] + sh[0][2] + sh[0][3];
-    partial[2 * blockIdx.x + 1] = sh[1][0] + sh[1][1] + sh[1][2] + sh[1][3];
-  }
-}
+// Rows go to groups of L lanes (L = the smallest power of two >= r/4, at
+// most 64), so a wave covers 64/L rows at a time; with 16-byte aligned rows
+// and r % 4 == 0 each lane moves float4s.  Three grid-wide kernels: (1) per
+// row m_i, the v_i update, sqrt(vh_i) and ||S_i||^2, plus per-block float64
+// sums of sqrt(vh) and ||S_i||^2; (2) every block re-sums those partials in a
+// fixed order (so every block holds the same eps), then adds
+// ||S_i||^2 / (sqrt(vh_i) + eps)^2 over its rows into a second set of
+// partials; (3) every block re-sums both sets the same way, forms
+// f = ||S|| / ||Ut|| and rescales its rows by f / (sqrt(vh_i) + eps).  All
+// sums are in a fixed order: the result is deterministic.
+struct RowGroup {
+  int L, lane_in_row;
+  int64_t row_in_wave;
+};
 
 __device__ __forceinline__ double block_sum_256(double x, double* sh) {
   sh[threadIdx.x] = x;
@@ -62,51 +39,131 @@ __device__ __forceinline__ double block_sum_256(double x, double* sh) {
   return out;
 }
 
-// One workgroup, fixed summation order (deterministic): scal[0] = eps,
-// scal[1] = ||S|| / ||Ut||.
-__global__ __launch_bounds__(256) void rowadam_finalize_kernel(const double* partial, int nparts, const float* root,
-                                                              const float* ssq, int64_t d, float eps_rel,
-                                                              double* scal) {
+// Fixed-order sum of n values spaced `stride` apart (every block that calls
+// it with the same arguments gets the same bits).
+__device__ __forceinline__ double sum_partials(const double* p, int n, int stride, double* sh) {
+  double a = 0.0;
+  for (int j = threadIdx.x; j < n; j += 256) a += p[(int64_t)j * stride];
+  return block_sum_256(a, sh);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void rowadam_rows_kernel(const float* S, int64_t lds, float* v, int64_t d, int r,
+                                                          int L, float beta2, double inv_bias, float* root,
+                                                          float* ssq, double* partial) {
   __shared__ double sh[256];
-  double a = 0.0, b = 0.0;
-  for (int j = threadIdx.x; j < nparts; j += 256) {
-    a += partial[2 * j];
-    b += partial[2 * j + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & (L - 1);
+  const int rpw = 64 / L;                      // rows per wave and pass
+  const int64_t rpb = 4 * (int64_t)rpw;        // rows per block and pass
+  double sum_root = 0.0, sum_ssq = 0.0;
+  for (int64_t base = (int64_t)blockIdx.x * rpb; base < d; base += (int64_t)gridDim.x * rpb) {
+    const int64_t row = base + wave * rpw + lane / L;
+    float q = 0.f;
+    if (row < d) {
+      const float* src = S + row * lds;
+      if constexpr (VEC) {
+        for (int j = 4 * sub; j < r; j += 4 * L) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + j);
+          q = __fmaf_rn(x[0], x[0], q);
+          q = __fmaf_rn(x[1], x[1], q);
+          q = __fmaf_rn(x[2], x[2], q);
+          q = __fmaf_rn(x[3], x[3], q);
+        }
+      } else {
+        for (int j = sub; j < r; j += L) q = __fmaf_rn(src[j], src[j], q);
+      }
+    }
+    for (int off = L >> 1; off > 0; off >>= 1) q += __shfl_xor(q, off, 64);
+    if (sub == 0 && row < d) {
+      const float m = q / (float)r;
+      const float vn = beta2 * v[row] + (1.f - beta2) * m;
+      const float rt = (float)sqrt((double)vn * inv_bias);
+      v[row] = vn;
+      root[row] = rt;
+      ssq[row] = q;
+      sum_root += (double)rt;
+      sum_ssq += (double)q;
+    }
   }
-  const double sum_root = block_sum_256(a, sh);
-  const double norm_s2 = block_sum_256(b, sh);
-  const double eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
-  double c = 0.0;
-  for (int64_t row = threadIdx.x; row < d; row += 256) {
-    const double den = (double)root[row] + eps;
-    c += (double)ssq[row] / (den * den);
-  }
-  const double norm_u2 = block_sum_256(c, sh);
+  const double a = block_sum_256(sum_root, sh);
+  const double b = block_sum_256(sum_ssq, sh);
   if (threadIdx.x == 0) {
-    scal[0] = eps;
-    scal[1] = norm_u2 > 0.0 ? sqrt(norm_s2 / norm_u2) : 0.0;
+    partial[2 * blockIdx.x] = a;
+    partial[2 * blockIdx.x + 1] = b;
   }
 }
 
-__global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t lds, int64_t d, int r,
-                                                           const float* root, const double* scal) {
-  const double eps = scal[0], fac = scal[1];
-  for (int64_t row = blockIdx.x; row < d; row += gridDim.x) {
+__global__ __launch_bounds__(256) void rowadam_norm_kernel(const double* partial, int nparts, const float* root,
+                                                          const float* ssq, int64_t d, float eps_rel,
+                                                          double* partial2) {
+  __shared__ double sh[256];
+  const double sum_root = sum_partials(partial, nparts, 2, sh);
+  const double eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
+  double c = 0.0;
+  for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < d; row += (int64_t)gridDim.x * 256) {
+    const double den = (double)root[row] + eps;
+    c += (double)ssq[row] / (den * den);
+  }
+  const double t = block_sum_256(c, sh);
+  if (threadIdx.x == 0) partial2[blockIdx.x] = t;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t lds, int64_t d, int r, int L,
+                                                           const float* root, const double* partial, int nparts,
+                                                           const double* partial2, int nparts2, float eps_rel) {
+  __shared__ double sh[256];
+  const double sum_root = sum_partials(partial, nparts, 2, sh);
+  const double norm_s2 = sum_partials(partial + 1, nparts, 2, sh);
+  const double norm_u2 = sum_partials(partial2, nparts2, 1, sh);
+  const double eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
+  const double fac = norm_u2 > 0.0 ? sqrt(norm_s2 / norm_u2) : 0.0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane & (L - 1);
+  const int rpw = 64 / L;
+  const int64_t rpb = 4 * (int64_t)rpw;
+  for (int64_t base = (int64_t)blockIdx.x * rpb; base < d; base += (int64_t)gridDim.x * rpb) {
+    const int64_t row = base + wave * rpw + lane / L;
+    if (row >= d) continue;
     const float f = (float)(fac / ((double)root[row] + eps));
-    for (int j = threadIdx.x; j < r; j += 256) S[row * lds + j] *= f;
+    float* dst = S + row * lds;
+    if constexpr (VEC) {
+      for (int j = 4 * sub; j < r; j += 4 * L) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(dst + j);
+        x[0] *= f; x[1] *= f; x[2] *= f; x[3] *= f;
+        *reinterpret_cast<f32x4*>(dst + j) = x;
+      }
+    } else {
+      for (int j = sub; j < r; j += L) dst[j] *= f;
+    }
   }
 }
 
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias, float eps_rel,
-                    float* root, float* ssq, double* partial, double* scal, hipStream_t s) {
-  int blocks = (int)((d + 3) / 4);
+                    float* root, float* ssq, double* partial, double* partial2, hipStream_t s) {
+  const bool vec = (((uintptr_t)S & 15) == 0) && (lds % 4 == 0) && (r % 4 == 0);
+  int L = 1;
+  while (L < 64 && 4 * L < r) L <<= 1;  // float4 lanes per row (the scalar path uses the same grouping)
+  const int64_t rpb = 4 * (int64_t)(64 / L);
+  int64_t blocks = (d + rpb - 1) / rpb;
   if (blocks > kRowAdamBlocks) blocks = kRowAdamBlocks;
-  hipLaunchKernelGGL(rowadam_rows_kernel, dim3(blocks), dim3(256), 0, s, S, lds, v, d, r, beta2, inv_bias, root,
-                     ssq, partial);
-  hipLaunchKernelGGL(rowadam_finalize_kernel, dim3(1), dim3(256), 0, s, partial, blocks, root, ssq, d, eps_rel,
-                     scal);
-  const int ablocks = (int)(d < 4096 ? d : 4096);
-  hipLaunchKernelGGL(rowadam_apply_kernel, dim3(ablocks), dim3(256), 0, s, S, lds, d, r, root, scal);
+  int64_t nblocks = (d + 255) / 256;
+  if (nblocks > kRowAdamBlocks) nblocks = kRowAdamBlocks;
+  if (vec)
+    hipLaunchKernelGGL(rowadam_rows_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, v, d, r, L, beta2,
+                       inv_bias, root, ssq, partial);
+  else
+    hipLaunchKernelGGL(rowadam_rows_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, v, d, r, L, beta2,
+                       inv_bias, root, ssq, partial);
+  hipLaunchKernelGGL(rowadam_norm_kernel, dim3((unsigned)nblocks), dim3(256), 0, s, partial, (int)blocks, root, ssq, d,
+                     eps_rel, partial2);
+  if (vec)
+    hipLaunchKernelGGL(rowadam_apply_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L, root,
+                       partial, (int)blocks, partial2, (int)nblocks, eps_rel);
+  else
+    hipLaunchKernelGGL(rowadam_apply_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L, root,
+                       partial, (int)blocks, partial2, (int)nblocks, eps_rel);
 }
 
 // Signs s (r x k) as int8 +-1; one thread per (row, 256-column block).

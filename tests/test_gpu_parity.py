@@ -436,7 +436,7 @@ def test_merge_full_size_sampled_rows(key, layer):
 # RowAdam
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("beta2", [0.95, 0.999])
-@pytest.mark.parametrize("d,r", [(256, 16), (3584, 64), (1000, 100), (7, 256)])
+@pytest.mark.parametrize("d,r", [(256, 16), (3584, 64), (1000, 100), (7, 256), (18944, 256), (500, 30), (65, 1)])
 def test_rowadam_three_steps(beta2, d, r):
     _say("rowadam", d, r, beta2)
     v = torch.zeros(d, dtype=torch.float32, device=DEV)
@@ -453,6 +453,23 @@ def test_rowadam_three_steps(beta2, d, r):
         assert rel_frob(f64(v), v_ref) < 1e-5
         # Frobenius norm of the sketch is preserved
         assert math.isclose(float(np.linalg.norm(f64(S))), float(np.linalg.norm(S_in)), rel_tol=1e-5)
+
+
+@pytest.mark.parametrize("d,r,ld", [(700, 64, 67), (300, 128, 132), (41, 256, 260)])
+def test_rowadam_strided_rows(d, r, ld):
+    """Rows with a padded stride (the scalar path when a row is not 16-byte
+    aligned, the float4 path when it is); the padding is left untouched."""
+    _say("rowadam strided", d, r, ld)
+    base = wl.random_tensor((d, ld), 900 + d, device=DEV)
+    S = base[:, :r]
+    pad = base[:, r:].clone()
+    S_in = f64(S)
+    v = torch.zeros(d, dtype=torch.float32, device=DEV)
+    lg.rowadam_scale(S, v, 1, 0.95, 1e-8)
+    U_ref, v_ref = oracle.rowadam_scale(S_in, np.zeros(d), 1, float(np.float32(0.95)), float(np.float32(1e-8)))
+    assert_sketch_close(f64(S), U_ref, what="U")
+    assert rel_frob(f64(v), v_ref) < 1e-5
+    assert torch.equal(base[:, r:], pad)
 
 
 def test_rowadam_zero_sketch_gives_zero_update():
