@@ -94,6 +94,19 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
                                      hipStream_t stream);
 
 /*
+ * Bitwise-reproducible sketches (off by default; a setting of the calling
+ * thread).  Atomic adds from several workgroups into the same S entries
+ * make S depend on their order at the level of fp32 rounding; any such
+ * order is within the stated error bound.  When enabled, logra_sketch_
+ * accumulate and logra_contract give every row tile of S to one workgroup,
+ * which sums all the tokens in one fixed order and stores without atomic
+ * adds, so repeated calls on the same inputs give the same bits.  This is a
+ * testing and debugging mode: with few row tiles it runs on few compute
+ * units.  Returns the previous setting.
+ */
+int logra_set_deterministic(int enable);
+
+/*
  * Split sketch accumulation: project at forward time, contract at backward
  * time.  The paper counts cached projections among the memory the method
  * keeps (section 2.2, "Memory and synchronization") and projects the inputs

@@ -25,6 +25,7 @@ __all__ = [
     "load_library",
     "library_loaded",
     "sketch_accumulate",
+    "set_deterministic",
     "projection_bytes",
     "project",
     "contract",
@@ -48,6 +49,7 @@ MAX_RANK = 256
 # Every symbol include/logra.h declares.
 EXPORTED_SYMBOLS = (
     "logra_sketch_accumulate",
+    "logra_set_deterministic",
     "logra_projection_bytes",
     "logra_project",
     "logra_contract",
@@ -93,6 +95,8 @@ def _declare(lib):
     c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
     lib.logra_sketch_accumulate.restype = ctypes.c_int
+    lib.logra_set_deterministic.argtypes = [ctypes.c_int]
+    lib.logra_set_deterministic.restype = ctypes.c_int
     lib.logra_projection_bytes.argtypes = [c_i64, c_i32]
     lib.logra_projection_bytes.restype = ctypes.c_size_t
     lib.logra_project.argtypes = [c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, ctypes.c_size_t, c_vp]
@@ -219,6 +223,12 @@ def sketch_accumulate(X, dY, seed: int, r: int, S):
         )
     )
     return S
+
+
+def set_deterministic(enable: bool) -> bool:
+    """Bitwise-reproducible sketches on the calling thread (one workgroup per
+    row tile of S, no atomic adds; slower).  Returns the previous setting."""
+    return bool(load_library().logra_set_deterministic(1 if enable else 0))
 
 
 def projection_bytes(T: int, r: int) -> int:

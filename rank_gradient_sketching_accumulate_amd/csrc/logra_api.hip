@@ -94,14 +94,18 @@ bool plan_overrides_present() {
   return false;
 }
 
+// Per-thread switch of logra_set_deterministic.
+thread_local bool g_deterministic = false;
+
 SketchPlan sketch_plan_for(int64_t T, int64_t k, int64_t d, int r) {
-  if (plan_overrides_present()) return plan_sketch(T, k, d, r);
-  thread_local std::map<std::tuple<int64_t, int64_t, int64_t, int>, SketchPlan> plans;
-  const auto key = std::make_tuple(T, k, d, r);
+  const bool det = g_deterministic;
+  if (plan_overrides_present()) return plan_sketch(T, k, d, r, det);
+  thread_local std::map<std::tuple<int64_t, int64_t, int64_t, int, bool>, SketchPlan> plans;
+  const auto key = std::make_tuple(T, k, d, r, det);
   auto it = plans.find(key);
   if (it != plans.end()) return it->second;
   if (plans.size() >= 1024) plans.clear();
-  const SketchPlan pl = plan_sketch(T, k, d, r);
+  const SketchPlan pl = plan_sketch(T, k, d, r, det);
   plans.emplace(key, pl);
   return pl;
 }
@@ -270,6 +274,12 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+int logra_set_deterministic(int enable) {
+  const int prev = g_deterministic ? 1 : 0;
+  g_deterministic = enable != 0;
+  return prev;
 }
 
 size_t logra_projection_bytes(int64_t T, int32_t r) {

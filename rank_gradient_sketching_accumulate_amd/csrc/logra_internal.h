@@ -64,7 +64,9 @@ struct SketchPlan {
   size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };
 
-SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r);
+// det: bitwise-reproducible contraction (one workgroup per row tile of S,
+// fixed summation order, no atomic adds).
+SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det = false);
 // Caller-held projection cache of the split project / contract calls: a high
 // plane then a low plane, each cache_tokens(T) x 16*NB bf16 entries in Pk
 // order.  Every projection tiling's padded token count fits in it (token

@@ -1017,7 +1017,7 @@ int env_int(const char* name, int dflt) {
   return (s && *s) ? atoi(s) : dflt;
 }
 
-SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
+SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
   SketchPlan pl{};
   pl.NB = pow2_blocks(r);
   const int RP = 16 * pl.NB;
@@ -1093,7 +1093,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     // atomic adds into S per step.  They pay off only for tall S (18944 x
     // 3584 at r = 64: 99.6 -> 93.1 us per 8192-token call; 1536- and
     // 3584-row layers ran 0-35 % slower).
-    const int tile4 = pl.NB == 4 ? env_int("LOGRA_CON_TILE", d >= 8192 ? 1 : 0) : 0;
+    const int tile4 = (pl.NB == 4 && !det) ? env_int("LOGRA_CON_TILE", d >= 8192 ? 1 : 0) : 0;
     if (tile4) {
       int wm = env_int("LOGRA_CON_WM", 2);
       if (wm != 1 && wm != 2 && wm != 4) wm = 2;
@@ -1116,13 +1116,13 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
     // times and, with at least 36 row tiles, need only a few token splits.
     const bool tall = (d + bd8 - 1) / bd8 >= 36;
     pl.few_ts = tall ? 1 : 0;
-    const int tile = env_int("LOGRA_CON_TILE", tall ? 0 : ((pl.NB == 8 || T <= 8192) ? 1 : 0));
+    const int tile = det ? 1 : env_int("LOGRA_CON_TILE", tall ? 0 : ((pl.NB == 8 || T <= 8192) ? 1 : 0));
     const int big = env_int("LOGRA_CON_BIG", tall ? 1 : -1);
     const bool use_big = big >= 0 ? big != 0 : ((d + bd8 - 1) / bd8) * (nks / 16) >= 256;
     if (tile) {
       // NB = 8: 2 column groups; NB = 16: 4 column groups; WM row groups.
       const int wn = pl.NB / 4;
-      int wm = env_int("LOGRA_CON_WM", 1);
+      int wm = det ? 1 : env_int("LOGRA_CON_WM", 1);
       if (wm < 1 || wm * wn > 8) wm = 1;
       pl.WM = wm;
       pl.cvar = 5;
@@ -1186,6 +1186,14 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
       pl.cbands = 1;
     }
     pl.cgrid = (int)grid;
+    if (det) {
+      // One workgroup per row tile over all the tokens: every S element is
+      // summed in one fixed order and stored without atomic adds.
+      pl.cbands = 1;
+      pl.cgrid = pl.n_dt;
+      pl.n_ts = 1;
+      pl.ksp = nks;
+    }
   }
 
   size_t off = 0;
@@ -1200,7 +1208,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r) {
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
-  pl.use_part = env_int("LOGRA_CON_PART", pl.n_ts >= 3 ? 1 : 0) && pl.n_ts > 1 && (pl.cvar == 3 || pl.cvar == 4);
+  pl.use_part = !det && env_int("LOGRA_CON_PART", pl.n_ts >= 3 ? 1 : 0) && pl.n_ts > 1 && (pl.cvar == 3 || pl.cvar == 4);
   pl.bigdp = env_int("LOGRA_CON_BIGDP", 2) == 1 ? 1 : 2;
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);

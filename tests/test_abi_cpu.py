@@ -89,6 +89,13 @@ def test_sketch_validation(lib):
     assert _sketch(lib, d=0) == OK
 
 
+def test_set_deterministic_is_per_call_setting(lib):
+    assert lib.logra_set_deterministic(1) == 0
+    assert lib.logra_set_deterministic(7) == 1
+    assert lib.logra_set_deterministic(0) == 1
+    assert lib.logra_set_deterministic(0) == 0
+
+
 def test_projection_bytes(lib):
     assert lib.logra_projection_bytes(0, 16) == 0
     assert lib.logra_projection_bytes(16, 0) == 0

@@ -262,6 +262,36 @@ def test_sketch_launch_plans(r, env, monkeypatch):
     assert_sketch_close(f64(S), ref)
 
 
+@pytest.mark.parametrize("T,k,d,r", [(700, 1300, 300, 16), (4096, 1536, 1536, 64), (1000, 700, 900, 128),
+                                     (2048, 3584, 3584, 256), (33, 264, 17, 5)])
+def test_sketch_deterministic_mode(T, k, d, r):
+    """With the deterministic setting, two accumulations of the same inputs
+    give the same bits, through the fused and the split calls alike, and
+    match the oracle."""
+    _say("deterministic", T, k, d, r)
+    X, dY = _ragged_inputs(T, k, d, 777 + r)
+    prev = lg.set_deterministic(True)
+    try:
+        S1 = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+        S2 = torch.zeros_like(S1)
+        lg.sketch_accumulate(X, dY, 3, r, S1)
+        lg.sketch_accumulate(X, dY, 3, r, S1)
+        lg.sketch_accumulate(X, dY, 3, r, S2)
+        lg.sketch_accumulate(X, dY, 3, r, S2)
+        P = lg.project(X, 3, r)
+        S3 = torch.zeros_like(S1)
+        lg.contract(dY, P, r, S3)
+        lg.contract(dY, P, r, S3)
+        torch.cuda.synchronize()
+    finally:
+        lg.set_deterministic(prev)
+    assert torch.equal(S1, S2)
+    assert torch.equal(S1, S3)
+    rows = None if d <= 1000 else np.arange(0, d, 29)
+    ref = _oracle_sketch(torch.zeros((d, r)), [X, X], [dY, dY], 3, r, k, rows=rows)
+    assert_sketch_close(f64(S1) if rows is None else f64(S1)[rows], ref)
+
+
 def test_sketch_additivity_and_empty():
     """M calls equal one call on the concatenated tokens (Algorithm 1 sums
     microbatch contributions); empty calls leave S bitwise unchanged."""
