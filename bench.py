@@ -321,7 +321,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(
-            "bench.py measures one GPU: this build has no multi-GPU path "
+            "bench.py measures one GPU: the library has no multi-GPU path "
             "(the sketch is additive over tokens; sharding is described in the design notes).",
             file=sys.stderr,
         )
