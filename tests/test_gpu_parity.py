@@ -466,7 +466,8 @@ def test_merge_full_size_sampled_rows(key, layer):
 # RowAdam
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("beta2", [0.95, 0.999])
-@pytest.mark.parametrize("d,r", [(256, 16), (3584, 64), (1000, 100), (7, 256), (18944, 256), (500, 30), (65, 1)])
+@pytest.mark.parametrize("d,r", [(256, 16), (3584, 64), (1000, 100), (7, 256), (18944, 256), (500, 30), (65, 1),
+                                 (2048, 64), (2049, 48)])
 def test_rowadam_three_steps(beta2, d, r):
     _say("rowadam", d, r, beta2)
     v = torch.zeros(d, dtype=torch.float32, device=DEV)
