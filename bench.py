@@ -206,6 +206,27 @@ def grouped_merge_timing(torch, lg, wl, stream, dev, calls: int, r: int = 128, s
     }
 
 
+def gpu_time_reps(torch, stream, fn, n, reps):
+    """Per-call GPU seconds of `reps` separate repetitions of n back-to-back
+    calls fn(i) (each repetition queued behind its own sleep kernel, timed
+    with HIP events on `stream`): returns the sorted list."""
+    out = []
+    for rep in range(reps):
+        t, _ = gpu_time_per_call(torch, stream, lambda i: fn(rep * n + i), n)
+        out.append(t)
+    return sorted(out)
+
+
+def quantiles_us(ts):
+    """p10, median and p90 of a sorted list of seconds, in microseconds."""
+    def q(f):
+        x = f * (len(ts) - 1)
+        lo = int(math.floor(x))
+        hi = min(lo + 1, len(ts) - 1)
+        return (ts[lo] + (ts[hi] - ts[lo]) * (x - lo)) * 1e6
+    return {"p10_us": q(0.1), "median_us": q(0.5), "p90_us": q(0.9), "repetitions": len(ts)}
+
+
 def cpu_baseline(w, layer, r, seed, budget_s: float):
     """Time the float64 oracle (as it stands) on host copies of the
     workload's microbatches: dense G = dY^T X, then the projection."""
@@ -413,12 +434,16 @@ def main():
         lg.sketch_accumulate(X, dY, seed, r, S)
 
     t_call, h_call = gpu_time(sketch_call, n_calls)
+    # The layer's M calls of one step, repeated (median, p10, p90 per call).
+    sk_reps = quantiles_us(gpu_time_reps(torch, stream, sketch_call, M, 20))
     # Merge: over enough copies of W to exceed the MALL (in a step, W was
     # last touched a whole step earlier).
     n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
     Ws = [W.clone() for _ in range(n_w)]
     n_merges = max(args.steps, 2 * n_w)
     t_merge, h_merge = gpu_time(lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale), n_merges)
+    mg_reps = quantiles_us(gpu_time_reps(torch, stream, lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale),
+                                         4, 20))
 
     # Streaming ceilings measured on this machine for the same bytes, timed the
     # same way: the sketch call's two input streams read as two launches (X,
@@ -495,6 +520,7 @@ def main():
             "avg_call_us": t_call * 1e6,
             "calls_timed": n_calls,
             "host_us_per_call": h_call * 1e6,
+            "per_call_over_repetitions": {"what": f"{M} calls (one step's microbatches) per repetition", **sk_reps},
         },
         "merge": {
             "kernel": "merge_kernel",
@@ -508,6 +534,7 @@ def main():
             "merges_timed": n_merges,
             "host_us_per_call": h_merge * 1e6,
             "weight_copies_rotated": n_w,
+            "per_call_over_repetitions": {"what": "4 merges per repetition", **mg_reps},
         },
         "ceiling": {
             "what": "streaming reads/writes of the same bytes on this box (logra_stream_read; torch in-place mul for W)",
