@@ -42,7 +42,7 @@ struct ContractParams {
   int atomic_out;  // 1 when several workgroups add into the same S tile
   float* part;      // non-null: token split ts stores its tile at part + ts*part_split instead
   int64_t part_split;  // floats per split (d x 16*NB, row stride 16*NB)
-  int bands;        // stream-K kernels: token bands, 1 or 8 (one per XCD; grid a multiple of 8)
+  int bands;        // stream-K kernels: token bands, 1, 4 or 8 (grid a multiple of bands)
 };
 
 struct SketchPlan {
@@ -59,7 +59,7 @@ struct SketchPlan {
   int64_t ksp;
   int use_part;           // token-split tiles stored as partials, then summed by sketch_reduce
   int cgrid;              // contract_small / contract_tile: workgroups sharing the step units
-  int cbands;             // token bands of that split (1, or 8 = one per XCD)
+  int cbands;             // token bands of that split (1; 4 = one per XCD pair; 8 = one per XCD)
   int bigdp;              // contract_big: steps between requesting a step's operands and using them
   size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
 };

@@ -480,10 +480,12 @@ __device__ __forceinline__ void put_s(const ContractParams& p, int ts, int64_t r
 struct StreamK {
   int64_t kb0, blen, u_beg, u_end;
   __device__ __forceinline__ StreamK(const ContractParams& p, int64_t nks) {
+    // Workgroup ids are dealt to the eight XCDs round-robin: with B = 8 each
+    // XCD takes one band, with B = 4 the XCDs b and b + 4 share band b.
     const int B = p.bands;
-    const int band = B == 8 ? (int)(blockIdx.x & 7) : 0;
-    const int64_t gx = B == 8 ? gridDim.x >> 3 : gridDim.x;  // workgroups sharing the band
-    const int64_t jx = B == 8 ? blockIdx.x >> 3 : blockIdx.x;
+    const int band = (int)(blockIdx.x % B);
+    const int64_t gx = gridDim.x / B;  // workgroups sharing the band
+    const int64_t jx = blockIdx.x / B;
     kb0 = nks * band / B;
     blen = nks * (band + 1) / B - kb0;
     const int64_t units = (int64_t)p.n_dt * blen;
@@ -1176,11 +1178,18 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
     // over 256 workgroups (runs that straddle tiles cost one more set of
     // atomic adds each, and many tiles per band would cut every run up).
     const int64_t units = (int64_t)pl.n_dt * nks;
-    pl.cbands = env_int("LOGRA_CON_BANDS", (nks >= 128 && pl.n_dt * 8 <= 256) ? 8 : 1) == 8 ? 8 : 1;
-    int64_t grid = pl.cbands == 8 ? 8 * (int64_t)pl.n_dt : 256;
+    // Four bands (one per pair of XCDs) when eight do not fit one round but
+    // four do, at r <= 128: 3584-row layers at r = 64 and 128 took 4-7 %
+    // less than with one band over 256 workgroups; at r = 256 no gain.
+    int bands = 1;
+    if (nks >= 128 && pl.n_dt * 8 <= 256) bands = 8;
+    else if (nks >= 128 && pl.n_dt * 4 <= 256 && pl.NB <= 8) bands = 4;
+    pl.cbands = env_int("LOGRA_CON_BANDS", bands);
+    if (pl.cbands != 4 && pl.cbands != 8) pl.cbands = 1;
+    int64_t grid = pl.cbands > 1 ? (int64_t)pl.cbands * pl.n_dt : 256;
     grid = env_int("LOGRA_CON_GRID", (int)grid);
     if (grid > units / 8) grid = units / 8;
-    if (pl.cbands == 8) grid = grid / 8 * 8;
+    if (pl.cbands > 1) grid = grid / pl.cbands * pl.cbands;
     if (grid < 1) {
       grid = 1;
       pl.cbands = 1;

@@ -210,6 +210,9 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2},
     {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 4},
     {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2, "LOGRA_CON_BANDS": 1, "LOGRA_CON_GRID": 37},
+    {"LOGRA_CON_BANDS": 4},
+    {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 24},
+    {"LOGRA_CON_BANDS": 4, "LOGRA_CON_GRID": 12},
 ]
 
 
