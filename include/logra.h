@@ -107,6 +107,27 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
 int logra_set_deterministic(int enable);
 
 /*
+ * Precision of the contraction (a setting of the calling thread; returns the
+ * previous mode).  The projected inputs P are fp32 sums; the contraction
+ * multiplies them on bf16 matrix cores.
+ *
+ *   LOGRA_PRECISION_BF16X2 (default): P is carried as a bf16 high part plus
+ *     a bf16 low part of the remainder (about 16 significant bits) and each
+ *     product takes two MFMAs; S matches an fp64 evaluation to about 1e-5
+ *     relative (Frobenius).
+ *   LOGRA_PRECISION_BF16: P is rounded once to bf16 (round to nearest even)
+ *     and each product takes one MFMA; half the matrix-core work and half the
+ *     P traffic.  S then carries the error of that one rounding, about
+ *     1.6e-3 relative (Frobenius) on iid data.
+ *
+ * Applies to logra_sketch_accumulate and logra_contract; logra_project
+ * always writes both planes, so a projection cache serves either mode.
+ */
+#define LOGRA_PRECISION_BF16X2 0
+#define LOGRA_PRECISION_BF16 1
+int logra_set_precision(int mode);
+
+/*
  * Split sketch accumulation: project at forward time, contract at backward
  * time.  The paper counts cached projections among the memory the method
  * keeps (section 2.2, "Memory and synchronization") and projects the inputs

@@ -31,6 +31,7 @@ from .logra_oracle import (  # noqa: F401
     merge_update,
     rowadam_scale,
     reconstruction_cosine,
+    sketch_accumulate_rounded_projection,
 )
 from .predicted_kl import (  # noqa: F401
     token_probabilities,

@@ -265,3 +265,26 @@ def reconstruction_cosine(G, A) -> float:
     G = np.asarray(G, dtype=np.float64)
     Gh = low_rank_expand(sketch_from_gradient(G, A), A)
     return float((G * Gh).sum() / (np.linalg.norm(G) * np.linalg.norm(Gh)))
+
+
+def sketch_accumulate_rounded_projection(S0, X_list, dY_list, seed: int, r: int, rows=None) -> np.ndarray:
+    """S = S0 + (1/sqrt(r)) sum_m dY_m^T RNE_bf16(X_m s^T): the sketch with the
+    projected inputs rounded once to bf16 before the backward multiply.
+
+    This is the plain definition of a lower-precision way to evaluate
+    equation 2 of LoGRA section 2.1 (inputs projected first, the paragraph
+    after equation 2): P_m = X_m s^T (s the signs of ``sign_matrix``) is
+    formed in float64, rounded to the nearest bf16 value (ties to even), and
+    then multiplied by the backward derivatives.  With exact bf16 P it equals
+    ``sketch_accumulate``.
+    """
+    s = sign_matrix(seed, r, np.asarray(X_list[0]).shape[1]).astype(np.float64)
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = (S0[rows] if rows is not None else S0).copy()
+    for X, dY in zip(X_list, dY_list):
+        P = round_to_bf16(np.asarray(X, dtype=np.float64) @ s.T)
+        dY = np.asarray(dY, dtype=np.float64)
+        if rows is not None:
+            dY = dY[:, rows]
+        S += (dY.T @ P) / math.sqrt(r)
+    return S

@@ -26,6 +26,9 @@ __all__ = [
     "library_loaded",
     "sketch_accumulate",
     "set_deterministic",
+    "set_precision",
+    "PRECISION_BF16X2",
+    "PRECISION_BF16",
     "projection_bytes",
     "project",
     "contract",
@@ -50,6 +53,7 @@ MAX_RANK = 256
 EXPORTED_SYMBOLS = (
     "logra_sketch_accumulate",
     "logra_set_deterministic",
+    "logra_set_precision",
     "logra_projection_bytes",
     "logra_project",
     "logra_contract",
@@ -97,6 +101,8 @@ def _declare(lib):
     lib.logra_sketch_accumulate.restype = ctypes.c_int
     lib.logra_set_deterministic.argtypes = [ctypes.c_int]
     lib.logra_set_deterministic.restype = ctypes.c_int
+    lib.logra_set_precision.argtypes = [ctypes.c_int]
+    lib.logra_set_precision.restype = ctypes.c_int
     lib.logra_projection_bytes.argtypes = [c_i64, c_i32]
     lib.logra_projection_bytes.restype = ctypes.c_size_t
     lib.logra_project.argtypes = [c_vp, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, ctypes.c_size_t, c_vp]
@@ -229,6 +235,17 @@ def set_deterministic(enable: bool) -> bool:
     """Bitwise-reproducible sketches on the calling thread (one workgroup per
     row tile of S, no atomic adds; slower).  Returns the previous setting."""
     return bool(load_library().logra_set_deterministic(1 if enable else 0))
+
+
+PRECISION_BF16X2 = 0
+PRECISION_BF16 = 1
+
+
+def set_precision(mode: int) -> int:
+    """Contraction precision on the calling thread: PRECISION_BF16X2 (P as a
+    bf16 high/low pair, the default) or PRECISION_BF16 (P rounded once to
+    bf16).  Returns the previous mode."""
+    return int(load_library().logra_set_precision(int(mode)))
 
 
 def projection_bytes(T: int, r: int) -> int:

@@ -1,7 +1,9 @@
 """Build liblogra.so (HIP, gfx950) in-tree with hipcc.
 
 Run ``python -m rank_gradient_sketching_accumulate_amd.build`` or call
-``build_library()``.  The library is always rebuilt when this is called.
+``build_library()``.  The library is always rebuilt when this is called:
+every translation unit is compiled to an object in parallel, then the
+objects are linked into one shared library.
 """
 
 from __future__ import annotations
@@ -10,6 +12,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
@@ -18,6 +22,8 @@ SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith("
 LIB_NAME = "liblogra.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
+# hipcc's host pass warns that it does not know the packed-fp32 feature.
+_NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -33,7 +39,6 @@ def compile_flags() -> list[str]:
         "-O3",
         "-std=c++17",
         "-fPIC",
-        "-shared",
         "-munsafe-fp-atomics",
         # Keep the compiler from forming packed fp32 arithmetic.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -43,19 +48,34 @@ def compile_flags() -> list[str]:
     ]
 
 
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    return res.returncode, err
+
+
 def build_library(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature.
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    with tempfile.TemporaryDirectory(prefix="logra_build_") as od:
+        objs = [os.path.join(od, os.path.basename(s)[:-4] + ".o") for s in SOURCES]
+        cmds = [[hipcc(), *compile_flags(), "-c", s, "-o", o] for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", "8"))))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(_run, cmds))
+        for c, (rc, err) in zip(cmds, results):
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed ({rc}) on {c[-3]}:\n{err}")
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        rc, err = _run(link)
+        if rc != 0:
+            raise RuntimeError(f"link failed ({rc}):\n{err}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

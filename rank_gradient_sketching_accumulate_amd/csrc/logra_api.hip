@@ -41,14 +41,18 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
   return ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * elem;
 }
 
-// Scratch per (device, purpose, stream).  It grows and never shrinks; before
-// it grows the stream is synchronised, so no queued kernel still uses the old
-// buffer.  New memory is zeroed (the sketch path keeps counters there that
-// must start at zero; its kernels leave them at zero).
-enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaKL = 2 };
+// Scratch per (device, purpose, stream).  It grows and never shrinks, and
+// it is zeroed when it grows (the split counters must start at zero; the
+// kernels leave them at zero).  A buffer it outgrows is retired, not freed:
+// a graph captured earlier on the stream may still launch kernels that use
+// it.  Retired and current buffers are freed only by logra_workspace_release.
+// Growing is refused while the stream is being captured (allocation and
+// clearing are not capturable); logra_workspace_reserve grows it beforehand.
+enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaKL = 2, kArenaCounters = 3, kArenaKinds = 4 };
 struct Arena {
   void* ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;
 };
 std::mutex g_arena_mu;
 std::map<std::pair<std::pair<int, int>, hipStream_t>, Arena> g_arenas;
@@ -62,26 +66,40 @@ logra_status arena_get(int kind, hipStream_t stream, size_t need, void** out) {
   if (a.bytes < need) {
     const char* fa = getenv("LOGRA_TEST_FAIL_ALLOC");
     if (fa && fa[0] == '1') return fail(LOGRA_ERR_NOMEM, "scratch allocation refused (LOGRA_TEST_FAIL_ALLOC=1)");
-    if (a.ptr) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-      e = hipFree(a.ptr);
-      if (e != hipSuccess) return hip_fail(e, "hipFree");
-      a.ptr = nullptr;
-      a.bytes = 0;
-    }
-    const size_t cap = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
-    e = hipMalloc(&a.ptr, cap);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(LOGRA_ERR_NOMEM,
+                  "the library's scratch for this stream must grow, but the stream is being captured: "
+                  "call logra_workspace_reserve before capturing");
+    size_t cap = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
+    if (a.bytes && cap < 2 * a.bytes) cap = 2 * a.bytes;  // geometric: retired buffers stay below the current one
+    void* np = nullptr;
+    e = hipMalloc(&np, cap);
     if (e != hipSuccess) {
-      a.ptr = nullptr;
+      (void)hipGetLastError();
       return fail(LOGRA_ERR_NOMEM, std::string("hipMalloc of scratch failed: ") + hipGetErrorString(e));
     }
-    e = hipMemset(a.ptr, 0, cap);
-    if (e != hipSuccess) return hip_fail(e, "hipMemset");
+    e = hipMemsetAsync(np, 0, cap, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(np);
+      return hip_fail(e, "hipMemsetAsync");
+    }
+    if (a.ptr) a.retired.push_back(a.ptr);
+    a.ptr = np;
     a.bytes = cap;
   }
   *out = a.ptr;
   return LOGRA_OK;
+}
+
+// Split counters: one unsigned per token tile, in an arena of their own.
+logra_status counters_get(hipStream_t stream, int64_t n, unsigned** out) {
+  void* p = nullptr;
+  logra_status st = arena_get(kArenaCounters, stream, (size_t)(n > 0 ? n : 1) * sizeof(unsigned), &p);
+  *out = static_cast<unsigned*>(p);
+  return st;
 }
 
 // Launch plans depend only on the shape, unless a LOGRA_ variable in the
@@ -96,16 +114,19 @@ bool plan_overrides_present() {
 
 // Per-thread switch of logra_set_deterministic.
 thread_local bool g_deterministic = false;
+// Per-thread switch of logra_set_precision: contract with the high bf16 half
+// of P only (one MFMA per product instead of two).
+thread_local bool g_precision_hi_only = false;
 
-SketchPlan sketch_plan_for(int64_t T, int64_t k, int64_t d, int r) {
+SketchPlan sketch_plan_for(int64_t T, int64_t k, int64_t d, int r, bool ho) {
   const bool det = g_deterministic;
-  if (plan_overrides_present()) return plan_sketch(T, k, d, r, det);
-  thread_local std::map<std::tuple<int64_t, int64_t, int64_t, int, bool>, SketchPlan> plans;
-  const auto key = std::make_tuple(T, k, d, r, det);
+  if (plan_overrides_present()) return plan_sketch(T, k, d, r, det, ho);
+  thread_local std::map<std::tuple<int64_t, int64_t, int64_t, int, bool, bool>, SketchPlan> plans;
+  const auto key = std::make_tuple(T, k, d, r, det, ho);
   auto it = plans.find(key);
   if (it != plans.end()) return it->second;
   if (plans.size() >= 1024) plans.clear();
-  const SketchPlan pl = plan_sketch(T, k, d, r, det);
+  const SketchPlan pl = plan_sketch(T, k, d, r, det, ho);
   plans.emplace(key, pl);
   return pl;
 }
@@ -156,8 +177,13 @@ logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t ld
 }
 
 // P = X s^T into the hi/lo planes (Pk order); tokens in [T, Tpad) get zeros.
+// hi_only: the fused call contracts with P rounded once to bf16: its
+// projection writes no low plane when the contraction reads none (the
+// single-bf16 tiling), or a zero one otherwise.  The split call always
+// writes both planes.
 logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X, int64_t ldx, int64_t T, int64_t k,
-                                uint64_t seed, int r, uint16_t* Phi, uint16_t* Plo, hipStream_t stream) {
+                                uint64_t seed, int r, uint16_t* Phi, uint16_t* Plo, bool hi_only,
+                                hipStream_t stream) {
   ProjParams pp{};
   pp.X = static_cast<const uint16_t*>(X);
   pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
@@ -166,7 +192,11 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
   pp.Plo = Plo;
   pp.Ppart = reinterpret_cast<float*>(base + pl.off_part);
   pp.part_stride = pl.Tpad * 16 * pl.NB;
-  pp.counters = reinterpret_cast<unsigned*>(base + pl.off_counters);
+  if (pl.n_k > 1) {
+    logra_status st = counters_get(stream, pl.n_counters, &pp.counters);
+    if (st != LOGRA_OK) return st;
+  }
+  pp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
   if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "projection launch");
@@ -175,7 +205,7 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
 
 // S += (1/sqrt r) dY^T P from the hi/lo planes.
 logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* dY, int64_t lddy, int64_t T, int64_t d,
-                                 const uint16_t* Phi, const uint16_t* Plo, int r, float* S, int64_t lds,
+                                 const uint16_t* Phi, const uint16_t* Plo, int r, float* S, int64_t lds, bool hi_only,
                                  hipStream_t stream) {
   ContractParams cp{};
   cp.dY = static_cast<const uint16_t*>(dY);
@@ -186,6 +216,7 @@ logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* d
   cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
   cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
   cp.bands = pl.cbands;
+  cp.hi_only = (hi_only && pl.cvar == 6) ? 1 : 0;
   if (pl.use_part) {
     cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
     cp.part_split = d * 16 * pl.NB;
@@ -259,7 +290,7 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     if (overlaps(S, span_bytes(d, r, lds, 4), X, span_bytes(T, k, ldx, 2)))
       return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
 
-    const SketchPlan pl = sketch_plan_for(T, k, d, r);
+    const SketchPlan pl = sketch_plan_for(T, k, d, r, g_precision_hi_only);
     st = check_plan(pl, T, ldx, lddy);
     if (st != LOGRA_OK) return st;
     void* ws = nullptr;
@@ -268,12 +299,18 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     char* base = static_cast<char*>(ws);
     uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
     uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
-    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, stream);
+    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, g_precision_hi_only, stream);
     if (st != LOGRA_OK) return st;
-    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, stream);
+    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, g_precision_hi_only, stream);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
+}
+
+int logra_set_precision(int mode) {
+  const int prev = g_precision_hi_only ? LOGRA_PRECISION_BF16 : LOGRA_PRECISION_BF16X2;
+  g_precision_hi_only = mode == LOGRA_PRECISION_BF16;
+  return prev;
 }
 
 int logra_set_deterministic(int enable) {
@@ -310,7 +347,7 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
     if (st != LOGRA_OK) return st;
     if (overlaps(P, need, X, span_bytes(T, k, ldx, 2))) return fail(LOGRA_ERR_ALIAS, "P overlaps X");
 
-    SketchPlan pl = sketch_plan_for(T, k, 1, r);
+    SketchPlan pl = sketch_plan_for(T, k, 1, r, false);
     st = check_plan(pl, T, ldx, 8);
     if (st != LOGRA_OK) return st;
     if (pl.Tpad > cache_tokens(T)) return fail(LOGRA_ERR_RANGE, "projection tile does not fit the cache");
@@ -320,7 +357,7 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
     if (st != LOGRA_OK) return st;
     uint16_t* Phi = static_cast<uint16_t*>(P);
     uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
-    return enqueue_projection(pl, static_cast<char*>(ws), X, ldx, T, k, seed, r, Phi, Plo, stream);
+    return enqueue_projection(pl, static_cast<char*>(ws), X, ldx, T, k, seed, r, Phi, Plo, false, stream);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -343,7 +380,7 @@ logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d, 
     if (overlaps(S, span_bytes(d, r, lds, 4), P, need)) return fail(LOGRA_ERR_ALIAS, "S overlaps P");
 
     // The contraction's tiling does not depend on k; 256 stands in for it.
-    SketchPlan pl = sketch_plan_for(T, 256, d, r);
+    SketchPlan pl = sketch_plan_for(T, 256, d, r, false);
     st = check_plan(pl, T, 8, lddy);
     if (st != LOGRA_OK) return st;
     scratch_layout(pl, d, false, true);
@@ -352,7 +389,7 @@ logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d, 
     if (st != LOGRA_OK) return st;
     const uint16_t* Phi = static_cast<const uint16_t*>(P);
     const uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
-    return enqueue_contraction(pl, static_cast<char*>(ws), dY, lddy, T, d, Phi, Plo, r, S, lds, stream);
+    return enqueue_contraction(pl, static_cast<char*>(ws), dY, lddy, T, d, Phi, Plo, r, S, lds, false, stream);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }

@@ -184,4 +184,74 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// MFMAs with the accumulators pinned to AGPRs.  Kernels that keep 256
+// accumulator registers per lane (one wave per SIMD) need them in the AGPR
+// half of the register file; with the builtin the compiler keeps loop-carried
+// accumulators in VGPRs and copies every MFMA result across (thousands of
+// v_accvgpr moves and spills).  Inline asm with "a" constraints keeps them in
+// AGPRs, but the compiler's hazard recognizer does not look inside it, so
+// every block states its own wait states:
+//   * it opens with s_nop 2 (three wait states), more than the two a VALU
+//     write of a VGPR needs before an MFMA reads it as SrcA/B/C (the
+//     operands here are often written by the VALU just before);
+//   * MFMAs inside a block write distinct accumulators, and an accumulator
+//     is read as SrcC only by a later MFMA of the same shape (exact overlap,
+//     which the hardware forwards);
+//   * before any non-MFMA instruction reads the accumulators, call
+//     mfma_drain(): it waits out the longest MFMA-write -> VALU/memory-read
+//     distance, and mfma_touch() orders each later read after that wait.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mfma4_b(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, const u32x4& a0,
+                                        const u32x4& a1, const u32x4& a2, const u32x4& a3, const u32x4& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %8, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %8, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %8, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %7, %8, %3"
+      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b));
+}
+// Eight accumulators sharing one B operand: c_q += a_q * b.
+__device__ __forceinline__ void mfma8_b(f32x4 (&c)[8], const u32x4 (&a)[8], const u32x4& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %8, %16, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %9, %16, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %10, %16, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %11, %16, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %4, %12, %16, %4\n\t"
+      "v_mfma_f32_16x16x32_bf16 %5, %13, %16, %5\n\t"
+      "v_mfma_f32_16x16x32_bf16 %6, %14, %16, %6\n\t"
+      "v_mfma_f32_16x16x32_bf16 %7, %15, %16, %7"
+      : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3]), "+a"(c[4]), "+a"(c[5]), "+a"(c[6]), "+a"(c[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(b));
+}
+// Four accumulators, each multiplied by its own A operand and two B operands
+// in turn (the high and low bf16 halves of one fp32 operand): c_q += a_q*bh,
+// then c_q += a_q*bl; the four bh products come first, so dependent MFMAs are
+// four apart.
+__device__ __forceinline__ void mfma4_hl(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& c3, const u32x4& a0,
+                                         const u32x4& a1, const u32x4& a2, const u32x4& a3, const u32x4& bh,
+                                         const u32x4& bl) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %8, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %8, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %8, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %7, %8, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %9, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %5, %9, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %9, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %7, %9, %3"
+      : "+a"(c0), "+a"(c1), "+a"(c2), "+a"(c3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(bh), "v"(bl));
+}
+// Wait states after the last MFMA before its results are read by anything
+// else (more than the 19 a 16-pass MFMA write needs before a VALU read).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+// Orders later reads of c after mfma_drain() (volatile asm keeps its order).
+__device__ __forceinline__ void mfma_touch(f32x4& c) { asm volatile("" : "+a"(c)); }
+
 }  // namespace logra

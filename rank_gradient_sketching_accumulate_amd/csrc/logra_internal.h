@@ -25,6 +25,8 @@ struct ProjParams {
   float* Ppart;     // n_k fp32 partial sums, Pk order (n_k > 1 only)
   int64_t part_stride;
   unsigned* counters;  // one per token tile; zero between calls
+  int hi_only;      // 0: write P's high and low planes; 1: the high plane only (the
+                    // contraction reads no low plane); 2: high plane, zero low plane
 };
 
 struct ContractParams {
@@ -43,6 +45,7 @@ struct ContractParams {
   float* part;      // non-null: token split ts stores its tile at part + ts*part_split instead
   int64_t part_split;  // floats per split (d x 16*NB, row stride 16*NB)
   int bands;        // stream-K kernels: token bands, 1, 4 or 8 (grid a multiple of bands)
+  int hi_only;      // contract with the high bf16 plane of P only
 };
 
 struct SketchPlan {
@@ -50,9 +53,12 @@ struct SketchPlan {
   int small_proj;         // 1: proj_small_kernel (all signs of k in LDS)
   int MBW, WK;            // projection: 16-token blocks per wave, waves along k
   int PNW;                // projection (round-based): waves per workgroup (4 or 8)
+  int pwide;              // 1: proj_wide_kernel (NB = 8 or 16, 128-token tiles, one wave per SIMD)
+  int pnx;                // proj_wide_kernel: X ring depth in 32-column steps (4 or 8)
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)
+  int cwide;              // cvar 6: 1 = eight-wave shared-operand kernel, 2 = four-wave kernel
   int WM;                 // contraction row groups per workgroup (cvar 5)
   int few_ts;             // tall S: at most one round of workgroups, few token splits
   int n_dt, n_ts;
@@ -61,12 +67,14 @@ struct SketchPlan {
   int cgrid;              // contract_small / contract_tile: workgroups sharing the step units
   int cbands;             // token bands of that split (1; 4 = one per XCD pair; 8 = one per XCD)
   int bigdp;              // contract_big: steps between requesting a step's operands and using them
-  size_t off_counters, off_phi, off_plo, off_part, off_cpart, total;
+  int64_t n_counters;     // split counters the projection needs (a separate zeroed region)
+  size_t off_phi, off_plo, off_part, off_cpart, total;
 };
 
 // det: bitwise-reproducible contraction (one workgroup per row tile of S,
 // fixed summation order, no atomic adds).
-SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det = false);
+// hi_only: the contraction uses the high bf16 plane of P only.
+SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det = false, bool hi_only = false);
 // Caller-held projection cache of the split project / contract calls: a high
 // plane then a low plane, each cache_tokens(T) x 16*NB bf16 entries in Pk
 // order.  Every projection tiling's padded token count fits in it (token

@@ -109,8 +109,11 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   const uint32_t wbase = (uint32_t)(((rw + lrow) * p.ldw + c_begin + lcol) * 2);
   const uint32_t wrowstep = (uint32_t)(RPI * p.ldw * 2);
   u32x2 wv[PD][NI];
+  // Loads are unconditional (chunks past the range re-read the last one,
+  // which is never used): a load under a branch would make the compiler's
+  // wait counts wait for every load in flight.
   auto load_w = [&](int slot, int ch) {
-    if (ch >= nch) return;
+    ch = min(ch, nch - 1);
     uint32_t off = wbase + (uint32_t)(ch * CW * 2);
 #pragma unroll
     for (int q = 0; q < NI; ++q) {
@@ -226,8 +229,8 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
           }
         }
         __builtin_amdgcn_wave_barrier();
-        load_w(u, ch + PD);
       }
+      load_w(u, ch + PD);
     }
   }
 }

@@ -85,20 +85,23 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 xr[8][MBW];
+  // Loads are unconditional (steps past the wave's range re-read the last
+  // step of k and are never used): a load under a branch would make the
+  // compiler's wait counts wait for every load in flight.
   auto issue = [&](u32x4 (&slot)[MBW], int j) {
-    const int64_t col = (int64_t)(ks0 + j) * 32 + 8 * g;
+    const int64_t col = (int64_t)min(ks0 + j, nks - 1) * 32 + 8 * g;
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < nloc) {
-        v = buf_load16(rx, rowoff[mb] + (uint32_t)(col * 2));
-        if (col + 8 > p.k) {  // last step of a k that is not a multiple of 32
+    for (int mb = 0; mb < MBW; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + (uint32_t)(col * 2));
+  };
+  // The last step of a k that is not a multiple of 32: zero the entries past k.
+  auto xmask = [&](u32x4 (&slot)[MBW], int ks) {
+    if ((int64_t)ks * 32 + 32 <= p.k) return;
+    const int64_t nv = p.k - ((int64_t)ks * 32 + 8 * g);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e >= p.k) v[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-      }
-      slot[mb] = v;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) slot[mb][q] &= m;
     }
   };
 #pragma unroll
@@ -119,9 +122,10 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int j = j0 + u;
+      issue(xr[(u + 7) & 7], j + 7);
       if (j < nloc) {
-        issue(xr[(u + 7) & 7], j + 7);
         const int ks = ks0 + j;
+        xmask(xr[u], ks);
         const uint32_t* sb = lds + ((ks >> 3) * RP + i) * SROW + (ks & 7);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
       split_hi_lo2(sum[0], sum[1], h0, l0);
       split_hi_lo2(sum[2], sum[3], h1, l1);
       *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
+      if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
     }
   }
 }
@@ -241,12 +245,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
+  // X through a buffer descriptor: token rows past T read as zero.  Every
+  // load is issued unconditionally (a block past the range re-reads the
+  // range's last block, which is in cache): a load under a branch would make
+  // the compiler's wait counts assume the path without it and wait for every
+  // load in flight.  Columns past k, and blocks past the range, are zeroed
+  // where the step is used (xmask).
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
+  uint32_t rowoff[MBW];
+#pragma unroll
+  for (int mb = 0; mb < MBW; ++mb) rowoff[mb] = (uint32_t)((tw + 16 * mb + i) * p.ldx * 2);
   u32x4 xr[8][MBW];
   auto issue = [&](u32x4 (&slot)[MBW], int cb, int s) {
+    const int cbl = min(cb, cbe - 1);
+    const uint32_t coff = (uint32_t)(((int64_t)cbl * 256 + 32 * s + 8 * g) * 2);
 #pragma unroll
-    for (int mb = 0; mb < MBW; ++mb)
-      slot[mb] = (cb < cbe) ? load_x8(p.X, p.ldx, p.T, p.k, tw + 16 * mb + i, (int64_t)cb * 256 + 32 * s + 8 * g)
-                            : u32x4{0u, 0u, 0u, 0u};
+    for (int mb = 0; mb < MBW; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + coff);
+  };
+  // Zero the entries of a step's X operands whose columns fall past k (only
+  // the last step of k can have any; wave-uniform test).
+  auto xmask = [&](u32x4 (&slot)[MBW], int cb, int s) {
+    const int64_t c0 = (int64_t)cb * 256 + 32 * s;
+    if (c0 + 32 <= p.k) return;
+    const int64_t nv = p.k - (c0 + 8 * g);  // valid entries of this lane's eight
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MBW; ++mb) slot[mb][q] &= m;
+    }
   };
 
   gen(0, 0);
@@ -270,6 +297,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       else
         issue(xr[s - 1], cb + WK, s - 1);
       if (cb < cbe) {
+        xmask(xr[s], cb, s);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
@@ -325,7 +353,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
           split_hi_lo2(acc[mb][nb][0], acc[mb][nb][1], h0, l0);
           split_hi_lo2(acc[mb][nb][2], acc[mb][nb][3], h1, l1);
           *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
-          *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
+          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
         }
     }
     return;
@@ -368,7 +396,241 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     split_hi_lo2(sum[0], sum[1], h0, l0);
     split_hi_lo2(sum[2], sum[3], h1, l1);
     *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
-    *reinterpret_cast<u32x2*>(p.Plo + e0) = u32x2{l0, l1};
+    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+  }
+  if (threadIdx.x == 0) p.counters[tt] = 0u;
+}
+
+// ===========================================================================
+// Projection for ranks above 64 (NB = 8 or 16).  Eight waves, two per SIMD.
+// Wave (wn, wk) keeps the workgroup's 64 tokens x one half of P's 16*NB
+// columns in accumulators (8*NB*2 registers: 128 at NB = 16, pinned to the
+// AGPR half of the wave's registers so that its VGPRs hold the X ring and
+// the sign work), so each
+// expanded sign operand feeds four MFMAs (the sign expansion is half the
+// VALU work it is when a wave holds every column), while the second wave of
+// each SIMD hides the first's VALU and memory latency.  wk picks which of a
+// round's four 256-column blocks the wave multiplies.  Each round
+// regenerates the signs of the next round's four blocks into LDS
+// (branch-free: two Philox blocks per thread at NB = 16, one at NB = 8) while
+// the current ones are multiplied; X streams through a ring of NX 32-column
+// steps.  After the last round the four wave columns are summed through LDS
+// in two halving rounds, and the wk = 0 waves write P (or, with column
+// splits across workgroups, their fp32 partial).
+// ===========================================================================
+template <int NB, int NX>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_wide_kernel(ProjParams p) {
+  constexpr int RP = 16 * NB;
+  constexpr int NBW = NB / 2;           // column blocks per wave
+  constexpr int MT = 4;                 // 16-token blocks per wave: the whole tile
+  constexpr int TT = 16 * MT;           // tokens per workgroup
+  constexpr int WK = 4;                 // blocks per round
+  constexpr int SROW = 9;               // 8 dwords of sign bits + 1 pad dword per row
+  constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
+  constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
+  constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
+  constexpr int NGEN = RP * WK / 512;   // Philox blocks per thread and round
+  static_assert(NGEN * 512 == RP * WK, "one or two sign blocks per thread");
+  static_assert(NX >= 2 && NX <= 8, "ring depth");
+  static_assert(MT == 4, "one asm block of four MFMAs per column block");
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
+  __shared__ int s_last;
+
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int tt = lin / p.n_k;
+  const int ksp = lin - tt * p.n_k;
+  if (tt >= p.n_tt) return;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int wn = wave & 1, wk = wave >> 1;
+  const int64_t t0 = (int64_t)tt * TT;
+  const int cbb = ksp * p.cbs_per;
+  const int cbe = min(p.ncb, cbb + p.cbs_per);
+  const int nrounds = (cbe - cbb + WK - 1) / WK;
+
+  f32x4 acc[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) into
+  // sign buffer buf.  Blocks past the range are generated all the same
+  // (their X operands are zeroed) so that the code has no branch.
+  auto gen = [&](int j, int buf) {
+#pragma unroll 1
+    for (int q = 0; q < NGEN; ++q) {
+      const int b = threadIdx.x + 512 * q;
+      const int row = b % RP, wkk = b / RP;
+      uint32_t w[8];
+      philox_sign_block(p.seed, (uint32_t)row, (uint32_t)(cbb + WK * j + wkk), w);
+      uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = w[e];
+    }
+  };
+
+  // X through a buffer descriptor (token rows past T read as zero).  Loads
+  // are unconditional: a block past the range re-reads the range's last block
+  // (in cache) and is zeroed where used, so the compiler's wait counts never
+  // take a path without the load.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
+  uint32_t rowoff[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) rowoff[mb] = (uint32_t)((t0 + 16 * mb + i) * p.ldx * 2);
+  u32x4 xr[NX][MT];
+  auto issue = [&](u32x4 (&slot)[MT], int cb, int s) {
+    const int cbl = min(cb, cbe - 1);
+    const uint32_t coff = (uint32_t)(((int64_t)cbl * 256 + 32 * s + 8 * g) * 2);
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + coff);
+  };
+  // Zero the X entries of step (cb, s) whose columns are past k or whose
+  // block is past the range (wave-uniform test; no loads inside).
+  auto xmask = [&](u32x4 (&slot)[MT], int cb, int s) {
+    const int64_t c0 = (int64_t)cb * 256 + 32 * s;
+    if (cb < cbe && c0 + 32 <= p.k) return;
+    const int64_t nv = cb < cbe ? p.k - (c0 + 8 * g) : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) slot[mb][q] &= m;
+    }
+  };
+
+  gen(0, 0);
+#pragma unroll
+  for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
+  __syncthreads();
+
+  const SignExpander ex(g);
+  for (int j = 0; j < nrounds; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
+    const int cb = cbb + WK * j + wk;
+    const uint32_t* sb = smem + buf * SBUF + (wk * RP + 16 * NBW * wn + i) * SROW;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int t = s + NX - 1;  // the step whose loads go out now
+      issue(xr[t % NX], t < 8 ? cb : cb + WK, t & 7);
+      xmask(xr[s % NX], cb, s);
+      const u32x4(&xs)[MT] = xr[s % NX];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
+        mfma4_b(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], xs[0], xs[1], xs[2], xs[3], bsg);
+      }
+    }
+    __syncthreads();
+  }
+  // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
+  // sums are worked on in VGPRs.
+  mfma_drain();
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) mfma_touch(acc[nb][mb]);
+  f32x4 v[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) v[nb][mb] = acc[nb][mb];
+  // (Columns >= r, from sign rows the caller did not ask for, are left in P:
+  // they only feed columns of S that are never stored.)
+
+  // Sum the four wave columns in two halving rounds through LDS (the sign
+  // buffers are free: the last round ended with a barrier): wk = 2, 3 park
+  // and wk = 0, 1 add, then wk = 1 parks and wk = 0 adds.
+  float* const red = reinterpret_cast<float*>(smem);
+  auto slot = [&](int half, int nb, int mb) {
+    return red + (((half * 2 + wn) * NBW + nb) * MT + mb) * 256 + 4 * lane;
+  };
+#pragma unroll
+  for (int level = 2; level >= 1; level >>= 1) {
+    if (wk >= level && wk < 2 * level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) *reinterpret_cast<f32x4*>(slot(wk - level, nb, mb)) = v[nb][mb];
+    }
+    __syncthreads();
+    if (wk < level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) v[nb][mb] += *reinterpret_cast<const f32x4*>(slot(wk, nb, mb));
+    }
+    __syncthreads();
+  }
+  const int cb0 = NBW * wn;  // first column block of this wave
+
+  if (p.n_k == 1) {
+    if (wk == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          const f32x4 o = v[nb][mb];
+          const int64_t e0 = pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+          uint32_t h0, l0, h1, l1;
+          split_hi_lo2(o[0], o[1], h0, l0);
+          split_hi_lo2(o[2], o[3], h1, l1);
+          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+        }
+    }
+    return;
+  }
+
+  // Column splits across workgroups (the splits of a token tile are
+  // consecutive logical ids, all on one XCD): each split stores its fp32
+  // partial with agent-coherent (sc1) stores; the last to arrive sums them
+  // in split order and writes P, with all of a thread's loads in flight at
+  // once.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Ppart, (uint32_t)((int64_t)p.n_k * p.part_stride * 4));
+  if (wk == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) {
+        const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+        store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
+      }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(p.counters + tt, 1u);
+    s_last = (prev == (unsigned)(p.n_k - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
+  f32x4 sum[ITEMS];
+  int64_t e0[ITEMS];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int v = threadIdx.x + 512 * q;
+    e0[q] = pk_index(t0 + 4 * (int64_t)(v / RP), v % RP, NB);
+    sum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp = 0; sp < p.n_k; ++sp) {
+    f32x4 part[ITEMS];
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q)
+      part[q] = __builtin_bit_cast(f32x4, load16_agent(rs, (uint32_t)(((int64_t)sp * p.part_stride + e0[q]) * 4)));
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) sum[q] += part[q];
+  }
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    uint32_t h0, l0, h1, l1;
+    split_hi_lo2(sum[q][0], sum[q][1], h0, l0);
+    split_hi_lo2(sum[q][2], sum[q][3], h1, l1);
+    *reinterpret_cast<u32x2*>(p.Phi + e0[q]) = u32x2{h0, h1};
+    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0[q]) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
   }
   if (threadIdx.x == 0) p.counters[tt] = 0u;
 }
@@ -549,9 +811,11 @@ __global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
 
     u32x2 y[DEPTH][8];
     u32x4 bh[DEPTH][NB], bl[DEPTH][NB];
+    // Loads are unconditional (steps past the wave's share re-read the
+    // segment's last step, which is never used): a load under a branch would
+    // make the compiler's wait counts wait for every load in flight.
     auto issue = [&](int slot_y, int m) {
-      if (m >= nsteps) return;
-      const int64_t ks = ks0 + (int64_t)NW * m;
+      const int64_t ks = min(ks0 + (int64_t)NW * m, ks_end - 1);
       uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -572,8 +836,8 @@ __global__ __launch_bounds__(512) void contract_small_kernel(ContractParams p) {
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
         const int m = m0 + u;
+        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
         if (m < nsteps) {
-          issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
           u32x4 a[kDC];
           transpose_dy(y[u], a);
 #pragma unroll
@@ -762,8 +1026,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
   // half at the end of step m, DP - 1 steps after it was requested.
   u32x2 y[DP + 1][8];
   u32x4 stg[DP][PER];
+  // Loads are issued unconditionally (a step past the range reloads the
+  // last one): a load under a branch makes the compiler's wait counts assume
+  // the shortest path, which would wait for every prefetch at each step.
   auto load_y = [&](u32x2 (&slot)[8], int m) {
-    if (m >= nsteps) return;
+    m = min(m, nsteps - 1);
     uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -773,7 +1040,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
   };
   // Thread q moves words q, q + 512, ... of the step's [hi | lo] tile.
   auto load_p = [&](u32x4 (&sl)[PER], int m) {
-    if (m >= nsteps) return;
+    m = min(m, nsteps - 1);
     const int64_t base = (ks_beg + m) * (int64_t)PV;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -790,21 +1057,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
   // Steps 0 .. DP - 1 in flight; step 0 staged.  P of step m lives in
   // stg[m % DP] until it is staged, dY of step m in y[m % (DP + 1)]; the loop
   // body covers DP * (DP + 1) steps so that both indices are constants.
+  // Every active workgroup has at least one step (token splits are cut so).
+  if (nsteps > 0) {
 #pragma unroll
   for (int q = 0; q < DP; ++q) {
     load_p(stg[q], q);
     load_y(y[q], q);
   }
-  if (nsteps > 0) store_p(stg[0], 0);
+  store_p(stg[0], 0);
   __syncthreads();
   constexpr int L = DP * (DP + 1);
   for (int m0 = 0; m0 < nsteps; m0 += L) {
 #pragma unroll
     for (int u = 0; u < L; ++u) {
       const int m = m0 + u;
+      load_p(stg[u % DP], m + DP);  // stg[m % DP] was staged at the end of step m - 1
+      load_y(y[(u + DP) % (DP + 1)], m + DP);
       if (m < nsteps) {
-        load_p(stg[u % DP], m + DP);  // stg[m % DP] was staged at the end of step m - 1
-        load_y(y[(u + DP) % (DP + 1)], m + DP);
         u32x4 a[kDC];
         transpose_dy(y[u % (DP + 1)], a);
         const u32x4* ph = &pt[u & 1][0];
@@ -820,6 +1089,287 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
         }
         if (m + 1 < nsteps) store_p(stg[(u + 1) % DP], (u + 1) & 1);
         __syncthreads();
+      }
+    }
+  }
+  }
+  store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
+}
+
+// Rank 256 on large layers: four waves, one per SIMD, each owning 64 rows x
+// all 256 columns of the workgroup's 256 x 256 S tile (256 accumulator
+// registers, pinned to the AGPR half of the register file).  Every wave
+// streams its own rows of dY (no two waves load the same bytes: duplicated
+// loads from one CU halve the streaming rate), and the step's P tile (hi
+// and, unless HL == 1, lo planes) sits in a two-stage LDS ring written by
+// all four waves from registers loaded one step ahead, with one barrier per
+// step.  Within a step the B operands of column block nb + 1 are read from
+// LDS while the MFMAs of block nb run.  HL == 1 contracts with the high
+// bf16 half of P only (one MFMA per product).
+template <int HL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1))) void contract_wide_kernel(ContractParams p) {
+  constexpr int NB = 16;
+  constexpr int PV = NB * 64;      // u32x4 words per plane and step
+  constexpr int PW = HL * PV;      // u32x4 words per stage
+  constexpr int PER = PW / 256;    // words each thread moves per step
+  constexpr int DY = 4;            // dY ring depth (steps): loads go out three steps ahead
+  constexpr int DPP = 2;           // P register ring depth: loads go out two steps before staging
+  __shared__ u32x4 pt[2][PW];
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int dt = lin / p.n_ts;
+  const int ts = lin - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t d0w = (int64_t)dt * 256 + (int64_t)wave * 16 * kDC;
+  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+  const int64_t nks = (p.T + 31) >> 5;
+  const int64_t ks_beg = ts * p.ksp;
+  const int64_t ks_end = min(nks, ks_beg + p.ksp);
+  const int nsteps = ks_end > ks_beg ? (int)(ks_end - ks_beg) : 0;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+  const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+
+  f32x4 acc[kDC][NB];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Loads are unconditional (steps past the range re-read the last step):
+  // a load under a branch would make the compiler's wait counts wait for
+  // every load in flight.
+  u32x2 y[DY][8];
+  auto load_y = [&](u32x2 (&slot)[8], int m) {
+    m = min(m, nsteps - 1);
+    uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      slot[e] = buf_load8(ry, off);
+      off += rowstep;
+    }
+  };
+  // Thread q moves words q, q + 256, ... of the step's [hi | lo] tile.
+  u32x4 stg[DPP][PER];
+  auto load_p = [&](u32x4 (&sl)[PER], int m) {
+    m = min(m, nsteps - 1);
+    const int64_t base = (ks_beg + m) * (int64_t)PV;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int w = threadIdx.x + 256 * j;
+      const uint16_t* src = (w < PV) ? p.Phi + (base + w) * 8 : p.Plo + (base + w - PV) * 8;
+      sl[j] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pt[buf][threadIdx.x + 256 * j] = sl[j];
+  };
+
+  // Every active workgroup has at least one step (token splits are cut so).
+  // P of step m sits in stg[m % DPP] from step m - 2 (when it is requested)
+  // to step m - 1 (when it goes into LDS stage m % 2); dY of step m sits in
+  // y[m % DY] from step m - 3.  The loop body covers four steps so that all
+  // ring indices are constants.
+  static_assert(DY == 4 && DPP == 2, "loop body of four steps");
+  if (nsteps > 0) {
+    load_p(stg[0], 0);
+    load_p(stg[1], 1);
+    load_y(y[0], 0);
+    load_y(y[1], 1);
+    load_y(y[2], 2);
+    store_p(stg[0], 0);
+    load_p(stg[0], 2);
+    __syncthreads();
+    for (int m0 = 0; m0 < nsteps; m0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = m0 + u;
+        // P of step m + 1 into the other stage (its readers finished step
+        // m - 1 before the last barrier), then request step m + 3 into the
+        // freed registers and dY of step m + 3.
+        store_p(stg[(u + 1) % DPP], (u + 1) & 1);
+        load_p(stg[(u + 1) % DPP], m + 3);
+        load_y(y[(u + 3) % DY], m + 3);
+        if (m < nsteps) {
+          u32x4 a[kDC];
+          transpose_dy(y[u % DY], a);
+          const u32x4* ph = &pt[u & 1][0];
+          u32x4 bh = ph[lane], bl = HL == 2 ? ph[PV + lane] : bh;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            u32x4 nh = bh, nl = bl;
+            if (nb + 1 < NB) {
+              nh = ph[(nb + 1) * 64 + lane];
+              if (HL == 2) nl = ph[PV + (nb + 1) * 64 + lane];
+            }
+            if (HL == 2)
+              mfma4_hl(acc[0][nb], acc[1][nb], acc[2][nb], acc[3][nb], a[0], a[1], a[2], a[3], bh, bl);
+            else
+              mfma4_b(acc[0][nb], acc[1][nb], acc[2][nb], acc[3][nb], a[0], a[1], a[2], a[3], bh);
+            bh = nh;
+            bl = nl;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  mfma_drain();
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) mfma_touch(acc[c][nb]);
+  store_s_tile<NB>(p, acc, d0w, 0, g, i, ts);
+}
+
+// Rank 256 on large layers, eight waves (two per SIMD): wave (wm, wn) owns
+// 64 rows x 128 columns of the workgroup's 256 x 256 S tile (128 accumulator
+// registers).  Both column halves of a row group need the same dY operands,
+// and two waves of one CU loading the same bytes halve the streaming rate;
+// so the wn = 0 wave alone loads its rows of dY (three steps ahead),
+// transposes them into MFMA operands one step ahead and hands them to its
+// wn = 1 partner through LDS, while the wn = 1 waves alone move the step's P
+// tile (hi and, unless HL == 1, lo planes; requested two steps ahead) into a
+// two-stage LDS ring.  One barrier per step publishes both.
+template <int HL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void contract_share_kernel(ContractParams p) {
+  constexpr int NB = 16, WN = 2, WM = 4, NBW = NB / WN;
+  constexpr int PV = NB * 64;      // u32x4 words per plane and step
+  constexpr int PW = HL * PV;      // u32x4 words per stage
+  constexpr int PER = PW / 256;    // words each wn = 1 thread moves per step
+  constexpr int DY = 4;            // dY ring of the wn = 0 waves (steps)
+  __shared__ u32x4 pt[2][PW];
+  __shared__ u32x4 at[2][WM][kDC][64];
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int dt = lin / p.n_ts;
+  const int ts = lin - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int wn = wave % WN, wm = wave / WN;
+  const int64_t d0w = ((int64_t)dt * WM + wm) * 16 * kDC;
+  const int64_t nks = (p.T + 31) >> 5;
+  const int64_t ks_beg = ts * p.ksp;
+  const int64_t ks_end = min(nks, ks_beg + p.ksp);
+  const int nsteps = ks_end > ks_beg ? (int)(ks_end - ks_beg) : 0;
+
+  f32x4 acc[kDC][NBW];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const u32x4 (&a)[kDC], int buf) {
+    const u32x4* ph = &pt[buf][0];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const u32x4 bh = ph[(wn * NBW + nb) * 64 + lane];
+      if constexpr (HL == 2) {
+        const u32x4 bl = ph[PV + (wn * NBW + nb) * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < kDC; ++c) {
+          acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
+          acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kDC; ++c) acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
+      }
+    }
+  };
+
+  // Every active workgroup has at least one step (token splits are cut so).
+  // Both branches below run the same number of barriers.  Loads are
+  // unconditional (steps past the range re-read the last one): a load under
+  // a branch would make the compiler's wait counts wait for every load in
+  // flight.
+  if (nsteps > 0) {
+    if (wn == 0) {
+      const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+      const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+      const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+      u32x2 y[DY][8];
+      auto load_y = [&](u32x2 (&slot)[8], int m) {
+        m = min(m, nsteps - 1);
+        uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          slot[e] = buf_load8(ry, off);
+          off += rowstep;
+        }
+      };
+#pragma unroll
+      for (int q = 0; q < DY - 1; ++q) load_y(y[q], q);
+      {
+        u32x4 a0[kDC];
+        transpose_dy(y[0], a0);
+#pragma unroll
+        for (int c = 0; c < kDC; ++c) at[0][wm][c][lane] = a0[c];
+      }
+      __syncthreads();
+      for (int m0 = 0; m0 < nsteps; m0 += DY) {
+#pragma unroll
+        for (int u = 0; u < DY; ++u) {
+          const int m = m0 + u;
+          load_y(y[(u + DY - 1) % DY], m + DY - 1);
+          {
+            u32x4 an[kDC];
+            transpose_dy(y[(u + 1) % DY], an);  // operands of step m + 1
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) at[(u + 1) & 1][wm][c][lane] = an[c];
+          }
+          if (m < nsteps) {
+            u32x4 a[kDC];
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) a[c] = at[u & 1][wm][c][lane];
+            compute(a, u & 1);
+          }
+          __syncthreads();
+        }
+      }
+    } else {
+      // Thread q of the wn = 1 waves moves words q, q + 256, ... of the
+      // step's [hi | lo] tile.
+      const int tq = (wm * 64) + lane;
+      u32x4 stg[2][PER];
+      auto load_p = [&](u32x4 (&sl)[PER], int m) {
+        m = min(m, nsteps - 1);
+        const uint16_t* hi = p.Phi + ((ks_beg + m) * (int64_t)PV) * 8;
+        const uint16_t* lo = p.Plo + ((ks_beg + m) * (int64_t)PV) * 8;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int w = tq + 256 * j;  // plane fixed at compile time: PV is a multiple of 256
+          sl[j] = *reinterpret_cast<const u32x4*>(j * 256 < PV ? hi + (size_t)w * 8 : lo + (size_t)(w - PV) * 8);
+        }
+      };
+      auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) pt[buf][tq + 256 * j] = sl[j];
+      };
+      load_p(stg[0], 0);
+      load_p(stg[1], 1);
+      store_p(stg[0], 0);
+      load_p(stg[0], 2);
+      __syncthreads();
+      for (int m0 = 0; m0 < nsteps; m0 += DY) {
+#pragma unroll
+        for (int u = 0; u < DY; ++u) {
+          const int m = m0 + u;
+          // P of step m + 1 into the other stage (its readers finished step
+          // m - 1 before the last barrier), then request step m + 3.
+          store_p(stg[(u + 1) & 1], (u + 1) & 1);
+          load_p(stg[(u + 1) & 1], m + 3);
+          if (m < nsteps) {
+            u32x4 a[kDC];
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) a[c] = at[u & 1][wm][c][lane];
+            compute(a, u & 1);
+          }
+          __syncthreads();
+        }
       }
     }
   }
@@ -873,9 +1423,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
     u32x2 y[DEPTH][8];
     u32x4 bh[DEPTH][NBW], bl[DEPTH][NBW];
+    // Unconditional loads, as in contract_small_kernel.
     auto issue = [&](int slot, int m) {
-      if (m >= nsteps) return;
-      const int64_t ks = ks0 + (int64_t)WT * m;
+      const int64_t ks = min(ks0 + (int64_t)WT * m, ks_end - 1);
       uint32_t off = (uint32_t)((32 * ks + 8 * g) * p.lddy * 2) + coloff;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -896,8 +1446,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
         const int m = m0 + u;
+        issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
         if (m < nsteps) {
-          issue((u + DEPTH - 1) % DEPTH, m + DEPTH - 1);
           u32x4 a[kDC];
           transpose_dy(y[u], a);
 #pragma unroll
@@ -1004,8 +1554,6 @@ size_t projection_cache_bytes(int64_t T, int r) {
 void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part) {
   const size_t RP = 16 * (size_t)pl.NB;
   size_t off = 0;
-  pl.off_counters = off;
-  off += align_up((size_t)pl.n_tt * sizeof(unsigned), 256);
   pl.off_phi = pl.off_plo = 0;
   pl.off_part = off;
   if (proj_part && pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
@@ -1019,18 +1567,42 @@ int env_int(const char* name, int dflt) {
   return (s && *s) ? atoi(s) : dflt;
 }
 
-SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
+SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi_only) {
   SketchPlan pl{};
   pl.NB = pow2_blocks(r);
   const int RP = 16 * pl.NB;
   pl.ncb = (int)((k + 255) / 256);
   const int64_t T32 = (T + 31) / 32 * 32;
 
-  // Projection.  Small r*k: the whole k range's signs fit in 64 KB of LDS.
-  pl.small_proj = ((size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
-  pl.small_proj = env_int("LOGRA_PROJ_SMALL", pl.small_proj);
+  // Projection.  Ranks above 64 with at least two 256-column blocks: the
+  // wide kernel (128-token tiles, one wave per SIMD).  Small r*k otherwise:
+  // the whole k range's signs fit in 64 KB of LDS.
+  pl.pwide = (pl.NB >= 8 && pl.ncb >= 2) ? 1 : 0;
+  pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 8 ? 1 : 0;
+  pl.pnx = env_int("LOGRA_PROJ_NX", 4) == 3 ? 3 : (env_int("LOGRA_PROJ_NX", 4) == 8 ? 8 : 4);
+  pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
+  pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
-  if (pl.small_proj) {
+  if (pl.pwide) {
+    // 128-token tiles; column splits across workgroups (powers of two, so
+    // that a tile's splits are consecutive ids on one XCD) until there is a
+    // workgroup per CU, each split at least one round of two blocks.
+    TT = 64;
+    pl.WK = 4;
+    pl.MBW = 4;
+    pl.n_tt = (int)((T32 + TT - 1) / TT);
+    const int rounds = (pl.ncb + 3) / 4;
+    int nk = 1;
+    while (nk < 8 && (int64_t)pl.n_tt * nk < 256 && 2 * nk <= rounds + 1) nk *= 2;  // at least ~a round per split
+    nk = env_int("LOGRA_PROJ_NK", nk);
+    if (nk != 1 && nk != 2 && nk != 4 && nk != 8) nk = 1;
+    const int rounds_per = (rounds + nk - 1) / nk;
+    pl.cbs_per = 4 * rounds_per;
+    pl.n_k = (pl.ncb + pl.cbs_per - 1) / pl.cbs_per;
+    // the grid must keep each tile's splits on one XCD: n_k a power of two
+    // dividing the per-XCD share (the launch rounds the grid up to 8 * n_k)
+    while (pl.n_k & (pl.n_k - 1)) ++pl.n_k;
+  } else if (pl.small_proj) {
     // More tokens per workgroup amortise the signs; keep >= 256 workgroups.
     int MBW = 4;
     while (MBW > 1 && (MBW * pl.NB > 16 || (T32 + 16 * MBW - 1) / (16 * MBW) < 256)) MBW >>= 1;
@@ -1121,7 +1693,15 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
     const int tile = det ? 1 : env_int("LOGRA_CON_TILE", tall ? 0 : ((pl.NB == 8 || T <= 8192) ? 1 : 0));
     const int big = env_int("LOGRA_CON_BIG", tall ? 1 : -1);
     const bool use_big = big >= 0 ? big != 0 : ((d + bd8 - 1) / bd8) * (nks / 16) >= 256;
-    if (tile) {
+    // Rank 256 on large layers: the one-wave-per-SIMD 256 x 256 tiles.
+    // (With P as a hi/lo pair contract_big_kernel is as fast; the shared-
+    // operand kernel serves the single-bf16 contraction.)
+    const int wide = (!det && pl.NB == 16) ? env_int("LOGRA_CON_WIDE", (hi_only && (tall || use_big)) ? 1 : 0) : 0;
+    if (wide) {
+      pl.cvar = 6;
+      pl.cwide = wide;  // 1: contract_share_kernel (eight waves), 2: contract_wide_kernel (four)
+      BD = 256;
+    } else if (tile) {
       // NB = 8: 2 column groups; NB = 16: 4 column groups; WM row groups.
       const int wn = pl.NB / 4;
       int wm = det ? 1 : env_int("LOGRA_CON_WM", 1);
@@ -1145,7 +1725,11 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
   int64_t n_ts = (384 + pl.n_dt - 1) / pl.n_dt;
   int64_t max_ts = nks / min_steps;
   if (max_ts < 1) max_ts = 1;
-  if (pl.cvar >= 3 && pl.few_ts) {
+  if (pl.cvar == 6) {
+    // One round of one workgroup per CU at most.
+    n_ts = 256 / pl.n_dt;
+    if (n_ts < 1) n_ts = 1;
+  } else if (pl.cvar >= 3 && pl.few_ts) {
     n_ts = 256 / pl.n_dt;  // one round of 256 eight-wave workgroups at most
     if (n_ts < 1) n_ts = 1;
     if (n_ts > 8) n_ts = 8;
@@ -1205,9 +1789,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
     }
   }
 
+  // Split counters (one per token tile) live in a region of their own that
+  // nothing else writes (the kernels leave them at zero); see n_counters.
+  pl.n_counters = pl.n_k > 1 ? pl.n_tt : 0;
   size_t off = 0;
-  pl.off_counters = off;
-  off += align_up((size_t)pl.n_tt * sizeof(unsigned), 256);
   pl.off_phi = off;
   off += align_up((size_t)pl.Tpad * RP * 2, 256);
   pl.off_plo = off;
@@ -1217,7 +1802,8 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
-  pl.use_part = !det && env_int("LOGRA_CON_PART", pl.n_ts >= 3 ? 1 : 0) && pl.n_ts > 1 && (pl.cvar == 3 || pl.cvar == 4);
+  pl.use_part = !det && env_int("LOGRA_CON_PART", (pl.n_ts >= 3 || pl.cvar == 6) ? 1 : 0) && pl.n_ts > 1 &&
+                (pl.cvar == 3 || pl.cvar == 4 || pl.cvar == 6);
   pl.bigdp = env_int("LOGRA_CON_BIGDP", 2) == 1 ? 1 : 2;
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
@@ -1226,6 +1812,15 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det) {
 }
 
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
+  if (pl.pwide) {
+    const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
+    if (pl.NB == 16 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 3>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 8 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 8) hipLaunchKernelGGL((proj_wide_kernel<8, 8>), dim3(grid), dim3(512), 0, s, p);
+    else return false;
+    return true;
+  }
   if (pl.small_proj) {
     const size_t shm = proj_small_lds_bytes(pl.NB, pl.ncb);
 #define LOGRA_PSMALL(nb, mb)                                                                       \
@@ -1296,6 +1891,15 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
     case 4:
       if (pl.bigdp == 2) hipLaunchKernelGGL((contract_big_kernel<16, 2, 2>), dim3(grid), dim3(512), 0, s, p);
       else hipLaunchKernelGGL((contract_big_kernel<16, 2, 1>), dim3(grid), dim3(512), 0, s, p);
+      return true;
+    case 6:
+      if (pl.cwide == 2) {
+        if (p.hi_only) hipLaunchKernelGGL((contract_wide_kernel<1>), dim3(grid), dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((contract_wide_kernel<2>), dim3(grid), dim3(256), 0, s, p);
+      } else {
+        if (p.hi_only) hipLaunchKernelGGL((contract_share_kernel<1>), dim3(grid), dim3(512), 0, s, p);
+        else hipLaunchKernelGGL((contract_share_kernel<2>), dim3(grid), dim3(512), 0, s, p);
+      }
       return true;
     case 5: {
 #define LOGRA_CT(nb, wm, wn)                                                                          \
