@@ -19,7 +19,7 @@ Prints ONE JSON line (rank 0): whole-step tokens/s of the layer, plus
   predicted_kl the predicted-KL reduction over a 2048 x 151,936 probe;
   cpu_baseline the float64 CPU oracle timed on this host on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn1536]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer27b --layer 1]
        python bench.py --sweep    (per-layer table, one JSON line per layer and rank)
 """
 
@@ -229,44 +229,59 @@ def quantiles_us(ts):
 
 def cpu_baseline(w, layer, r, seed, budget_s: float):
     """Time the float64 oracle (as it stands) on host copies of the
-    workload's microbatches: dense G = dY^T X, then the projection."""
+    workload's microbatches: the dense gradient G = dY^T X, then the
+    projection.  On a large layer the oracle forms a seeded subset of the rows
+    of G (rows of S are independent), and the rate is scaled to the whole
+    layer: tokens/s = T * rows / (d * seconds)."""
     import numpy as np
     import torch
 
     import oracle
     import workloads as wl
 
+    blas, threads = "unknown", os.cpu_count() or 1
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            threads = max(p.get("num_threads", 1) for p in info)
+            blas = ",".join(sorted({str(p.get("internal_api")) for p in info}))
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = os.cpu_count() or 1
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     L = w.layers[layer]
     A = oracle.rademacher_projection(seed, r, L.k)
-    S = np.zeros((L.d, r))
+    rows_n = min(L.d, 256)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(L.d, size=rows_n, replace=False)) if rows_n < L.d else None
     host = []
     for m in range(min(w.M, 2)):
         X, dY = wl.layer_inputs(w, layer, m, device="cpu")
         host.append((X.float().numpy().astype(np.float64), dY.float().numpy().astype(np.float64)))
+    S = np.zeros((L.d, r))
     tokens = 0
     t0 = time.perf_counter()
     n = 0
     while True:
         Xh, dYh = host[n % len(host)]
-        S = oracle.sketch_accumulate(S, [Xh], [dYh], A)
+        oracle.sketch_accumulate(S, [Xh], [dYh], A, rows=rows)
         tokens += Xh.shape[0]
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    frac = (rows_n / L.d) if rows is not None else 1.0
     return {
-        "value": tokens / dt,
+        "value": tokens * frac / dt,
         "unit": "tokens/s/layer",
         "cores": int(threads),
+        "affinity_cores": int(affinity),
+        "blas": blas,
         "kind": "oracle",
-        "sample": f"{n} microbatch sketch(es) of {w.T} tokens of the {L.name} {L.d}x{L.k} layer, r={r}: "
-                  f"dense fp64 G = dY^T X then G A^T, {dt:.1f} s of host time",
+        "sample": f"{n} microbatch sketch(es) of {w.T} tokens of the {L.name} {L.d}x{L.k} layer, r={r}, "
+                  f"{'all' if rows is None else rows_n} of {L.d} rows of S: dense fp64 G rows = dY^T X, then G A^T; "
+                  f"{dt:.1f} s of host time, rate scaled to all {L.d} rows",
     }
 
 
@@ -322,17 +337,57 @@ def sweep(steps: int):
                 }), flush=True)
 
 
+def layer_rates(torch, lg, wl, stream, dev, w, li, r, calls, precisions=("bf16x2", "bf16")):
+    """Sketch-call and merge timing of one layer (HBM-resident inputs, enough
+    distinct microbatches to exceed the MALL), per precision mode."""
+    L = w.layers[li]
+    T, d, k = w.T, L.d, L.k
+    ns = max(2, math.ceil(2.5 * MALL_BYTES / (2 * T * (k + d))))
+    ins = [wl.layer_inputs(w, li, m, device=dev) for m in range(ns)]
+    S = torch.zeros((d, r), dtype=torch.float32, device=dev)
+    seed = wl.sign_seed(li)
+    out = {"layer": f"{L.name} d={d} k={k}", "T": T, "r": r}
+    sb = sketch_bytes(T, k, d, r)
+    for prec in precisions:
+        prev = lg.set_precision(PRECISIONS[prec])
+        try:
+            t, _ = gpu_time_per_call(torch, stream, lambda j: lg.sketch_accumulate(ins[j % ns][0], ins[j % ns][1],
+                                                                                     seed, r, S), max(calls, 2 * ns))
+        finally:
+            lg.set_precision(prev)
+        out[f"sketch_{prec}"] = {"us": t * 1e6, "GBps": sb / t / 1e9, "frac": sb / t / 1e9 / HBM_PEAK_GBS,
+                                 "tokens_per_s": T / t}
+    del ins
+    torch.cuda.empty_cache()
+    n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
+    Ws = [wl.layer_weight(w, li, device=dev) for _ in range(n_w)]
+    t, _ = gpu_time_per_call(torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]),
+                             max(calls, 2 * n_w))
+    mb = merge_bytes(d, k, r)
+    out["merge"] = {"us": t * 1e6, "GBps": mb / t / 1e9, "frac": mb / t / 1e9 / HBM_PEAK_GBS}
+    del Ws, S
+    torch.cuda.empty_cache()
+    return out
+
+
+PRECISIONS = {"bf16x2": 0, "bf16": 1}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="attn1536")
-    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="layer27b")
+    ap.add_argument("--layer", type=int, default=1)
     ap.add_argument("--rank", type=int, default=0, help="rank r (default: the workload's first)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--precision", default="bf16x2", choices=sorted(PRECISIONS),
+                    help="contraction precision of the timed step (bf16x2: P as a bf16 high/low pair)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kl", action="store_true", help="skip the predicted-KL probe timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step, sketch call and merge (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -380,14 +435,15 @@ def main():
     T, M, d, k = w.T, w.M, L.d, L.k
     seed = wl.sign_seed(args.layer)
     scale = w.scales[-1]
+    lg.set_precision(PRECISIONS[args.precision])
 
     set_bytes = M * 2 * T * (k + d)
     nsets = max(1, math.ceil(2.5 * MALL_BYTES / set_bytes)) if set_bytes < 2.5 * MALL_BYTES else 1
     sets = []
-    for s in range(nsets):
+    for s_ in range(nsets):
         mbs = []
         for m in range(M):
-            X, dY = wl.layer_inputs(w, args.layer, m + M * s, device=dev)
+            X, dY = wl.layer_inputs(w, args.layer, m + M * s_, device=dev)
             mbs.append((X, dY))
         sets.append(mbs)
     S = torch.zeros((d, r), dtype=torch.float32, device=dev)
@@ -421,12 +477,10 @@ def main():
     # loop is issued twice: once untimed (which also measures how fast the
     # host issues the calls), then behind a sleep kernel long enough for the
     # host to queue the whole loop before the first timed launch, so the
-    # events see GPU time only (one Python call takes several microseconds,
-    # about as long as a small kernel).
+    # events see GPU time only.
     def gpu_time(fn, n):
         return gpu_time_per_call(torch, stream, fn, n)
 
-    # Sketch: M*K back-to-back calls over the same rotating inputs.
     n_calls = args.steps * M
 
     def sketch_call(i):
@@ -434,54 +488,86 @@ def main():
         lg.sketch_accumulate(X, dY, seed, r, S)
 
     t_call, h_call = gpu_time(sketch_call, n_calls)
-    # The layer's M calls of one step, repeated (median, p10, p90 per call).
-    sk_reps = quantiles_us(gpu_time_reps(torch, stream, sketch_call, M, 20))
-    # Merge: over enough copies of W to exceed the MALL (in a step, W was
-    # last touched a whole step earlier).
+    sk_reps = quantiles_us(gpu_time_reps(torch, stream, sketch_call, M, 10))
     n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
     Ws = [W.clone() for _ in range(n_w)]
     n_merges = max(args.steps, 2 * n_w)
     t_merge, h_merge = gpu_time(lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale), n_merges)
     mg_reps = quantiles_us(gpu_time_reps(torch, stream, lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale),
-                                         4, 20))
-
-    # Streaming ceilings measured on this machine for the same bytes, timed the
-    # same way: the sketch call's two input streams read as two launches (X,
-    # then dY) over the same rotating inputs, and as one launch over windows of
-    # one buffer larger than the MALL; the merge's W as an in-place
-    # read-modify-write over the copies.
-    sink = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    def read_two(i):
-        X, dY = sets[(i // M) % nsets][i % M]
-        lg.stream_read(X, sink)
-        lg.stream_read(dY, sink)
-
-    t_read2, _ = gpu_time(read_two, n_calls)
-    win = (2 * T * (k + d) + 15) // 16 * 16
-    n_win = max(4, math.ceil(2.5 * MALL_BYTES / win))
-    buf = torch.zeros(n_win * win, dtype=torch.uint8, device=dev)
-    t_read1, _ = gpu_time(lambda i: lg.stream_read(buf[(i % n_win) * win:(i % n_win + 1) * win], sink), n_calls)
-    del buf
-    t_rmw, _ = gpu_time(lambda i: Ws[i % n_w].mul_(1.0), n_merges)
-    del Ws
-
-    # Split calls: the projection of every microbatch into its own cache (as
-    # at forward time), then the contractions from the caches (backward).
-    caches = [[lg.project(X, seed, r) for X, _ in mbs] for mbs in sets]
-    t_proj, _ = gpu_time(lambda i: lg.project(sets[(i // M) % nsets][i % M][0], seed, r,
-                                              caches[(i // M) % nsets][i % M]), n_calls)
-    t_con, _ = gpu_time(lambda i: lg.contract(sets[(i // M) % nsets][i % M][1], caches[(i // M) % nsets][i % M],
-                                              r, S), n_calls)
-    del caches
-    pb, cb = split_bytes(T, k, d, r)
-    t_ra, h_ra = rowadam_time(torch, lg, stream, S, args.steps)
-    grouped = grouped_merge_timing(torch, lg, wl, stream, dev, max(10, args.steps))
-    kl = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps)) if not args.no_kl else None
+                                         4, 10))
     sb = sketch_bytes(T, k, d, r)
     mb = merge_bytes(d, k, r)
     sk_gbs = sb / t_call / 1e9
     mg_gbs = mb / t_merge / 1e9
+
+    extras = {}
+    if not args.no_extras:
+        # Streaming ceilings measured on this machine for the same bytes, timed
+        # the same way: the sketch call's two input streams read as two
+        # launches, one window of the same size read in a single launch, and
+        # the merge's W as an in-place read-modify-write over the copies.
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def read_two(i):
+            X, dY = sets[(i // M) % nsets][i % M]
+            lg.stream_read(X, sink)
+            lg.stream_read(dY, sink)
+
+        t_read2, _ = gpu_time(read_two, n_calls)
+        t_rmw, _ = gpu_time(lambda i: Ws[i % n_w].mul_(1.0), n_merges)
+        extras["ceiling"] = {
+            "what": "streaming reads/writes of the same bytes on this box (logra_stream_read; torch in-place mul for W)",
+            "sketch_bytes_two_reads_us": t_read2 * 1e6,
+            "sketch_frac_of_two_reads": t_read2 / t_call,
+            "merge_w_rmw_us": t_rmw * 1e6,
+            "merge_frac_of_rmw": t_rmw / t_merge,
+        }
+        # The other precision mode on the same inputs.
+        other = "bf16" if args.precision == "bf16x2" else "bf16x2"
+        prev = lg.set_precision(PRECISIONS[other])
+        try:
+            t_other, _ = gpu_time(sketch_call, n_calls)
+        finally:
+            lg.set_precision(prev)
+        extras["sketch_" + other] = {"avg_call_us": t_other * 1e6, "achieved": sb / t_other / 1e9,
+                                     "frac": sb / t_other / 1e9 / HBM_PEAK_GBS, "tokens_per_s": T / t_other}
+        # Split calls: the projection of every microbatch into its own cache
+        # (forward time), then the contractions from the caches (backward).
+        caches = [[lg.project(X, seed, r) for X, _ in mbs] for mbs in sets]
+        t_proj, _ = gpu_time(lambda i: lg.project(sets[(i // M) % nsets][i % M][0], seed, r,
+                                                  caches[(i // M) % nsets][i % M]), n_calls)
+        t_con, _ = gpu_time(lambda i: lg.contract(sets[(i // M) % nsets][i % M][1], caches[(i // M) % nsets][i % M],
+                                                  r, S), n_calls)
+        del caches
+        pb, cb = split_bytes(T, k, d, r)
+        extras["split"] = {
+            "what": "logra_project (forward, X -> cache: the projection kernel) and logra_contract (backward, dY "
+                    "and cache -> S: the contraction kernels), per call",
+            "project_us": t_proj * 1e6, "project_GBps": pb / t_proj / 1e9, "project_frac": pb / t_proj / 1e9 / HBM_PEAK_GBS,
+            "contract_us": t_con * 1e6, "contract_GBps": cb / t_con / 1e9,
+            "contract_frac": cb / t_con / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": [pb, cb],
+        }
+        t_ra, h_ra = rowadam_time(torch, lg, stream, S, args.steps)
+        extras["rowadam"] = {
+            "kernel": "rowadam_rows_kernel + rowadam_norm_kernel + rowadam_apply_kernel",
+            "avg_us": t_ra * 1e6, "achieved": rowadam_bytes(d, r) / t_ra / 1e9,
+            "frac": rowadam_bytes(d, r) / t_ra / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": rowadam_bytes(d, r),
+            "host_us_per_call": h_ra * 1e6,
+        }
+    del Ws
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        del sets
+        torch.cuda.empty_cache()
+        # The workload's other layers, both precision modes.
+        others = {}
+        for li, Lo in enumerate(w.layers):
+            if li != args.layer:
+                others[Lo.name] = layer_rates(torch, lg, wl, stream, dev, w, li, r, 2 * args.steps)
+        extras["other_layers"] = others
+        extras["grouped_merge"] = grouped_merge_timing(torch, lg, wl, stream, dev, max(10, args.steps))
+        if not args.no_kl:
+            extras["predicted_kl"] = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps))
 
     traffic = load_traffic(args.workload)
     out = {
@@ -505,11 +591,13 @@ def main():
             "microbatches": M,
             "tokens_per_microbatch": T,
             "merge_scale": scale,
+            "precision": args.precision,
             "input_sets_rotated": nsets,
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "sketch_accumulate call (proj_kernel + contract_kernel)",
+            "kernel": "sketch_accumulate call: projection kernel, contraction kernel, and the sum of the "
+                      "contraction's token-split partial tiles (kernel names per layer in the committed trace summary)",
             "bound": "hbm",
             "achieved": sk_gbs,
             "peak": HBM_PEAK_GBS,
@@ -536,39 +624,10 @@ def main():
             "weight_copies_rotated": n_w,
             "per_call_over_repetitions": {"what": "4 merges per repetition", **mg_reps},
         },
-        "ceiling": {
-            "what": "streaming reads/writes of the same bytes on this box (logra_stream_read; torch in-place mul for W)",
-            "sketch_bytes_one_read_us": t_read1 * 1e6,
-            "sketch_bytes_two_reads_us": t_read2 * 1e6,
-            "sketch_frac_of_one_read": t_read1 / t_call,
-            "sketch_frac_of_two_reads": t_read2 / t_call,
-            "merge_w_rmw_us": t_rmw * 1e6,
-            "merge_frac_of_rmw": t_rmw / t_merge,
-        },
-        "rowadam": {
-            "kernel": "rowadam_rows_kernel + rowadam_norm_kernel + rowadam_apply_kernel",
-            "avg_us": t_ra * 1e6,
-            "achieved": rowadam_bytes(d, r) / t_ra / 1e9,
-            "frac": rowadam_bytes(d, r) / t_ra / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": rowadam_bytes(d, r),
-            "host_us_per_call": h_ra * 1e6,
-        },
-        "split": {
-            "what": "logra_project (forward, X -> cache) and logra_contract (backward, dY and cache -> S), per call",
-            "project_us": t_proj * 1e6,
-            "project_GBps": pb / t_proj / 1e9,
-            "project_frac": pb / t_proj / 1e9 / HBM_PEAK_GBS,
-            "contract_us": t_con * 1e6,
-            "contract_GBps": cb / t_con / 1e9,
-            "contract_frac": cb / t_con / 1e9 / HBM_PEAK_GBS,
-            "algorithmic_bytes": [pb, cb],
-        },
-        "grouped_merge": grouped,
-        "predicted_kl": kl,
+        **extras,
         "kernel_source_sha": kernel_source_sha(),
     }
     if not args.no_cpu_baseline:
-        del sets
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, args.layer, r, seed, args.cpu_seconds)
     print(json.dumps(out), flush=True)
