@@ -94,6 +94,38 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx,
                                      hipStream_t stream);
 
 /*
+ * logra_sketch_accumulate for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, validation, settings (precision,
+ * determinism) and result as logra_sketch_accumulate, within the same error
+ * bound.  It calls no hipMalloc or hipFree and no allocating library routine:
+ * its scratch (P as a bf16 hi/lo pair, the projection's column-split partial
+ * sums and their counters) lives in a static device array of
+ * LOGRA_NOALLOC_SCRATCH_BYTES bytes, one copy per GPU, held until the process
+ * ends; token splits of the contraction add into S with atomic adds instead
+ * of parking partial tiles.  The array is found on the first call on each
+ * device (one hipGetSymbolAddress).  A call whose scratch would exceed the
+ * array (roughly T * 16 * 2^ceil(log2(r/16)) * 4 bytes for P, plus the
+ * column-split partials of short microbatches) returns LOGRA_ERR_NOMEM before
+ * enqueuing anything: split the microbatch (the sketch is additive over
+ * tokens) or use logra_sketch_accumulate.
+ *
+ * Every call on a GPU shares that GPU's array and leaves its contents
+ * behind (the split counters are cleared by a kernel at the start of each
+ * call): calls that may overlap on one GPU -- on different streams, or from
+ * different threads without ordering -- race and give wrong results.  Order
+ * them on one stream, or use logra_sketch_accumulate, whose scratch is per
+ * stream.
+ */
+#define LOGRA_NOALLOC_SCRATCH_BYTES (64ull * 1024ull * 1024ull)
+logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx,
+                                             const void* dY, int64_t lddy,
+                                             int64_t T, int64_t k, int64_t d,
+                                             uint64_t seed, int32_t r,
+                                             float* S, int64_t lds,
+                                             hipStream_t stream);
+
+/*
  * Bitwise-reproducible sketches (off by default; a setting of the calling
  * thread).  Atomic adds from several workgroups into the same S entries
  * make S depend on their order at the level of fp32 rounding; any such

@@ -48,10 +48,12 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogra.so")
 MAX_RANK = 256
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # LOGRA_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/logra.h declares.
 EXPORTED_SYMBOLS = (
     "logra_sketch_accumulate",
+    "logra_sketch_accumulate_noalloc",
     "logra_set_deterministic",
     "logra_set_precision",
     "logra_projection_bytes",
@@ -71,6 +73,17 @@ EXPORTED_SYMBOLS = (
     "logra_last_error",
     "logra_abi_version",
 )
+
+
+# Status codes of include/logra.h.
+LOGRA_OK = 0
+LOGRA_ERR_NULL = 1
+LOGRA_ERR_SHAPE = 2
+LOGRA_ERR_ALIGN = 3
+LOGRA_ERR_RANGE = 4
+LOGRA_ERR_ALIAS = 5
+LOGRA_ERR_HIP = 6
+LOGRA_ERR_NOMEM = 7
 
 
 class LograError(RuntimeError):
@@ -99,6 +112,8 @@ def _declare(lib):
     c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
     lib.logra_sketch_accumulate.restype = ctypes.c_int
+    lib.logra_sketch_accumulate_noalloc.argtypes = lib.logra_sketch_accumulate.argtypes
+    lib.logra_sketch_accumulate_noalloc.restype = ctypes.c_int
     lib.logra_set_deterministic.argtypes = [ctypes.c_int]
     lib.logra_set_deterministic.restype = ctypes.c_int
     lib.logra_set_precision.argtypes = [ctypes.c_int]
@@ -205,14 +220,17 @@ def _ld(t) -> int:
     return int(t.stride(0)) if t.size(0) > 1 else max(int(t.stride(0)), int(t.size(1)))
 
 
-def sketch_accumulate(X, dY, seed: int, r: int, S):
+def sketch_accumulate(X, dY, seed: int, r: int, S, noalloc: bool = False):
     """S += (1/sqrt(r)) dY^T (X s^T) on the current stream; returns S.
 
     X: (T, k) bf16, dY: (T, d) bf16, S: (d, r) float32 (updated in place).
+    noalloc: call logra_sketch_accumulate_noalloc (scratch in the library's
+    static device array; calls that overlap on one GPU race).
     """
     import torch
 
     lib = load_library()
+    fn = lib.logra_sketch_accumulate_noalloc if noalloc else lib.logra_sketch_accumulate
     _need(X, torch.bfloat16, "X")
     _need(dY, torch.bfloat16, "dY")
     _need(S, torch.float32, "S")
@@ -223,7 +241,7 @@ def sketch_accumulate(X, dY, seed: int, r: int, S):
     if tuple(S.shape) != (d, r):
         raise ValueError(f"S must be ({d}, {r}), got {tuple(S.shape)}")
     _check(
-        lib.logra_sketch_accumulate(
+        fn(
             X.data_ptr(), _ld(X), dY.data_ptr(), _ld(dY), T, k, d,
             ctypes.c_uint64(seed & (2**64 - 1)), r, S.data_ptr(), _ld(S), _stream_handle(S),
         )

@@ -181,9 +181,11 @@ logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t ld
 // projection writes no low plane when the contraction reads none (the
 // single-bf16 tiling), or a zero one otherwise.  The split call always
 // writes both planes.
+// counters: the split counters (zero, n_counters of them), or null to take
+// them from the library's per-stream region.
 logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X, int64_t ldx, int64_t T, int64_t k,
                                 uint64_t seed, int r, uint16_t* Phi, uint16_t* Plo, bool hi_only,
-                                hipStream_t stream) {
+                                hipStream_t stream, unsigned* counters = nullptr) {
   ProjParams pp{};
   pp.X = static_cast<const uint16_t*>(X);
   pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
@@ -193,8 +195,12 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
   pp.Ppart = reinterpret_cast<float*>(base + pl.off_part);
   pp.part_stride = pl.Tpad * 16 * pl.NB;
   if (pl.n_k > 1) {
-    logra_status st = counters_get(stream, pl.n_counters, &pp.counters);
-    if (st != LOGRA_OK) return st;
+    if (counters) {
+      pp.counters = counters;
+    } else {
+      logra_status st = counters_get(stream, pl.n_counters, &pp.counters);
+      if (st != LOGRA_OK) return st;
+    }
   }
   pp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
   if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
@@ -269,26 +275,122 @@ logra_status prepare_merge(void* W, int64_t ldw, const float* U, int64_t ldu, in
   return LOGRA_OK;
 }
 
+// Argument checks of the fused sketch calls; *empty: nothing to do.
+logra_status check_sketch_args(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T, int64_t k,
+                               int64_t d, int32_t r, const float* S, int64_t lds, bool* empty) {
+  *empty = false;
+  if (T < 0 || k < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T, k and d must be >= 0");
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
+  if (T == 0 || k == 0 || d == 0) {
+    *empty = true;
+    return LOGRA_OK;
+  }
+  if (!X || !dY || !S) return fail(LOGRA_ERR_NULL, "X, dY and S must be non-null");
+  logra_status st = check_x(X, ldx, T, k);
+  if (st != LOGRA_OK) return st;
+  st = check_dy_s(dY, lddy, T, d, S, lds, r);
+  if (st != LOGRA_OK) return st;
+  if (overlaps(S, span_bytes(d, r, lds, 4), X, span_bytes(T, k, ldx, 2)))
+    return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
+  return LOGRA_OK;
+}
+
+}  // namespace
+
+// Scratch of logra_sketch_accumulate_noalloc: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol): it uses the device address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[LOGRA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per
+// device).
+logra_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LOGRA_ERR_RANGE, "device ordinal above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LOGRA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOGRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T,
+                                             int64_t k, int64_t d, uint64_t seed, int32_t r, float* S, int64_t lds,
+                                             hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    bool empty = false;
+    logra_status st = check_sketch_args(X, ldx, dY, lddy, T, k, d, r, S, lds, &empty);
+    if (st != LOGRA_OK || empty) return st;
+    // The plan of logra_sketch_accumulate, except that token splits of the
+    // contraction add into S directly instead of parking partial tiles (the
+    // scratch then holds P, the projection's column-split partials and the
+    // split counters only).  Worked out afresh (no plan cache: nothing is
+    // allocated on the host either).
+    SketchPlan pl = plan_sketch(T, k, d, r, g_deterministic, g_precision_hi_only);
+    pl.use_part = 0;
+    st = check_plan(pl, T, ldx, lddy);
+    if (st != LOGRA_OK) return st;
+    const size_t off_cnt = (pl.off_cpart + 255) / 256 * 256;
+    const size_t cnt_bytes = (size_t)(pl.n_k > 1 ? pl.n_counters : 0) * sizeof(unsigned);
+    const size_t cnt_span = (cnt_bytes + 15) / 16 * 16;
+    const size_t need = off_cnt + cnt_span;
+    if (need > (size_t)LOGRA_NOALLOC_SCRATCH_BYTES)
+      return fail(LOGRA_ERR_NOMEM, "this call needs " + std::to_string(need) +
+                                       " bytes of scratch, more than the static " +
+                                       std::to_string((size_t)LOGRA_NOALLOC_SCRATCH_BYTES) +
+                                       " bytes: split the microbatch or use logra_sketch_accumulate");
+    void* ptr = nullptr;
+    st = noalloc_scratch(&ptr);
+    if (st != LOGRA_OK) return st;
+    char* base = static_cast<char*>(ptr);
+    unsigned* counters = nullptr;
+    if (cnt_span) {
+      // The last call may have left anything here: clear the counters with
+      // a kernel (capturable, unlike a memset node).
+      counters = reinterpret_cast<unsigned*>(base + off_cnt);
+      zero_fill_launch(counters, (int64_t)(cnt_span / 16), stream);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+    }
+    uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
+    uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
+    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, g_precision_hi_only, stream, counters);
+    if (st != LOGRA_OK) return st;
+    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, g_precision_hi_only, stream);
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
 
 logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T, int64_t k,
                                      int64_t d, uint64_t seed, int32_t r, float* S, int64_t lds,
                                      hipStream_t stream) {
   try {
     g_last_error.clear();
-    if (T < 0 || k < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T, k and d must be >= 0");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
-    if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
-    if (T == 0 || k == 0 || d == 0) return LOGRA_OK;
-    if (!X || !dY || !S) return fail(LOGRA_ERR_NULL, "X, dY and S must be non-null");
-    logra_status st = check_x(X, ldx, T, k);
-    if (st != LOGRA_OK) return st;
-    st = check_dy_s(dY, lddy, T, d, S, lds, r);
-    if (st != LOGRA_OK) return st;
-    if (overlaps(S, span_bytes(d, r, lds, 4), X, span_bytes(T, k, ldx, 2)))
-      return fail(LOGRA_ERR_ALIAS, "S overlaps X or dY");
+    bool empty = false;
+    logra_status st = check_sketch_args(X, ldx, dY, lddy, T, k, d, r, S, lds, &empty);
+    if (st != LOGRA_OK || empty) return st;
 
     const SketchPlan pl = sketch_plan_for(T, k, d, r, g_precision_hi_only);
     st = check_plan(pl, T, ldx, lddy);
