@@ -32,6 +32,7 @@ from .logra_oracle import (  # noqa: F401
     rowadam_scale,
     reconstruction_cosine,
     sketch_accumulate_rounded_projection,
+    sketch_projected_first,
 )
 from .predicted_kl import (  # noqa: F401
     token_probabilities,

@@ -267,6 +267,25 @@ def reconstruction_cosine(G, A) -> float:
     return float((G * Gh).sum() / (np.linalg.norm(G) * np.linalg.norm(Gh)))
 
 
+def sketch_projected_first(S0, X_list, dY_list, A, rows=None) -> np.ndarray:
+    """S = S0 + sum_m dY_m^T (X_m A^T): equation 2 with the layer inputs
+    projected before the backward derivatives multiply them (LoGRA section
+    2.1, the paragraph after equation 2), in float64.  The same quantity as
+    ``sketch_accumulate`` with the products associated the other way; it
+    never forms the d x k gradient, so whole large layers stay cheap.
+    ``rows`` restricts the result to a subset of the d rows."""
+    A = np.asarray(A, dtype=np.float64)
+    S0 = np.asarray(S0, dtype=np.float64)
+    S = (S0[rows] if rows is not None else S0).copy()
+    for X, dY in zip(X_list, dY_list):
+        P = project_inputs(X, A)
+        dY = np.asarray(dY, dtype=np.float64)
+        if rows is not None:
+            dY = dY[:, rows]
+        S += dY.T @ P
+    return S
+
+
 def sketch_accumulate_rounded_projection(S0, X_list, dY_list, seed: int, r: int, rows=None) -> np.ndarray:
     """S = S0 + (1/sqrt(r)) sum_m dY_m^T RNE_bf16(X_m s^T): the sketch with the
     projected inputs rounded once to bf16 before the backward multiply.

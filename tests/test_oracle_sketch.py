@@ -11,7 +11,10 @@ What ties the oracle to the pages and to mathematics rather than to itself:
   * the accumulator-size arithmetic the paper prints (section 2.2);
   * the projection-first path dY^T (X A^T) (section 2.1, after equation 2)
     equals the dense-gradient path, and projecting a unit row returns the
-    matching column of A.
+    matching column of A;
+  * the variant with P rounded once to bf16 equals the exact sketch when P is
+    exact in bf16, follows explicit loops over a pinned rounding, and drops
+    exactly the part of P below half a bf16 spacing.
 """
 
 import json
@@ -27,8 +30,12 @@ from oracle import (
     project_inputs,
     rademacher_projection,
     reconstruction_cosine,
+    round_to_bf16,
+    sign_matrix,
     sketch_accumulate,
+    sketch_accumulate_rounded_projection,
     sketch_from_gradient,
+    sketch_projected_first,
 )
 
 GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
@@ -202,3 +209,79 @@ def test_projection_of_unit_rows_is_columns_of_A():
     np.testing.assert_allclose(project_inputs(2.0 * Y - X[:4], A), 2.0 * project_inputs(Y, A) - P[:4], atol=1e-12)
     # every entry of A has magnitude 1/sqrt(r), so |P[t, c]| <= sum_j |X[t, j]| / sqrt(r)
     assert np.all(np.abs(project_inputs(Y, A)) <= np.abs(Y).sum(axis=1, keepdims=True) / math.sqrt(r) + 1e-12)
+
+
+def test_projected_first_oracle_matches_definition():
+    # sketch_projected_first (never forms G) against the dense-gradient
+    # definition, with an incoming S0 and a row subset, and against explicit
+    # loops of equation 2 on a tiny case.
+    M, T, d, k, r = 3, 41, 13, 300, 24
+    Xs, dYs = _tiny(17, M, T, d, k)
+    A = rademacher_projection(9, r, k)
+    S0 = np.random.default_rng(3).standard_normal((d, r))
+    np.testing.assert_allclose(sketch_projected_first(S0, Xs, dYs, A), sketch_accumulate(S0, Xs, dYs, A),
+                               rtol=1e-12, atol=1e-10)
+    rows = np.array([0, 5, 12])
+    np.testing.assert_allclose(sketch_projected_first(S0, Xs, dYs, A, rows=rows),
+                               sketch_accumulate(S0, Xs, dYs, A)[rows], rtol=1e-12, atol=1e-10)
+    Xs, dYs = _tiny(4, 2, 5, 3, 7)
+    A = rademacher_projection(2, 4, 7)
+    want = np.zeros((3, 4))
+    for X, dY in zip(Xs, dYs):
+        for i in range(3):
+            for c in range(4):
+                want[i, c] += sum(dY[t, i] * X[t, j] * A[c, j] for t in range(5) for j in range(7))
+    np.testing.assert_allclose(sketch_projected_first(np.zeros((3, 4)), Xs, dYs, A), want, rtol=1e-12, atol=1e-12)
+
+
+def test_rounded_projection_exact_when_p_is_bf16():
+    # X in {-1, 0, 1} and k <= 256: every entry of X s^T is an integer of
+    # magnitude <= 256, exact in bf16, so rounding changes nothing.
+    rng = np.random.default_rng(8)
+    T, d, k, r, seed = 33, 9, 200, 16, 5
+    Xs = [rng.integers(-1, 2, size=(T, k)).astype(np.float64) for _ in range(2)]
+    dYs = [rng.standard_normal((T, d)) for _ in range(2)]
+    S0 = rng.standard_normal((d, r))
+    np.testing.assert_allclose(sketch_accumulate_rounded_projection(S0, Xs, dYs, seed, r),
+                               sketch_accumulate(S0, Xs, dYs, rademacher_projection(seed, r, k)),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_rounded_projection_follows_loops_over_pinned_rounding():
+    # Explicit loops: P[t, c] = sum_j X[t, j] s[c, j], rounded element by
+    # element with round_to_bf16 (itself pinned against torch), then
+    # S[i, c] = S0[i, c] + sum_t dY[t, i] P[t, c] / sqrt(r).
+    rng = np.random.default_rng(12)
+    T, d, k, r, seed = 6, 4, 9, 5, 77
+    X = rng.standard_normal((T, k))
+    dY = rng.standard_normal((T, d))
+    S0 = rng.standard_normal((d, r))
+    s = sign_matrix(seed, r, k).astype(np.float64)
+    P = np.zeros((T, r))
+    for t in range(T):
+        for c in range(r):
+            P[t, c] = float(round_to_bf16(np.array([sum(X[t, j] * s[c, j] for j in range(k))]))[0])
+    want = S0.copy()
+    for i in range(d):
+        for c in range(r):
+            want[i, c] += sum(dY[t, i] * P[t, c] for t in range(T)) / math.sqrt(r)
+    got = sketch_accumulate_rounded_projection(S0, [X], [dY], seed, r)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+    # Row subset.
+    np.testing.assert_allclose(sketch_accumulate_rounded_projection(S0, [X], [dY], seed, r, rows=np.array([1, 3])),
+                               want[[1, 3]], rtol=1e-13, atol=1e-13)
+
+
+def test_rounded_projection_drops_below_half_spacing():
+    # X = [1, 2^-9]: P[c] = s[c,0] + s[c,1] 2^-9 is within half a bf16 spacing
+    # of s[c,0] (above 1 the spacing is 2^-7; below 1 it is 2^-8 and
+    # 1 - 2^-9 is a tie that goes to the even neighbour, 1), so the rounded
+    # P is exactly s[:, 0] and S = s[:, 0] / sqrt(r) for dY = 1.
+    r, seed = 16, 3
+    X = np.array([[1.0, 2.0**-9]])
+    dY = np.array([[1.0]])
+    s = sign_matrix(seed, r, 2).astype(np.float64)
+    got = sketch_accumulate_rounded_projection(np.zeros((1, r)), [X], [dY], seed, r)
+    np.testing.assert_array_equal(got[0], s[:, 0] / math.sqrt(r))
+    exact = sketch_accumulate(np.zeros((1, r)), [X], [dY], rademacher_projection(seed, r, 2))
+    assert np.abs(exact[0] - got[0]).max() == pytest.approx(2.0**-9 / math.sqrt(r))
