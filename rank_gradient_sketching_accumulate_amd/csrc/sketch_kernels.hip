@@ -431,7 +431,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
   constexpr int NGEN = RP * WK / 512;   // Philox blocks per thread and round
   static_assert(NGEN * 512 == RP * WK, "one or two sign blocks per thread");
-  static_assert(NX >= 2 && NX <= 8, "ring depth");
+  // A block's eight steps use ring slots s % NX, and the loads issued in its
+  // last NX - 1 steps belong to the next block's first steps: NX must divide
+  // 8 for both to name the same slots.
+  static_assert(NX >= 2 && 8 % NX == 0, "ring depth divides a block's eight steps");
   static_assert(MT == 4, "one asm block of four MFMAs per column block");
   __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
   __shared__ int s_last;
@@ -1579,7 +1582,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   // the whole k range's signs fit in 64 KB of LDS.
   pl.pwide = (pl.NB >= 8 && pl.ncb >= 2) ? 1 : 0;
   pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 8 ? 1 : 0;
-  pl.pnx = env_int("LOGRA_PROJ_NX", 4) == 3 ? 3 : (env_int("LOGRA_PROJ_NX", 4) == 8 ? 8 : 4);
+  pl.pnx = (pl.NB == 8 && env_int("LOGRA_PROJ_NX", 4) == 8) ? 8 : 4;
   pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
   pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
@@ -1814,8 +1817,7 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   if (pl.pwide) {
     const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
-    if (pl.NB == 16 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
-    else if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 3>), dim3(grid), dim3(512), 0, s, p);
+    if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 8 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 8) hipLaunchKernelGGL((proj_wide_kernel<8, 8>), dim3(grid), dim3(512), 0, s, p);
     else return false;

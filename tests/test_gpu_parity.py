@@ -213,11 +213,42 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_BANDS": 4},
     {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 24},
     {"LOGRA_CON_BANDS": 4, "LOGRA_CON_GRID": 12},
+    {"LOGRA_PROJ_NX": 8},
+    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_NK": 2},
 ]
 
 
 def _plan_id(e):
     return ",".join(f"{k[6:]}={v}" for k, v in e.items()) or "default"
+
+
+# Knobs of proj_kernel's tiling (waves along k, token blocks per wave, waves
+# per workgroup); proj_wide_kernel has a fixed tiling.
+PROJ_KERNEL_KNOBS = ("LOGRA_PROJ_MB", "LOGRA_PROJ_WK", "LOGRA_PROJ_NW")
+
+# Tilings reachable at ranks 129-256 (NB = 16): the eight-wave projection
+# (column splits NK), the four- and eight-wave proj_kernel
+# (the latter with two token rows per workgroup), and the contraction's
+# 256 x 256 tiles (one or two steps of prefetch), the one-wave-per-SIMD and
+# shared-operand kernels, and the token-lane tiles.
+R256_PLANS = [
+    {},
+    {"LOGRA_PROJ_NK": 1},
+    {"LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_NK": 4},
+    {"LOGRA_PROJ_NK": 3},
+    {"LOGRA_PROJ_WIDE": 0},
+    {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 4},
+    {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_WK": 1, "LOGRA_PROJ_MB": 1},
+    {"LOGRA_CON_WIDE": 1},
+    {"LOGRA_CON_WIDE": 2},
+    {"LOGRA_CON_WIDE": 1, "LOGRA_CON_TS": 1},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_BIGDP": 1},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_TS": 2, "LOGRA_CON_PART": 0},
+    {"LOGRA_CON_TILE": 1},
+    {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2},
+]
 
 
 def test_sketch_consecutive_calls_changing_shapes():
@@ -252,8 +283,11 @@ def test_sketch_launch_plans(r, env, monkeypatch):
     contraction) gives the oracle's sketch."""
     if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
         env = dict(env, LOGRA_PROJ_SMALL=0)  # rank 256 always takes the round-based projection
-    if r == 256 and env.get("LOGRA_PROJ_WK", 1) != 1:
-        pytest.skip("rank 256 runs with one wave column along k")
+    if r >= 128 and any(k_ in env for k_ in PROJ_KERNEL_KNOBS):
+        # ranks above 64 with two or more 256-column blocks take
+        # proj_wide_kernel, whose tiling these knobs do not set: run them on
+        # proj_kernel
+        env = dict(env, LOGRA_PROJ_WIDE=0)
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, str(v_))
     T, k, d = 700, 1300, 300
@@ -263,6 +297,27 @@ def test_sketch_launch_plans(r, env, monkeypatch):
     lg.sketch_accumulate(X, dY, 11, r, S)
     ref = _oracle_sketch(torch.zeros((d, r)), [X], [dY], 11, r, k)
     assert_sketch_close(f64(S), ref)
+
+
+@pytest.mark.parametrize("T,k,d,r", [(700, 1300, 300, 256), (1500, 700, 900, 200), (4096, 5120, 600, 256)])
+@pytest.mark.parametrize("env", R256_PLANS, ids=_plan_id)
+def test_sketch_rank256_plans(T, k, d, r, env, monkeypatch):
+    """Every rank-256 tiling, including k = 700 (three 256-column blocks: two
+    waves along k in proj_kernel) and rank 200 (padded to 256 columns), gives
+    the oracle's sketch over two microbatches."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    _say("r256 plans", T, k, d, r, env)
+    seed = 60 + r
+    X, dY = _ragged_inputs(T, k, d, 4545)
+    X2, dY2 = _ragged_inputs(T, k, d, 4547)
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    lg.sketch_accumulate(X, dY, seed, r, S)
+    lg.sketch_accumulate(X2, dY2, seed, r, S)
+    rows = None if d <= 300 else np.arange(0, d, 7)
+    ref = _oracle_sketch(torch.zeros((d, r)), [X, X2], [dY, dY2], seed, r, k, rows=rows)
+    got = f64(S) if rows is None else f64(S)[rows]
+    assert_sketch_close(got, ref)
 
 
 @pytest.mark.parametrize("T,k,d,r", [(700, 1300, 300, 16), (4096, 1536, 1536, 64), (1000, 700, 900, 128),

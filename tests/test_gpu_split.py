@@ -15,7 +15,7 @@ import pytest
 import oracle
 import workloads as wl
 from tests._util import assert_sketch_close, f64, padded_ld, rel_frob
-from tests.test_gpu_parity import PLAN_OVERRIDES, _plan_id
+from tests.test_gpu_parity import PLAN_OVERRIDES, PROJ_KERNEL_KNOBS, R256_PLANS, _plan_id
 
 torch = pytest.importorskip("torch")
 lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
@@ -192,8 +192,11 @@ def test_split_launch_plans(r, env, monkeypatch):
     and a correct cache."""
     if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
         env = dict(env, LOGRA_PROJ_SMALL=0)
-    if r == 256 and env.get("LOGRA_PROJ_WK", 1) != 1:
-        pytest.skip("rank 256 runs with one wave column along k")
+    if r >= 128 and any(k_ in env for k_ in PROJ_KERNEL_KNOBS):
+        # ranks above 64 with two or more 256-column blocks take
+        # proj_wide_kernel, whose tiling these knobs do not set: run them on
+        # proj_kernel
+        env = dict(env, LOGRA_PROJ_WIDE=0)
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, str(v_))
     T, k, d = 700, 1300, 300
@@ -208,3 +211,25 @@ def test_split_launch_plans(r, env, monkeypatch):
     lg.contract(dY, P, r, S)
     ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(12, r, k))
     assert_sketch_close(f64(S), ref)
+
+
+@pytest.mark.parametrize("T,k,d,r", [(700, 1300, 300, 256), (1500, 700, 900, 200)])
+@pytest.mark.parametrize("env", R256_PLANS, ids=_plan_id)
+def test_split_rank256_plans(T, k, d, r, env, monkeypatch):
+    """The split calls under every rank-256 tiling: the cache matches the
+    oracle's projection and the contraction the oracle's sketch."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    _say("split r256 plans", T, k, d, r, env)
+    X, dY = _inputs(T, k, d, 4646)
+    P = lg.project(X, 13, r)
+    got, pad = decode_cache(P, T, r)
+    ref_p = oracle.project_inputs(f64(X), oracle.rademacher_projection(13, r, k)) * math.sqrt(r)
+    assert rel_frob(got, ref_p) <= 2e-5
+    np.testing.assert_array_equal(pad, np.zeros_like(pad))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    lg.contract(dY, P, r, S)
+    rows = None if d <= 300 else np.arange(0, d, 7)
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(13, r, k),
+                                   rows=rows)
+    assert_sketch_close(f64(S) if rows is None else f64(S)[rows], ref)
