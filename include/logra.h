@@ -22,7 +22,11 @@
  *   - Validation runs before anything is enqueued; on any error nothing is
  *     written and a nonzero status is returned.  logra_last_error() then gives
  *     a thread-local description.  No C++ exception crosses this boundary.
- *   - 1 <= r <= LOGRA_MAX_RANK.
+ *   - 1 <= r <= LOGRA_MAX_RANK (512).  The paper asks only r << min(d, k)
+ *     (section 2.1).  Ranks above 256 run as two column halves: sign rows
+ *     0..255 into columns 0..255 and rows 256..r-1 into columns 256..r-1 (a
+ *     sign depends only on seed, row and column), so they cost one more pass
+ *     over X per sketch call.
  *   - NaN and Inf in the inputs propagate to the outputs; nothing traps.
  *
  * Sign generator (this library's fixed choice; the paper only requires
@@ -44,8 +48,8 @@
 extern "C" {
 #endif
 
-#define LOGRA_ABI_VERSION 1
-#define LOGRA_MAX_RANK 256
+#define LOGRA_ABI_VERSION 2
+#define LOGRA_MAX_RANK 512
 
 typedef enum {
   LOGRA_OK = 0,
@@ -80,9 +84,9 @@ typedef enum {
  *   calls: the sketch is additive over tokens).
  *
  * Internal scratch (the projected inputs P = X s^T, T x r) is held by the
- * library per (device, stream) and grown on first use of a larger size;
- * concurrent calls on different streams are safe, calls that update the same S
- * must be ordered by the caller.  The result is not bitwise reproducible
+ * library per (device, stream) and grown on first use of a larger size (see
+ * logra_workspace_reserve); concurrent calls on different streams are safe,
+ * calls that update the same S must be ordered by the caller.  The result is not bitwise reproducible
  * across runs when the token range is split over several workgroups (fp32
  * atomic adds); any order is within the stated error bound.
  */
@@ -152,8 +156,9 @@ int logra_set_deterministic(int enable);
  *     P traffic.  S then carries the error of that one rounding, about
  *     1.6e-3 relative (Frobenius) on iid data.
  *
- * Applies to logra_sketch_accumulate and logra_contract; logra_project
- * always writes both planes, so a projection cache serves either mode.
+ * Applies to logra_sketch_accumulate and logra_sketch_accumulate_noalloc.
+ * The split calls always use both planes: logra_project writes them and
+ * logra_contract reads them.
  */
 #define LOGRA_PRECISION_BF16X2 0
 #define LOGRA_PRECISION_BF16 1
@@ -174,10 +179,13 @@ int logra_set_precision(int mode);
  * 4 * roundup(T, 256) * R bytes against 2 * T * k.
  *
  * The projection cache P is a caller-owned device buffer of at least
- * logra_projection_bytes(T, r) bytes, 16-byte aligned.  Its layout: R = 16 *
- * (the smallest power of two >= ceil(r / 16)) columns, Tc = roundup(T, 256)
- * tokens; a plane of bf16 high parts at byte 0 and a plane of bf16 low parts
- * at byte 2 * Tc * R, each Tc * R entries; entry (t, c) of a plane sits at
+ * logra_projection_bytes(T, r) bytes, 16-byte aligned.  Its layout for
+ * r <= 256: R = 16 * (the smallest power of two >= ceil(r / 16)) columns,
+ * Tc = roundup(T, 256) tokens; a plane of bf16 high parts at byte 0 and a
+ * plane of bf16 low parts at byte 2 * Tc * R, each Tc * R entries.  For
+ * r > 256 two such caches follow each other: columns 0..255 (R = 256) at
+ * byte 0, then columns 256..r-1 as a cache of rank r - 256 at byte
+ * 4 * Tc * 256.  Within a plane entry (t, c) sits at
  * index ((((t / 32) * (R / 16) + c / 16) * 64 + ((t % 32) / 8) * 16 + c % 16) * 8
  * + t % 8), the order in which the contraction feeds its matrix cores.  For
  * t < T and c < r, high + low equals P[t][c] = sum_j X[t][j] s[c][j] to about
@@ -357,12 +365,37 @@ logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out,
  * multiple of 16 (LOGRA_ERR_ALIGN otherwise); bytes == 0 is a no-op. */
 logra_status logra_stream_read(const void* ptr, size_t bytes, uint32_t* sink, hipStream_t stream);
 
-/* Upper bound on the per-stream scratch logra_sketch_accumulate allocates for
- * T tokens at rank r, over layer shapes up to 2^20 x 2^20 (P as a bf16 hi/lo
- * pair, column-split and token-split partial sums, per-tile counters).  It
- * also bounds the scratch of logra_project and logra_contract, which keep
- * the same partial sums but not P. */
-size_t logra_workspace_bytes(int64_t T, int32_t r);
+/*
+ * Library scratch per (device, stream).  logra_sketch_accumulate, the split
+ * calls and logra_rowadam_scale take scratch (P as a bf16 hi/lo pair,
+ * column- and token-split partial sums, split counters, RowAdam's row
+ * statistics) from regions the library keeps per (device, stream).  A region
+ * grows, by hipMalloc and a clearing hipMemsetAsync on the stream, the first
+ * time a call needs more than it holds, and never shrinks; a buffer it
+ * outgrows is retired, not freed, because a graph captured earlier may still
+ * launch kernels that use it.  Growing is refused with LOGRA_ERR_NOMEM while
+ * the stream is being captured (allocation cannot be captured): reserve
+ * before capturing.
+ *
+ * logra_workspace_bytes: the scratch, in bytes, that the sketch calls (fused
+ * and split) and logra_rowadam_scale need for one shape with the calling
+ * thread's settings (precision, determinism); 0 for an empty or invalid
+ * shape.  logra_predicted_kl's scratch is not included.
+ *
+ * logra_workspace_reserve: grows the stream's regions to that size now (on
+ * the current device).  After it, calls of that shape, or smaller ones whose
+ * plans fit, on that stream allocate nothing and may be captured into a graph.
+ * Errors: LOGRA_ERR_SHAPE / LOGRA_ERR_RANGE for bad arguments,
+ * LOGRA_ERR_NOMEM when the allocation fails or the stream is being captured.
+ *
+ * logra_workspace_release: waits for the stream's queued work, then frees
+ * every region the library holds for the stream on the current device,
+ * current and retired.  A graph captured before must not be launched after
+ * it.  Refused (LOGRA_ERR_RANGE) while the stream is being captured.
+ */
+size_t logra_workspace_bytes(int64_t T, int64_t d, int64_t k, int32_t r);
+logra_status logra_workspace_reserve(int64_t T, int64_t d, int64_t k, int32_t r, hipStream_t stream);
+logra_status logra_workspace_release(hipStream_t stream);
 
 /* Static text for a status code. */
 const char* logra_status_string(logra_status s);

@@ -41,13 +41,16 @@ __all__ = [
     "kl_effective_budget",
     "signs",
     "workspace_bytes",
+    "workspace_reserve",
+    "workspace_release",
     "stream_read",
     "abi_version",
     "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblogra.so")
-MAX_RANK = 256
+MAX_RANK = 512
+ABI_VERSION = 2  # LOGRA_ABI_VERSION this binding is written for
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # LOGRA_NOALLOC_SCRATCH_BYTES
 
 # Every symbol include/logra.h declares.
@@ -69,6 +72,8 @@ EXPORTED_SYMBOLS = (
     "logra_signs",
     "logra_stream_read",
     "logra_workspace_bytes",
+    "logra_workspace_reserve",
+    "logra_workspace_release",
     "logra_status_string",
     "logra_last_error",
     "logra_abi_version",
@@ -143,8 +148,12 @@ def _declare(lib):
     lib.logra_signs.restype = ctypes.c_int
     lib.logra_stream_read.argtypes = [c_vp, ctypes.c_size_t, c_vp, c_vp]
     lib.logra_stream_read.restype = ctypes.c_int
-    lib.logra_workspace_bytes.argtypes = [c_i64, c_i32]
+    lib.logra_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32]
     lib.logra_workspace_bytes.restype = ctypes.c_size_t
+    lib.logra_workspace_reserve.argtypes = [c_i64, c_i64, c_i64, c_i32, c_vp]
+    lib.logra_workspace_reserve.restype = ctypes.c_int
+    lib.logra_workspace_release.argtypes = [c_vp]
+    lib.logra_workspace_release.restype = ctypes.c_int
     lib.logra_status_string.argtypes = [ctypes.c_int]
     lib.logra_status_string.restype = ctypes.c_char_p
     lib.logra_last_error.argtypes = []
@@ -166,6 +175,9 @@ def load_library(path: str | None = None):
         )
     lib = ctypes.CDLL(p)
     _declare(lib)
+    got = lib.logra_abi_version()
+    if got != ABI_VERSION:
+        raise LograError(f"{p} has ABI version {got}, this binding needs {ABI_VERSION}: rebuild the library")
     _lib = lib
     return lib
 
@@ -183,6 +195,18 @@ def _check(status: int):
 
 
 _raw_stream = None
+
+
+def _stream_or_current(stream) -> int:
+    """Raw handle of a torch stream (or an int handle), or of torch's current
+    stream on the current device when None."""
+    import torch
+
+    if stream is None:
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
 
 
 def _stream_handle(tensor) -> int:
@@ -458,8 +482,23 @@ def stream_read(t, sink):
                                             _stream_handle(t)))
 
 
-def workspace_bytes(T: int, r: int) -> int:
-    return int(load_library().logra_workspace_bytes(T, r))
+def workspace_bytes(T: int, d: int, k: int, r: int) -> int:
+    """Scratch bytes the sketch calls and RowAdam need for this shape (the
+    calling thread's precision and determinism settings)."""
+    return int(load_library().logra_workspace_bytes(T, d, k, r))
+
+
+def workspace_reserve(T: int, d: int, k: int, r: int, stream=None) -> None:
+    """Grow the library's scratch for `stream` (default: the current torch
+    stream) to fit this shape, so later calls allocate nothing (for example
+    under graph capture)."""
+    _check(load_library().logra_workspace_reserve(T, d, k, r, _stream_or_current(stream)))
+
+
+def workspace_release(stream=None) -> None:
+    """Wait for `stream` and free every scratch buffer the library holds for
+    it (graphs captured before must not be replayed afterwards)."""
+    _check(load_library().logra_workspace_release(_stream_or_current(stream)))
 
 
 def abi_version() -> int:

@@ -183,12 +183,14 @@ logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t ld
 // writes both planes.
 // counters: the split counters (zero, n_counters of them), or null to take
 // them from the library's per-stream region.
+// row0: the sign row of P's first column (256 for the upper half of a rank
+// above 256).
 logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X, int64_t ldx, int64_t T, int64_t k,
-                                uint64_t seed, int r, uint16_t* Phi, uint16_t* Plo, bool hi_only,
+                                uint64_t seed, int r, int row0, uint16_t* Phi, uint16_t* Plo, bool hi_only,
                                 hipStream_t stream, unsigned* counters = nullptr) {
   ProjParams pp{};
   pp.X = static_cast<const uint16_t*>(X);
-  pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r;
+  pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r; pp.row0 = row0;
   pp.n_tt = pl.n_tt; pp.n_k = pl.n_k; pp.cbs_per = pl.cbs_per; pp.ncb = pl.ncb;
   pp.Phi = Phi;
   pp.Plo = Plo;
@@ -210,15 +212,17 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
 }
 
 // S += (1/sqrt r) dY^T P from the hi/lo planes.
+// r: the columns of S this contraction adds into; r_full: the rank whose
+// 1/sqrt scales them (r_full > r for the halves of a rank above 256).
 logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* dY, int64_t lddy, int64_t T, int64_t d,
-                                 const uint16_t* Phi, const uint16_t* Plo, int r, float* S, int64_t lds, bool hi_only,
-                                 hipStream_t stream) {
+                                 const uint16_t* Phi, const uint16_t* Plo, int r, int r_full, float* S, int64_t lds,
+                                 bool hi_only, hipStream_t stream) {
   ContractParams cp{};
   cp.dY = static_cast<const uint16_t*>(dY);
   cp.lddy = lddy; cp.T = T; cp.d = d;
   cp.Phi = Phi; cp.Plo = Plo; cp.NB = pl.NB;
   cp.S = S; cp.lds = lds; cp.r = r;
-  cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r));
+  cp.inv_sqrt_r = (float)(1.0 / sqrt((double)r_full));
   cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
   cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
   cp.bands = pl.cbands;
@@ -244,7 +248,7 @@ logra_status prepare_merge(void* W, int64_t ldw, const float* U, int64_t ldu, in
                            int32_t r, float scale, MergeParams& mp, MergePlan& pl, bool& skip) {
   skip = false;
   if (d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "d and k must be >= 0");
-  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
   if (ldu < r) return fail(LOGRA_ERR_SHAPE, "ldu must be >= r");
   if (d == 0 || k == 0) {
     skip = true;
@@ -275,12 +279,39 @@ logra_status prepare_merge(void* W, int64_t ldw, const float* U, int64_t ldu, in
   return LOGRA_OK;
 }
 
+// RowAdam scratch for d rows: per-row root and squared norm, then the two
+// rounds of per-block partial sums.  Returns the total bytes.
+size_t rowadam_layout(int64_t d, size_t& off_root, size_t& off_ssq, size_t& off_part, size_t& off_part2) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  off_root = 0;
+  off_ssq = up((size_t)d * 4);
+  off_part = off_ssq + up((size_t)d * 4);
+  off_part2 = off_part + up((size_t)2 * kRowAdamBlocks * 8);
+  return off_part2 + up((size_t)kRowAdamBlocks * 8);
+}
+
+// Ranks above 256 run as two column halves through the rank <= 256 tilings:
+// sign rows [0, 256) into columns [0, 256) of S (and of the projection cache),
+// rows [256, r) into columns [256, r).  A sign depends only on (seed, row,
+// column), so the halves add exactly the columns one rank-r pass would; both
+// scale by 1/sqrt(r).
+constexpr int kHalfRank = 256;
+int n_halves(int r) { return r > kHalfRank ? 2 : 1; }
+int half_rank(int r, int h) { return h == 0 ? std::min(r, kHalfRank) : r - kHalfRank; }
+// Projection cache of rank r: one cache per half, back to back.
+size_t cache_bytes(int64_t T, int r) {
+  size_t b = 0;
+  for (int h = 0; h < n_halves(r); ++h) b += projection_cache_bytes(T, half_rank(r, h));
+  return b;
+}
+size_t cache_half_offset(int64_t T, int h) { return h == 0 ? 0 : projection_cache_bytes(T, kHalfRank); }
+
 // Argument checks of the fused sketch calls; *empty: nothing to do.
 logra_status check_sketch_args(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T, int64_t k,
                                int64_t d, int32_t r, const float* S, int64_t lds, bool* empty) {
   *empty = false;
   if (T < 0 || k < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T, k and d must be >= 0");
-  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
   if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
   if (T == 0 || k == 0 || d == 0) {
     *empty = true;
@@ -347,12 +378,17 @@ logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx, const v
     // scratch then holds P, the projection's column-split partials and the
     // split counters only).  Worked out afresh (no plan cache: nothing is
     // allocated on the host either).
-    SketchPlan pl = plan_sketch(T, k, d, r, g_deterministic, g_precision_hi_only);
-    pl.use_part = 0;
-    st = check_plan(pl, T, ldx, lddy);
-    if (st != LOGRA_OK) return st;
-    const size_t off_cnt = (pl.off_cpart + 255) / 256 * 256;
-    const size_t cnt_bytes = (size_t)(pl.n_k > 1 ? pl.n_counters : 0) * sizeof(unsigned);
+    SketchPlan pls[2];
+    size_t off_cnt = 0, cnt_bytes = 0;
+    for (int h = 0; h < n_halves(r); ++h) {
+      SketchPlan& pl = pls[h];
+      pl = plan_sketch(T, k, d, half_rank(r, h), g_deterministic, g_precision_hi_only);
+      pl.use_part = 0;
+      st = check_plan(pl, T, ldx, lddy);
+      if (st != LOGRA_OK) return st;
+      off_cnt = std::max(off_cnt, (pl.off_cpart + 255) / 256 * 256);
+      cnt_bytes = std::max(cnt_bytes, (size_t)(pl.n_k > 1 ? pl.n_counters : 0) * sizeof(unsigned));
+    }
     const size_t cnt_span = (cnt_bytes + 15) / 16 * 16;
     const size_t need = off_cnt + cnt_span;
     if (need > (size_t)LOGRA_NOALLOC_SCRATCH_BYTES)
@@ -367,17 +403,26 @@ logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx, const v
     unsigned* counters = nullptr;
     if (cnt_span) {
       // The last call may have left anything here: clear the counters with
-      // a kernel (capturable, unlike a memset node).
+      // a kernel (capturable, unlike a memset node).  The projection kernels
+      // leave them at zero, so one clear serves both halves.
       counters = reinterpret_cast<unsigned*>(base + off_cnt);
       zero_fill_launch(counters, (int64_t)(cnt_span / 16), stream);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(e, "counter clear launch");
     }
-    uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
-    uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
-    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, g_precision_hi_only, stream, counters);
-    if (st != LOGRA_OK) return st;
-    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, g_precision_hi_only, stream);
+    for (int h = 0; h < n_halves(r); ++h) {
+      const SketchPlan& pl = pls[h];
+      const int rh = half_rank(r, h);
+      uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
+      uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
+      st = enqueue_projection(pl, base, X, ldx, T, k, seed, rh, kHalfRank * h, Phi, Plo, g_precision_hi_only, stream,
+                              counters);
+      if (st != LOGRA_OK) return st;
+      st = enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, rh, r, S + kHalfRank * h, lds,
+                               g_precision_hi_only, stream);
+      if (st != LOGRA_OK) return st;
+    }
+    return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -392,18 +437,38 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
     logra_status st = check_sketch_args(X, ldx, dY, lddy, T, k, d, r, S, lds, &empty);
     if (st != LOGRA_OK || empty) return st;
 
-    const SketchPlan pl = sketch_plan_for(T, k, d, r, g_precision_hi_only);
-    st = check_plan(pl, T, ldx, lddy);
-    if (st != LOGRA_OK) return st;
+    SketchPlan pls[2];
+    size_t need = 0;
+    int64_t n_cnt = 0;
+    for (int h = 0; h < n_halves(r); ++h) {
+      pls[h] = sketch_plan_for(T, k, d, half_rank(r, h), g_precision_hi_only);
+      st = check_plan(pls[h], T, ldx, lddy);
+      if (st != LOGRA_OK) return st;
+      need = std::max(need, pls[h].total);
+      n_cnt = std::max(n_cnt, pls[h].n_counters);
+    }
+    // All scratch is obtained before anything is enqueued.
     void* ws = nullptr;
-    st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    st = arena_get(kArenaSketch, stream, need, &ws);
     if (st != LOGRA_OK) return st;
+    if (n_cnt > 0) {
+      unsigned* cnt = nullptr;
+      st = counters_get(stream, n_cnt, &cnt);
+      if (st != LOGRA_OK) return st;
+    }
     char* base = static_cast<char*>(ws);
-    uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
-    uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
-    st = enqueue_projection(pl, base, X, ldx, T, k, seed, r, Phi, Plo, g_precision_hi_only, stream);
-    if (st != LOGRA_OK) return st;
-    return enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, r, S, lds, g_precision_hi_only, stream);
+    for (int h = 0; h < n_halves(r); ++h) {
+      const SketchPlan& pl = pls[h];
+      const int rh = half_rank(r, h);
+      uint16_t* Phi = reinterpret_cast<uint16_t*>(base + pl.off_phi);
+      uint16_t* Plo = reinterpret_cast<uint16_t*>(base + pl.off_plo);
+      st = enqueue_projection(pl, base, X, ldx, T, k, seed, rh, kHalfRank * h, Phi, Plo, g_precision_hi_only, stream);
+      if (st != LOGRA_OK) return st;
+      st = enqueue_contraction(pl, base, dY, lddy, T, d, Phi, Plo, rh, r, S + kHalfRank * h, lds,
+                               g_precision_hi_only, stream);
+      if (st != LOGRA_OK) return st;
+    }
+    return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -423,7 +488,7 @@ int logra_set_deterministic(int enable) {
 
 size_t logra_projection_bytes(int64_t T, int32_t r) {
   if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
-  return projection_cache_bytes(T, r);
+  return cache_bytes(T, r);
 }
 
 logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uint64_t seed, int32_t r, void* P,
@@ -431,10 +496,10 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
   try {
     g_last_error.clear();
     if (T < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "T and k must be >= 0");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
     if (T == 0) return LOGRA_OK;
     if (!P) return fail(LOGRA_ERR_NULL, "P must be non-null");
-    const size_t need = projection_cache_bytes(T, r);
+    const size_t need = cache_bytes(T, r);
     if (P_bytes < need) return fail(LOGRA_ERR_SHAPE, "P_bytes is smaller than logra_projection_bytes(T, r)");
     if ((uintptr_t)P & 15) return fail(LOGRA_ERR_ALIGN, "P must be 16-byte aligned");
     if (k == 0) {
@@ -449,17 +514,36 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
     if (st != LOGRA_OK) return st;
     if (overlaps(P, need, X, span_bytes(T, k, ldx, 2))) return fail(LOGRA_ERR_ALIAS, "P overlaps X");
 
-    SketchPlan pl = sketch_plan_for(T, k, 1, r, false);
-    st = check_plan(pl, T, ldx, 8);
-    if (st != LOGRA_OK) return st;
-    if (pl.Tpad > cache_tokens(T)) return fail(LOGRA_ERR_RANGE, "projection tile does not fit the cache");
-    scratch_layout(pl, 1, true, false);
+    SketchPlan pls[2];
+    size_t ws_need = 0;
+    int64_t n_cnt = 0;
+    for (int h = 0; h < n_halves(r); ++h) {
+      SketchPlan& pl = pls[h];
+      pl = sketch_plan_for(T, k, 1, half_rank(r, h), false);
+      st = check_plan(pl, T, ldx, 8);
+      if (st != LOGRA_OK) return st;
+      if (pl.Tpad > cache_tokens(T)) return fail(LOGRA_ERR_RANGE, "projection tile does not fit the cache");
+      scratch_layout(pl, 1, true, false);
+      ws_need = std::max(ws_need, pl.total);
+      n_cnt = std::max(n_cnt, pl.n_counters);
+    }
     void* ws = nullptr;
-    st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    st = arena_get(kArenaSketch, stream, ws_need, &ws);
     if (st != LOGRA_OK) return st;
-    uint16_t* Phi = static_cast<uint16_t*>(P);
-    uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
-    return enqueue_projection(pl, static_cast<char*>(ws), X, ldx, T, k, seed, r, Phi, Plo, false, stream);
+    if (n_cnt > 0) {
+      unsigned* cnt = nullptr;
+      st = counters_get(stream, n_cnt, &cnt);
+      if (st != LOGRA_OK) return st;
+    }
+    for (int h = 0; h < n_halves(r); ++h) {
+      const SketchPlan& pl = pls[h];
+      uint16_t* Phi = reinterpret_cast<uint16_t*>(static_cast<char*>(P) + cache_half_offset(T, h));
+      uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
+      st = enqueue_projection(pl, static_cast<char*>(ws), X, ldx, T, k, seed, half_rank(r, h), kHalfRank * h, Phi,
+                              Plo, false, stream);
+      if (st != LOGRA_OK) return st;
+    }
+    return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -470,11 +554,11 @@ logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d, 
   try {
     g_last_error.clear();
     if (T < 0 || d < 0) return fail(LOGRA_ERR_SHAPE, "T and d must be >= 0");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
     if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
     if (T == 0 || d == 0) return LOGRA_OK;
     if (!dY || !P || !S) return fail(LOGRA_ERR_NULL, "dY, P and S must be non-null");
-    const size_t need = projection_cache_bytes(T, r);
+    const size_t need = cache_bytes(T, r);
     if (P_bytes < need) return fail(LOGRA_ERR_SHAPE, "P_bytes is smaller than logra_projection_bytes(T, r)");
     if ((uintptr_t)P & 15) return fail(LOGRA_ERR_ALIGN, "P must be 16-byte aligned");
     logra_status st = check_dy_s(dY, lddy, T, d, S, lds, r);
@@ -482,16 +566,28 @@ logra_status logra_contract(const void* dY, int64_t lddy, int64_t T, int64_t d, 
     if (overlaps(S, span_bytes(d, r, lds, 4), P, need)) return fail(LOGRA_ERR_ALIAS, "S overlaps P");
 
     // The contraction's tiling does not depend on k; 256 stands in for it.
-    SketchPlan pl = sketch_plan_for(T, 256, d, r, false);
-    st = check_plan(pl, T, 8, lddy);
-    if (st != LOGRA_OK) return st;
-    scratch_layout(pl, d, false, true);
+    SketchPlan pls[2];
+    size_t ws_need = 0;
+    for (int h = 0; h < n_halves(r); ++h) {
+      SketchPlan& pl = pls[h];
+      pl = sketch_plan_for(T, 256, d, half_rank(r, h), false);
+      st = check_plan(pl, T, 8, lddy);
+      if (st != LOGRA_OK) return st;
+      scratch_layout(pl, d, false, true);
+      ws_need = std::max(ws_need, pl.total);
+    }
     void* ws = nullptr;
-    st = arena_get(kArenaSketch, stream, pl.total, &ws);
+    st = arena_get(kArenaSketch, stream, ws_need, &ws);
     if (st != LOGRA_OK) return st;
-    const uint16_t* Phi = static_cast<const uint16_t*>(P);
-    const uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
-    return enqueue_contraction(pl, static_cast<char*>(ws), dY, lddy, T, d, Phi, Plo, r, S, lds, false, stream);
+    for (int h = 0; h < n_halves(r); ++h) {
+      const SketchPlan& pl = pls[h];
+      const uint16_t* Phi = reinterpret_cast<const uint16_t*>(static_cast<const char*>(P) + cache_half_offset(T, h));
+      const uint16_t* Plo = Phi + (size_t)cache_tokens(T) * 16 * pl.NB;
+      st = enqueue_contraction(pl, static_cast<char*>(ws), dY, lddy, T, d, Phi, Plo, half_rank(r, h), r,
+                               S + kHalfRank * h, lds, false, stream);
+      if (st != LOGRA_OK) return st;
+    }
+    return LOGRA_OK;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -522,7 +618,7 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
     if (count < 0) return fail(LOGRA_ERR_SHAPE, "count must be >= 0");
     if (count == 0) return LOGRA_OK;
     if (!items) return fail(LOGRA_ERR_NULL, "items must be non-null");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
     // Validate everything before anything is enqueued.
     std::vector<MergeParams> mps;
     MergePlan pl0{};
@@ -580,7 +676,7 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
   try {
     g_last_error.clear();
     if (d < 0) return fail(LOGRA_ERR_SHAPE, "d must be >= 0");
-    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
     if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
     if (step < 1) return fail(LOGRA_ERR_RANGE, "step counts RowAdam updates and starts at 1");
     if (!(beta2 >= 0.0f && beta2 < 1.0f)) return fail(LOGRA_ERR_RANGE, "beta2 must be in [0, 1)");
@@ -590,12 +686,8 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
     if (((uintptr_t)S & 3) || ((uintptr_t)v & 3)) return fail(LOGRA_ERR_ALIGN, "S and v must be 4-byte aligned");
     if (overlaps(S, span_bytes(d, r, lds, 4), v, (size_t)d * 4)) return fail(LOGRA_ERR_ALIAS, "v overlaps S");
 
-    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t off_root = 0;
-    const size_t off_ssq = up((size_t)d * 4);
-    const size_t off_part = off_ssq + up((size_t)d * 4);
-    const size_t off_part2 = off_part + up((size_t)2 * kRowAdamBlocks * 8);
-    const size_t total = off_part2 + up((size_t)kRowAdamBlocks * 8);
+    size_t off_root, off_ssq, off_part, off_part2;
+    const size_t total = rowadam_layout(d, off_root, off_ssq, off_part, off_part2);
     void* ws = nullptr;
     logra_status st = arena_get(kArenaRowAdam, stream, total, &ws);
     if (st != LOGRA_OK) return st;
@@ -689,7 +781,7 @@ double logra_kl_effective_budget(double delta, double kappa) {
 
 logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out, hipStream_t stream) {
   g_last_error.clear();
-  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 256]");
+  if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
   if (k < 0) return fail(LOGRA_ERR_SHAPE, "k must be >= 0");
   if (k == 0) return LOGRA_OK;
   if (!out) return fail(LOGRA_ERR_NULL, "out must be non-null");
@@ -712,18 +804,96 @@ logra_status logra_stream_read(const void* ptr, size_t bytes, uint32_t* sink, hi
   return LOGRA_OK;
 }
 
-size_t logra_workspace_bytes(int64_t T, int32_t r) {
-  if (T <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
-  // The largest plan over k and d (powers of two up to 2^20) for this T and
-  // r.  The contraction's partial tiles grow with d only until the token
-  // splits shrink, so the maximum is reached inside this range.
-  size_t best = 0;
-  for (int64_t k = 256; k <= ((int64_t)1 << 20); k *= 2)
-    for (int64_t d = 256; d <= ((int64_t)1 << 20); d *= 2) {
-      const SketchPlan pl = plan_sketch(T, k, d, r);
-      if (pl.total > best) best = pl.total;
+}  // extern "C"
+
+namespace {
+
+// Scratch the calls for one (T, k, d, r) need on a stream, with the calling
+// thread's settings: the sketch region (the fused call's plan covers the
+// split calls' partials too), the split counters, and RowAdam's for d rows.
+struct WorkspaceNeed {
+  size_t sketch = 0, counters = 0, rowadam = 0;
+};
+
+WorkspaceNeed workspace_need(int64_t T, int64_t k, int64_t d, int r) {
+  WorkspaceNeed w;
+  for (int h = 0; h < n_halves(r); ++h) {
+    const int rh = half_rank(r, h);
+    const SketchPlan pl = sketch_plan_for(T, k, d, rh, g_precision_hi_only);
+    w.sketch = std::max(w.sketch, pl.total);
+    w.counters = std::max(w.counters, (size_t)std::max<int64_t>(pl.n_counters, 1) * sizeof(unsigned));
+    SketchPlan pp = sketch_plan_for(T, k, 1, rh, false);
+    scratch_layout(pp, 1, true, false);
+    w.sketch = std::max(w.sketch, pp.total);
+    w.counters = std::max(w.counters, (size_t)std::max<int64_t>(pp.n_counters, 1) * sizeof(unsigned));
+    SketchPlan pc = sketch_plan_for(T, 256, d, rh, false);
+    scratch_layout(pc, d, false, true);
+    w.sketch = std::max(w.sketch, pc.total);
+  }
+  size_t a, b, c, e;
+  w.rowadam = rowadam_layout(d, a, b, c, e);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t logra_workspace_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
+  if (T <= 0 || d <= 0 || k <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
+  try {
+    const WorkspaceNeed w = workspace_need(T, k, d, r);
+    return w.sketch + w.counters + w.rowadam;
+  } catch (...) {
+    return 0;
+  }
+}
+
+logra_status logra_workspace_reserve(int64_t T, int64_t d, int64_t k, int32_t r, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (T < 0 || d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "T, d and k must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
+    if (T == 0 || d == 0 || k == 0) return LOGRA_OK;
+    const WorkspaceNeed w = workspace_need(T, k, d, r);
+    void* p = nullptr;
+    logra_status st = arena_get(kArenaSketch, stream, w.sketch, &p);
+    if (st != LOGRA_OK) return st;
+    st = arena_get(kArenaCounters, stream, w.counters, &p);
+    if (st != LOGRA_OK) return st;
+    return arena_get(kArenaRowAdam, stream, w.rowadam, &p);
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_workspace_release(hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(LOGRA_ERR_RANGE, "the stream is being captured: release its scratch after the capture ends");
+    // Work already queued on the stream may still use the buffers.
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    std::lock_guard<std::mutex> lk(g_arena_mu);
+    for (int kind = 0; kind < kArenaKinds; ++kind) {
+      auto it = g_arenas.find({{dev, kind}, stream});
+      if (it == g_arenas.end()) continue;
+      Arena& a = it->second;
+      for (void* q : a.retired) (void)hipFree(q);
+      if (a.ptr) (void)hipFree(a.ptr);
+      g_arenas.erase(it);
     }
-  return best;
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
 }
 
 const char* logra_status_string(logra_status s) {

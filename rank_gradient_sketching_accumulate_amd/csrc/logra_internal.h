@@ -27,6 +27,7 @@ struct ProjParams {
   unsigned* counters;  // one per token tile; zero between calls
   int hi_only;      // 0: write P's high and low planes; 1: the high plane only (the
                     // contraction reads no low plane); 2: high plane, zero low plane
+  int row0;         // sign row of P's column 0 (256 for the upper half at ranks above 256)
 };
 
 struct ContractParams {
@@ -107,7 +108,7 @@ struct MergeParams {
 };
 
 struct MergePlan {
-  int NK;           // 32-wide steps of r (1, 2, 4 or 8; U zero-padded)
+  int NK;           // 32-wide steps of r (1, 2, 4, 8 or 16; U zero-padded)
   int NBW;          // 16-row blocks per wave
   int CB;           // 16-column blocks per chunk (4 or 8)
   int n_rb, n_cr;

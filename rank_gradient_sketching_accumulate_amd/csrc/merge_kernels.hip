@@ -9,8 +9,9 @@
 // each) load their U rows once, split them into bf16 hi/lo pairs held in
 // registers for the whole range, and keep the W tiles of the next PD chunks
 // in flight.  Whenever the walk enters a new 256-column sign block the
-// workgroup regenerates that block's signs (Philox, rows 0 .. 32*NK-1) into
-// LDS and bit-transposes them so that one byte holds 8 rows of a column;
+// workgroup regenerates that block's signs (Philox, rows 0 .. 32*NK-1, up to
+// 512) into LDS and bit-transposes them so that one byte holds 8 rows of a
+// column;
 // every wave then expands its own MFMA sign operands from those bytes.
 //
 // MFMA orientation D = s^T U^T: M = 16 columns of W, N = 16 rows of W,
@@ -44,7 +45,8 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
 // lin % n_cr) of the matrix p describes.
 template <int NBW, int CB, int NK, int PD>
 __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
-  constexpr int STR = 9;        // dwords per row (row-major bits) / per column (column-major bits)
+  constexpr int STR = 9;        // dwords per row of row-major bits (8 + 1 pad)
+  constexpr int CSTR = NK < 8 ? 9 : NK + 1;  // dwords per column of column-major bits (odd)
   constexpr int CW = 16 * CB;   // columns per chunk
   constexpr int KR = 32 * NK;   // sign rows generated (U entries >= r are zero)
   constexpr int RW = 16 * NBW;  // rows per wave
@@ -53,7 +55,7 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   constexpr int RPI = 64 / LPR; // rows per W instruction
   constexpr int NI = RW / RPI;  // W instructions per chunk
   __shared__ uint32_t rowbits[KR * STR];
-  __shared__ uint32_t colbits[256 * STR];
+  __shared__ uint32_t colbits[256 * CSTR];
   __shared__ float tiles[4 * RW * TSTR];
 
   const int rb = lin / p.n_cr;
@@ -127,11 +129,11 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   // Signs of the 256-column block holding col0: rows 0 .. KR-1 into rowbits,
   // then the columns of this workgroup's range inside the block into colbits.
   auto build_block = [&](int64_t col0) {
-    if (threadIdx.x < KR) {
+    for (int row = threadIdx.x; row < KR; row += 256) {
       uint32_t w[8];
-      philox_sign_block(p.seed, threadIdx.x, (uint32_t)(col0 >> 8), w);
+      philox_sign_block(p.seed, (uint32_t)row, (uint32_t)(col0 >> 8), w);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rowbits[threadIdx.x * STR + q] = w[q];
+      for (int q = 0; q < 8; ++q) rowbits[row * STR + q] = w[q];
     }
     __syncthreads();  // also: every wave is done with the previous colbits
     const uint8_t* rbt = reinterpret_cast<const uint8_t*>(rowbits);
@@ -148,7 +150,7 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
       for (int e = 0; e < 8; ++e) x |= (uint64_t)rbt[(8 * ro + e) * STR * 4 + co] << (8 * e);
       x = transpose8x8(x);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) cbt[(8 * co + b) * STR * 4 + ro] = (uint8_t)(x >> (8 * b));
+      for (int b = 0; b < 8; ++b) cbt[(8 * co + b) * CSTR * 4 + ro] = (uint8_t)(x >> (8 * b));
     }
     __syncthreads();
   };
@@ -190,7 +192,7 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
         for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
           for (int mb = 0; mb < CB; ++mb) {
-            const u32x4 a = ex(colbits[(cib + 16 * mb + i) * STR + kk]);
+            const u32x4 a = ex(colbits[(cib + 16 * mb + i) * CSTR + kk]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
               acc[mb][nb] = mfma_16x16x32(a, uh[kk][nb], acc[mb][nb]);
@@ -258,23 +260,26 @@ size_t align_up_m(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 MergePlan plan_merge(int64_t d, int64_t k, int r) {
   MergePlan pl{};
-  pl.NK = r <= 32 ? 1 : (r <= 64 ? 2 : (r <= 128 ? 4 : 8));
+  pl.NK = r <= 32 ? 1 : (r <= 64 ? 2 : (r <= 128 ? 4 : (r <= 256 ? 8 : 16)));
   // Tile per wave and chunk (two waves fit per SIMD): one 16-row block x 64
   // columns up to r = 128 with about 2048 workgroups; at r = 256, where the
   // U operands and sign expansion cost more, two 16-row blocks (each expanded
   // sign operand feeds both) with about 1024 longer column ranges.  Measured
   // with GPU-only timing over layers from 1536 x 1536 to 17408 x 5120.
+  // Above r = 256 (NK = 16) one 16-row block x 64 columns: the U operands
+  // alone take 128 registers.
   int NBW = pl.NK == 8 ? 2 : 1, CB = 4;
   NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
   CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
   if (NBW == 2 && CB == 8 && pl.NK >= 4) CB = 4;  // would not fit two waves per SIMD
+  if (pl.NK == 16) NBW = 1, CB = 4;
   pl.NBW = NBW;
   pl.CB = CB;
   pl.n_rb = (int)((d + 64 * NBW - 1) / (64 * NBW));
   // Column ranges: as long as possible while about `target` workgroups remain.
   const int64_t CW = 16 * CB;
   const int64_t chunks = (k + CW - 1) / CW;
-  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK == 8 ? 1024 : 2048);
+  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK >= 8 ? 1024 : 2048);
   if (target < 1) target = 1;
   int64_t n_cr = (target + pl.n_rb - 1) / pl.n_rb;
   if (n_cr > chunks) n_cr = chunks;
@@ -296,6 +301,7 @@ bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s) {
   LOGRA_MERGE(1, 4, 2) LOGRA_MERGE(1, 8, 2) LOGRA_MERGE(2, 4, 2) LOGRA_MERGE(2, 8, 2)
   LOGRA_MERGE(1, 4, 4) LOGRA_MERGE(1, 8, 4) LOGRA_MERGE(2, 4, 4)
   LOGRA_MERGE(1, 4, 8) LOGRA_MERGE(1, 8, 8) LOGRA_MERGE(2, 4, 8)
+  LOGRA_MERGE(1, 4, 16)
 #undef LOGRA_MERGE
   return false;
 }
@@ -315,6 +321,7 @@ bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s)
   LOGRA_MERGE_G(1, 4, 2) LOGRA_MERGE_G(1, 8, 2) LOGRA_MERGE_G(2, 4, 2) LOGRA_MERGE_G(2, 8, 2)
   LOGRA_MERGE_G(1, 4, 4) LOGRA_MERGE_G(1, 8, 4) LOGRA_MERGE_G(2, 4, 4)
   LOGRA_MERGE_G(1, 4, 8) LOGRA_MERGE_G(1, 8, 8) LOGRA_MERGE_G(2, 4, 8)
+  LOGRA_MERGE_G(1, 4, 16)
 #undef LOGRA_MERGE_G
   return false;
 }

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(512) void proj_small_kernel(ProjParams p) {
   for (int b = threadIdx.x; b < RP * p.ncb; b += NW * 64) {
     const int row = b % RP, cb = b / RP;
     uint32_t wd[8];
-    philox_sign_block(p.seed, (uint32_t)row, (uint32_t)cb, wd);
+    philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)cb, wd);
     uint32_t* dst = lds + (cb * RP + row) * SROW;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = wd[e];
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int cb = cbb + j * WK + wkk;
         if (cb < cbe) {
           uint32_t w[8];
-          philox_sign_block(p.seed, (uint32_t)row, (uint32_t)cb, w);
+          philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)cb, w);
           uint32_t* dst = &sbits[buf][(wkk * RP + row) * SROW];
 #pragma unroll
           for (int e = 0; e < 8; ++e) dst[e] = w[e];
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int b = threadIdx.x + 512 * q;
       const int row = b % RP, wkk = b / RP;
       uint32_t w[8];
-      philox_sign_block(p.seed, (uint32_t)row, (uint32_t)(cbb + WK * j + wkk), w);
+      philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
       uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e] = w[e];

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.logra_abi_version() == 1
+    assert lib.logra_abi_version() == 2
     for s in range(8):
         assert lib.logra_status_string(s)
     assert lib.logra_status_string(0) == b"ok"
@@ -53,13 +53,28 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.logra_workspace_bytes(0, 64) == 0
-    assert lib.logra_workspace_bytes(4096, 0) == 0
-    # P as a bf16 hi/lo pair: 4 bytes per (token, rank) at least, whatever
-    # the split partials add (those need not grow with T)
+    assert lib.logra_workspace_bytes(0, 64, 64, 64) == 0
+    assert lib.logra_workspace_bytes(4096, 1536, 1536, 0) == 0
+    assert lib.logra_workspace_bytes(4096, 1536, 1536, 513) == 0
+    assert lib.logra_workspace_bytes(4096, 0, 1536, 64) == 0
+    # P as a bf16 hi/lo pair: 4 bytes per (token, padded rank column) at
+    # least, plus RowAdam's two floats per row; a rank above 256 reuses the
+    # scratch of its two halves, so it needs no more than the larger half
+    # plus what the row statistics add.
     for T in (512, 4096, 8192, 16384):
-        for r in (16, 64, 128, 256):
-            assert lib.logra_workspace_bytes(T, r) >= T * r * 4
+        for r in (16, 64, 128, 256, 300, 512):
+            R = min(r, 256)
+            assert lib.logra_workspace_bytes(T, 5120, 17408, r) >= T * R * 4 + 8 * 5120
+    assert lib.logra_workspace_bytes(16384, 17408, 5120, 512) == lib.logra_workspace_bytes(16384, 17408, 5120, 256)
+
+
+def test_workspace_reserve_validation(lib):
+    assert lib.logra_workspace_reserve(-1, 4, 4, 4, None) == ERR_SHAPE
+    assert lib.logra_workspace_reserve(16, 4, 4, 0, None) == ERR_RANGE
+    assert lib.logra_workspace_reserve(16, 4, 4, 513, None) == ERR_RANGE
+    # empty shapes need nothing (no device call)
+    assert lib.logra_workspace_reserve(0, 4, 4, 4, None) == OK
+    assert lib.logra_workspace_reserve(16, 0, 4, 4, None) == OK
 
 
 FAKE = 0x10000  # a well-aligned non-null address; never dereferenced on these paths
@@ -71,7 +86,7 @@ def _sketch(lib, X=FAKE, ldx=512, dY=FAKE * 64, lddy=256, T=16, k=512, d=256, r=
 
 def test_sketch_validation(lib):
     assert _sketch(lib, r=0) == ERR_RANGE
-    assert _sketch(lib, r=257) == ERR_RANGE
+    assert _sketch(lib, r=513) == ERR_RANGE
     assert _sketch(lib, T=-1) == ERR_SHAPE
     assert _sketch(lib, lds=8) == ERR_SHAPE
     assert _sketch(lib, X=None) == ERR_NULL
@@ -99,12 +114,15 @@ def test_set_deterministic_is_per_call_setting(lib):
 def test_projection_bytes(lib):
     assert lib.logra_projection_bytes(0, 16) == 0
     assert lib.logra_projection_bytes(16, 0) == 0
-    assert lib.logra_projection_bytes(16, 257) == 0
+    assert lib.logra_projection_bytes(16, 513) == 0
     # two bf16 planes of roundup(T, 256) tokens x (16 * next power of two of ceil(r / 16)) columns
     assert lib.logra_projection_bytes(1, 1) == 4 * 256 * 16
     assert lib.logra_projection_bytes(4096, 64) == 4 * 4096 * 64
     assert lib.logra_projection_bytes(4097, 48) == 4 * 4352 * 64
     assert lib.logra_projection_bytes(16384, 256) == 4 * 16384 * 256
+    # above 256: the cache of columns 0..255, then one of rank r - 256
+    assert lib.logra_projection_bytes(16384, 300) == 4 * 16384 * 256 + 4 * 16384 * 64
+    assert lib.logra_projection_bytes(1000, 512) == 2 * 4 * 1024 * 256
 
 
 PB = 4 * 256 * 16  # logra_projection_bytes(16, 16)
@@ -130,7 +148,7 @@ def test_split_validation(lib):
     assert _project(lib, X=FAKE + 2) == ERR_ALIGN
     assert _project(lib, ldx=500) == ERR_SHAPE
     assert _project(lib, P=FAKE + 4096) == ERR_ALIAS  # inside X's 16 KiB span
-    assert _contract(lib, r=300) == ERR_RANGE
+    assert _contract(lib, r=513) == ERR_RANGE
     assert _contract(lib, lds=8) == ERR_SHAPE
     assert _contract(lib, T=0, dY=None, P=None, S=None) == OK
     assert _contract(lib, d=0) == OK

@@ -35,7 +35,8 @@ int main(void) {
   CHECK(fabs(logra_kl_budget(1, 300, 2e-4, 2e-5) - 2e-4) < 1e-18);
   CHECK(logra_kl_effective_budget(1e-4, 9e-5) == 5e-5);
   CHECK(logra_projection_bytes(4096, 64) == (size_t)4 * 4096 * 64);
-  CHECK(logra_workspace_bytes(4096, 64) >= (size_t)4 * 4096 * 64);
+  CHECK(logra_workspace_bytes(4096, 1536, 1536, 64) >= (size_t)4 * 4096 * 64);
+  CHECK(logra_workspace_reserve(4096, 1536, 1536, 0, 0) == LOGRA_ERR_RANGE);
   /* validation returns before any device work */
   void* fake = (void*)(uintptr_t)0x10000;
   CHECK(logra_sketch_accumulate(fake, 512, fake, 256, 16, 512, 256, 0, 0, (float*)fake, 16, 0) == LOGRA_ERR_RANGE);

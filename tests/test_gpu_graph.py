@@ -112,3 +112,100 @@ def test_graph_capture_and_replay():
     ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X), f64(X)], [f64(dY), f64(dY)], A)
     assert_sketch_close(f64(S), ref)
     assert float(q.item()) == pytest.approx(oracle.predicted_kl(f64(z), f64(zd), 0.9), rel=1e-4)
+
+
+def test_replay_after_scratch_grew():
+    """A graph captured while the stream's scratch was small keeps working
+    after a larger eager call on the same stream made the library grow the
+    scratch: the buffer the graph uses is retired, not freed."""
+    print("[case] graph replay after growth", flush=True)
+    T, k, d, r, seed = 700, 1300, 300, 64, 31
+    X = wl.gaussian_bf16((T, k), 1.0, 11, device=DEV, ld=padded_ld(k))
+    dY = wl.gaussian_bf16((T, d), 1e-2, 12, device=DEV, ld=padded_ld(d))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lg.workspace_reserve(T, d, k, r)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        S.zero_()
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    torch.cuda.synchronize()
+    # A much larger call on the same stream: the scratch grows.
+    TB, kB, dB, rB = 16384, 5120, 5120, 256
+    XB = wl.gaussian_bf16((TB, kB), 1.0, 13, device=DEV)
+    dYB = wl.gaussian_bf16((TB, dB), 1e-2, 14, device=DEV)
+    SB = torch.zeros((dB, rB), dtype=torch.float32, device=DEV)
+    before = lg.workspace_bytes(T, d, k, r)
+    assert lg.workspace_bytes(TB, dB, kB, rB) > before
+    with torch.cuda.stream(side):
+        lg.sketch_accumulate(XB, dYB, 3, rB, SB)
+    torch.cuda.synchronize()
+    del XB, dYB, SB
+    for rep in range(3):
+        X.copy_(wl.gaussian_bf16((T, k), 1.0, 40 + rep, device=DEV, ld=padded_ld(k)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        Se = torch.zeros_like(S)
+        lg.sketch_accumulate(X, dY, seed, r, Se)
+        torch.cuda.synchronize()
+        assert rel_frob(f64(S), f64(Se)) <= 1e-6, f"replay {rep}"
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(seed, r, k))
+    assert_sketch_close(f64(S), ref)
+
+
+def test_capture_without_reserve_is_refused_and_release_frees():
+    """On a fresh stream, a sketch call under capture whose scratch would have
+    to grow returns LOGRA_ERR_NOMEM (naming logra_workspace_reserve) and
+    enqueues nothing; after logra_workspace_reserve the same capture works;
+    logra_workspace_release then frees the stream's scratch and a later eager
+    call allocates it again."""
+    print("[case] capture without reserve", flush=True)
+    T, k, d, r, seed = 1000, 700, 900, 128, 41
+    X = wl.gaussian_bf16((T, k), 1.0, 21, device=DEV, ld=padded_ld(k))
+    dY = wl.gaussian_bf16((T, d), 1e-2, 22, device=DEV, ld=padded_ld(d))
+    S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+    marker = torch.zeros(1, dtype=torch.float32, device=DEV)
+    fresh = torch.cuda.Stream()
+    fresh.wait_stream(torch.cuda.current_stream())
+    # torch hands out streams from a pool: drop whatever an earlier user of
+    # this handle left, so the capture below starts with no scratch.
+    lg.workspace_release(fresh)
+    g = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.graph(g, stream=fresh):
+        marker.add_(1.0)
+        try:
+            lg.sketch_accumulate(X, dY, seed, r, S)
+        except lg.LograError as e:
+            err = e
+    torch.cuda.synchronize()
+    assert err is not None and err.status == lg.LOGRA_ERR_NOMEM
+    assert "logra_workspace_reserve" in str(err)
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(marker.item()) == 1.0 and not bool(S.any())
+    with torch.cuda.stream(fresh):
+        lg.workspace_reserve(T, d, k, r)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=fresh):
+        S.zero_()
+        lg.sketch_accumulate(X, dY, seed, r, S)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g2.replay()
+        torch.cuda.synchronize()
+        ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)],
+                                       oracle.rademacher_projection(seed, r, k))
+        assert_sketch_close(f64(S), ref)
+    del g, g2
+    lg.workspace_release(fresh)
+    S2 = torch.zeros_like(S)
+    with torch.cuda.stream(fresh):
+        lg.sketch_accumulate(X, dY, seed, r, S2)
+    torch.cuda.synchronize()
+    assert rel_frob(f64(S2), f64(S)) <= 1e-6

@@ -56,7 +56,8 @@ def _ragged_inputs(T, k, d, seed, sx=1.0, sdy=1e-2):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize(
     "seed,r,k",
-    [(0, 16, 512), (1, 3, 700), (2**63 + 5, 5, 257), (42, 256, 1536), (7, 64, 33), (123, 1, 1), (9, 200, 5120)],
+    [(0, 16, 512), (1, 3, 700), (2**63 + 5, 5, 257), (42, 256, 1536), (7, 64, 33), (123, 1, 1), (9, 200, 5120),
+     (5, 512, 700), (6, 300, 1300)],
 )
 def test_signs_bit_exact(seed, r, k):
     _say("signs", seed, r, k)
@@ -624,4 +625,4 @@ def test_errors_on_device_buffers():
         lg.sketch_accumulate(Xa, dY, 0, 16, Sa)
     assert ei.value.status == 5
     with pytest.raises(lg.LograError):
-        lg.sketch_accumulate(X, dY, 0, 300, torch.zeros((64, 300), device=DEV))
+        lg.sketch_accumulate(X, dY, 0, 513, torch.zeros((64, 513), device=DEV))

@@ -233,3 +233,26 @@ def test_split_rank256_plans(T, k, d, r, env, monkeypatch):
     ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(13, r, k),
                                    rows=rows)
     assert_sketch_close(f64(S) if rows is None else f64(S)[rows], ref)
+
+
+def test_counters_handoff_between_plans():
+    """Consecutive calls on one stream whose projections split their columns
+    across workgroups with different tilings (rank 256 on 5120 columns, rank
+    64 on 8192, rank 512 as two halves), through the fused and the split
+    calls: the split counters, kept apart from every other scratch, start
+    each call at zero and every result matches the oracle."""
+    cases = [(4096, 5120, 700, 256), (4096, 8192, 700, 64), (4096, 5120, 700, 256), (1000, 8192, 300, 512),
+             (4096, 8192, 700, 64)]
+    for j, (T, k, d, r) in enumerate(cases):
+        _say("counters handoff", j, T, k, d, r)
+        X, dY = _inputs(T, k, d, 800 + j)
+        A = oracle.rademacher_projection(50 + j, r, k)
+        rows = np.arange(0, d, 5)
+        ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], A, rows=rows)
+        S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+        lg.sketch_accumulate(X, dY, 50 + j, r, S)
+        assert_sketch_close(f64(S)[rows], ref, what=f"fused call {j}")
+        P = lg.project(X, 50 + j, r)
+        S2 = torch.zeros_like(S)
+        lg.contract(dY, P, r, S2)
+        assert_sketch_close(f64(S2)[rows], ref, what=f"split calls {j}")
