@@ -269,6 +269,78 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
                                         int32_t r, hipStream_t stream);
 
 /*
+ * Synchronisation payload (paper section 2.2, "Memory and synchronization";
+ * Algorithm 1, the rollout side's update): after the trainer's merge, the
+ * rollout engine receives each sketched matrix's factor -- O(d r) values --
+ * with its seed and metadata, regenerates the signs from the seed and applies
+ * the factor to its own copy of the weights.
+ *
+ * The payload is one contiguous byte buffer, little-endian:
+ *   bytes 0..31    header: u32 magic LOGRA_PAYLOAD_MAGIC ("LGRP"), u32 version
+ *                  (LOGRA_PAYLOAD_VERSION), i32 count, i32 r, u64 total
+ *                  bytes, u64 zero;
+ *   bytes 32..     count entries of 48 bytes (logra_payload_entry): u64 seed,
+ *                  i64 d, i64 k, f32 scale (alpha * eta), u32 zero, u64 byte
+ *                  offset of the entry's factor, u64 zero;
+ *   from logra_payload_header_bytes(count) (a multiple of 256): each factor U
+ *                  as fp32 d x r, rows packed (row stride r), at its offset
+ *                  (256-byte aligned).
+ * U and alpha*eta travel separately, not as one product: the receiver then
+ * runs the merge on exactly the trainer's inputs (U bits, seed, r, fp32
+ * scale), and a deterministic merge of the same inputs onto the same W bits
+ * gives the same W bits.  Receiver and trainer end bitwise equal when both
+ * hold the same W before the update and run this library build with the same
+ * tiling (no LOGRA_ tuning variables set); a product alpha*eta*U rounded to
+ * fp32 would not give that.
+ *
+ * logra_payload_bytes: total size for items' d (and r); 0 if count is out of
+ *   [1, LOGRA_PAYLOAD_MAX_ITEMS], r out of range or some d < 0 or k < 0.
+ * logra_payload_pack: writes the whole payload into the device buffer
+ *   `payload` (256-byte aligned, at least logra_payload_bytes bytes) on
+ *   `stream` from items' U (ldu >= r), d, k, seed and scale (W and ldw are
+ *   not read).  U must not overlap the payload.
+ * logra_payload_parse: host-side check of a host copy of the first
+ *   logra_payload_header_bytes(count) bytes (or more): magic, version, count
+ *   in range, every factor inside total bytes and 256-byte aligned, sizes
+ *   consistent.  Fills *header and entries[0 .. count-1] (max_entries of
+ *   room).  LOGRA_ERR_SHAPE for a malformed or truncated header,
+ *   LOGRA_ERR_RANGE when count exceeds max_entries.
+ * logra_payload_apply: the receiver's merge: W_j <- RNE_bf16(W_j - scale_j
+ *   (1/sqrt(r)) U_j s(seed_j)) for every entry, through
+ *   logra_merge_update_grouped with U_j read from the device payload
+ *   (`payload_bytes` bytes) at entry j's offset.  W[j] and ldw[j] are the
+ *   receiver's weights (host arrays of count pointers and strides); the
+ *   header and entries are those logra_payload_parse returned.
+ */
+#define LOGRA_PAYLOAD_MAGIC 0x5052474Cu
+#define LOGRA_PAYLOAD_VERSION 1
+#define LOGRA_PAYLOAD_MAX_ITEMS 32
+typedef struct {
+  uint32_t magic, version;
+  int32_t count, r;
+  uint64_t total_bytes;
+  uint64_t reserved;
+} logra_payload_header;
+typedef struct {
+  uint64_t seed;
+  int64_t d, k;
+  float scale;
+  uint32_t reserved0;
+  uint64_t u_offset;
+  uint64_t reserved1;
+} logra_payload_entry;
+
+size_t logra_payload_header_bytes(int32_t count);
+size_t logra_payload_bytes(const logra_merge_item* items, int32_t count, int32_t r);
+logra_status logra_payload_pack(const logra_merge_item* items, int32_t count, int32_t r,
+                                void* payload, size_t payload_bytes, hipStream_t stream);
+logra_status logra_payload_parse(const void* header_host, size_t bytes, logra_payload_header* header,
+                                 logra_payload_entry* entries, int32_t max_entries);
+logra_status logra_payload_apply(const void* payload, size_t payload_bytes,
+                                 const logra_payload_header* header, const logra_payload_entry* entries,
+                                 void* const* W, const int64_t* ldw, hipStream_t stream);
+
+/*
  * RowAdam row scaling (paper appendix B, equation 15), S -> U in place:
  *
  *     m_i   = (1/r) sum_j S_ij^2

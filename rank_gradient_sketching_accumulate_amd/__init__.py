@@ -34,6 +34,11 @@ __all__ = [
     "contract",
     "merge_update",
     "merge_update_grouped",
+    "payload_bytes",
+    "payload_header_bytes",
+    "payload_pack",
+    "payload_parse",
+    "payload_apply",
     "rowadam_scale",
     "predicted_kl",
     "kl_step_scale",
@@ -64,6 +69,11 @@ EXPORTED_SYMBOLS = (
     "logra_contract",
     "logra_merge_update",
     "logra_merge_update_grouped",
+    "logra_payload_header_bytes",
+    "logra_payload_bytes",
+    "logra_payload_pack",
+    "logra_payload_parse",
+    "logra_payload_apply",
     "logra_rowadam_scale",
     "logra_predicted_kl",
     "logra_kl_step_scale",
@@ -113,6 +123,29 @@ class MergeItem(ctypes.Structure):
     ]
 
 
+class PayloadHeader(ctypes.Structure):
+    """The C struct logra_payload_header (32 bytes)."""
+
+    _fields_ = [
+        ("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+        ("count", ctypes.c_int32), ("r", ctypes.c_int32),
+        ("total_bytes", ctypes.c_uint64), ("reserved", ctypes.c_uint64),
+    ]
+
+
+class PayloadEntry(ctypes.Structure):
+    """The C struct logra_payload_entry (48 bytes)."""
+
+    _fields_ = [
+        ("seed", ctypes.c_uint64), ("d", ctypes.c_int64), ("k", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("reserved0", ctypes.c_uint32),
+        ("u_offset", ctypes.c_uint64), ("reserved1", ctypes.c_uint64),
+    ]
+
+
+PAYLOAD_MAX_ITEMS = 32
+
+
 def _declare(lib):
     c_i64, c_u64, c_i32, c_vp, c_f = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.logra_sketch_accumulate.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_u64, c_i32, c_vp, c_i64, c_vp]
@@ -133,6 +166,19 @@ def _declare(lib):
     lib.logra_merge_update.restype = ctypes.c_int
     lib.logra_merge_update_grouped.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32, c_vp]
     lib.logra_merge_update_grouped.restype = ctypes.c_int
+    lib.logra_payload_header_bytes.argtypes = [c_i32]
+    lib.logra_payload_header_bytes.restype = ctypes.c_size_t
+    lib.logra_payload_bytes.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32]
+    lib.logra_payload_bytes.restype = ctypes.c_size_t
+    lib.logra_payload_pack.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32, c_vp, ctypes.c_size_t, c_vp]
+    lib.logra_payload_pack.restype = ctypes.c_int
+    lib.logra_payload_parse.argtypes = [c_vp, ctypes.c_size_t, ctypes.POINTER(PayloadHeader),
+                                        ctypes.POINTER(PayloadEntry), c_i32]
+    lib.logra_payload_parse.restype = ctypes.c_int
+    lib.logra_payload_apply.argtypes = [c_vp, ctypes.c_size_t, ctypes.POINTER(PayloadHeader),
+                                        ctypes.POINTER(PayloadEntry), ctypes.POINTER(c_vp),
+                                        ctypes.POINTER(c_i64), c_vp]
+    lib.logra_payload_apply.restype = ctypes.c_int
     lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
     lib.logra_rowadam_scale.restype = ctypes.c_int
     lib.logra_predicted_kl.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_vp, c_vp, c_vp]
@@ -385,6 +431,80 @@ def merge_update_grouped(items, r: int):
         if stream is None:
             stream = _stream_handle(W)
     _check(lib.logra_merge_update_grouped(arr, len(items), r, stream))
+
+
+def _factor_items(factors, r: int):
+    """ctypes items for a payload: factors is a sequence of (U, seed, scale,
+    k) with U (d, r) float32 on the GPU."""
+    import torch
+
+    arr = (MergeItem * max(1, len(factors)))()
+    for j, (U, seed, scale, k) in enumerate(factors):
+        _need(U, torch.float32, "U")
+        if U.dim() != 2 or U.size(1) != r:
+            raise ValueError(f"factor {j}: U must be (d, {r}), got {tuple(U.shape)}")
+        arr[j] = MergeItem(None, 0, U.data_ptr() if U.numel() else None, _ld(U), U.size(0), int(k),
+                           seed & (2**64 - 1), float(scale))
+    return arr
+
+
+def payload_bytes(factors, r: int) -> int:
+    """Size of the sync payload of factors [(U, seed, scale, k), ...]."""
+    return int(load_library().logra_payload_bytes(_factor_items(factors, r), len(factors), r))
+
+
+def payload_pack(factors, r: int, out=None):
+    """Pack factors [(U, seed, scale, k), ...] (U: (d, r) float32 on the GPU,
+    the matrix's alpha*eta `scale`, its column count k) into a uint8 device
+    tensor (allocated when `out` is None); returns it."""
+    import torch
+
+    lib = load_library()
+    arr = _factor_items(factors, r)
+    n = int(lib.logra_payload_bytes(arr, len(factors), r))
+    if n == 0:
+        raise LograError("invalid payload items", LOGRA_ERR_RANGE)
+    dev = factors[0][0].device
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=dev)
+    _check(lib.logra_payload_pack(arr, len(factors), r, out.data_ptr(), out.numel(), _stream_handle(out)))
+    return out
+
+
+def payload_parse(header_bytes: bytes):
+    """Parse and check the host copy of a payload's first bytes (at least
+    payload_header_bytes(count)); returns (header, entries) as ctypes
+    structures."""
+    lib = load_library()
+    h = PayloadHeader()
+    es = (PayloadEntry * PAYLOAD_MAX_ITEMS)()
+    buf = ctypes.create_string_buffer(bytes(header_bytes), len(header_bytes))
+    _check(lib.logra_payload_parse(buf, len(header_bytes), ctypes.byref(h), es, PAYLOAD_MAX_ITEMS))
+    return h, es
+
+
+def payload_header_bytes(count: int) -> int:
+    return int(load_library().logra_payload_header_bytes(count))
+
+
+def payload_apply(payload, header, entries, Ws):
+    """Receiver side: W_j <- merge of entry j for every entry of a parsed
+    payload (payload: the uint8 device tensor); Ws: the receiver's (d_j, k_j)
+    bf16 weights, in entry order."""
+    import torch
+
+    lib = load_library()
+    n = header.count
+    if len(Ws) != n:
+        raise ValueError(f"{n} weights needed, got {len(Ws)}")
+    ptrs = (ctypes.c_void_p * n)()
+    lds = (ctypes.c_int64 * n)()
+    for j, W in enumerate(Ws):
+        _need(W, torch.bfloat16, "W")
+        ptrs[j] = W.data_ptr() if W.numel() else None
+        lds[j] = _ld(W)
+    _check(lib.logra_payload_apply(payload.data_ptr(), payload.numel(), ctypes.byref(header), entries, ptrs, lds,
+                                   _stream_handle(payload)))
 
 
 def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):

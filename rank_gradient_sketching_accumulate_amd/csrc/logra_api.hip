@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#include <cstring>
 #include <unistd.h>
 
 #include <map>
@@ -666,6 +667,185 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
       if (e != hipSuccess) return hip_fail(e, "grouped merge launch");
     }
     return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+static_assert(sizeof(logra_payload_header) == 32, "payload header is 32 bytes");
+static_assert(sizeof(logra_payload_entry) == 48, "payload entry is 48 bytes");
+static_assert(LOGRA_PAYLOAD_MAX_ITEMS == kPayloadMaxItems, "one item limit");
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Offsets of the factors (and the total) for count items of d_j rows.
+void payload_layout(const int64_t* d, int32_t count, int32_t r, uint64_t* off, uint64_t* span, size_t* total) {
+  size_t o = up256(32 + 48 * (size_t)count);
+  for (int32_t j = 0; j < count; ++j) {
+    off[j] = o;
+    span[j] = up256((size_t)d[j] * (size_t)r * 4);
+    o += span[j];
+  }
+  *total = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t logra_payload_header_bytes(int32_t count) {
+  if (count < 1 || count > LOGRA_PAYLOAD_MAX_ITEMS) return 0;
+  return up256(32 + 48 * (size_t)count);
+}
+
+size_t logra_payload_bytes(const logra_merge_item* items, int32_t count, int32_t r) {
+  if (!items || count < 1 || count > LOGRA_PAYLOAD_MAX_ITEMS || r < 1 || r > LOGRA_MAX_RANK) return 0;
+  int64_t d[kPayloadMaxItems];
+  uint64_t off[kPayloadMaxItems], span[kPayloadMaxItems];
+  for (int32_t j = 0; j < count; ++j) {
+    if (items[j].d < 0 || items[j].k < 0) return 0;
+    d[j] = items[j].d;
+  }
+  size_t total = 0;
+  payload_layout(d, count, r, off, span, &total);
+  return total;
+}
+
+logra_status logra_payload_pack(const logra_merge_item* items, int32_t count, int32_t r, void* payload,
+                                size_t payload_bytes, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (count < 1 || count > LOGRA_PAYLOAD_MAX_ITEMS)
+      return fail(LOGRA_ERR_RANGE, "count must be in [1, " + std::to_string(LOGRA_PAYLOAD_MAX_ITEMS) + "]");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
+    if (!items || !payload) return fail(LOGRA_ERR_NULL, "items and payload must be non-null");
+    if ((uintptr_t)payload & 255) return fail(LOGRA_ERR_ALIGN, "payload must be 256-byte aligned");
+    PayloadPackArgs a{};
+    a.count = count;
+    a.r = r;
+    for (int32_t j = 0; j < count; ++j) {
+      const logra_merge_item& it = items[j];
+      const std::string tag = "item " + std::to_string(j) + ": ";
+      if (it.d < 0 || it.k < 0) return fail(LOGRA_ERR_SHAPE, tag + "d and k must be >= 0");
+      if (it.ldu < r) return fail(LOGRA_ERR_SHAPE, tag + "ldu must be >= r");
+      if (it.d > 0 && !it.U) return fail(LOGRA_ERR_NULL, tag + "U must be non-null");
+      if ((uintptr_t)it.U & 3) return fail(LOGRA_ERR_ALIGN, tag + "U must be 4-byte aligned");
+      if (!isfinite(it.scale)) return fail(LOGRA_ERR_RANGE, tag + "scale must be finite");
+      a.U[j] = it.U;
+      a.ldu[j] = it.ldu;
+      a.d[j] = it.d;
+    }
+    size_t total = 0;
+    payload_layout(a.d, count, r, a.off, a.span, &total);
+    if (payload_bytes < total) return fail(LOGRA_ERR_SHAPE, "payload_bytes is smaller than logra_payload_bytes");
+    for (int32_t j = 0; j < count; ++j)
+      if (overlaps(items[j].U, span_bytes(items[j].d, r, items[j].ldu, 4), payload, total))
+        return fail(LOGRA_ERR_ALIAS, "item " + std::to_string(j) + ": U overlaps the payload");
+    // Header and entries as little-endian words.
+    logra_payload_header h{};
+    h.magic = LOGRA_PAYLOAD_MAGIC;
+    h.version = LOGRA_PAYLOAD_VERSION;
+    h.count = count;
+    h.r = r;
+    h.total_bytes = total;
+    std::memcpy(a.head, &h, sizeof(h));
+    for (int32_t j = 0; j < count; ++j) {
+      logra_payload_entry e{};
+      e.seed = items[j].seed;
+      e.d = items[j].d;
+      e.k = items[j].k;
+      e.scale = items[j].scale;
+      e.u_offset = a.off[j];
+      std::memcpy(reinterpret_cast<char*>(a.head) + 32 + 48 * (size_t)j, &e, sizeof(e));
+    }
+    a.n_head_words = (32 + 48 * count) / 4;
+    a.header_words = (int)(a.off[0] / 4);
+    payload_pack_launch(a, payload, stream);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return hip_fail(err, "payload pack launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_payload_parse(const void* header_host, size_t bytes, logra_payload_header* header,
+                                 logra_payload_entry* entries, int32_t max_entries) {
+  try {
+    g_last_error.clear();
+    if (!header_host || !header) return fail(LOGRA_ERR_NULL, "header_host and header must be non-null");
+    if (bytes < sizeof(logra_payload_header)) return fail(LOGRA_ERR_SHAPE, "fewer bytes than a payload header");
+    logra_payload_header h;
+    std::memcpy(&h, header_host, sizeof(h));
+    if (h.magic != LOGRA_PAYLOAD_MAGIC) return fail(LOGRA_ERR_SHAPE, "not a payload (magic)");
+    if (h.version != LOGRA_PAYLOAD_VERSION) return fail(LOGRA_ERR_SHAPE, "unknown payload version");
+    if (h.reserved != 0) return fail(LOGRA_ERR_SHAPE, "header reserved word is not zero");
+    if (h.count < 1 || h.count > LOGRA_PAYLOAD_MAX_ITEMS) return fail(LOGRA_ERR_SHAPE, "entry count out of range");
+    if (h.r < 1 || h.r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_SHAPE, "rank out of range");
+    const size_t hb = up256(32 + 48 * (size_t)h.count);
+    if (bytes < 32 + 48 * (size_t)h.count) return fail(LOGRA_ERR_SHAPE, "header truncated before its entries end");
+    if (h.total_bytes < hb) return fail(LOGRA_ERR_SHAPE, "total bytes smaller than the header");
+    if (h.count > max_entries) return fail(LOGRA_ERR_RANGE, "more entries than max_entries");
+    if (!entries) return fail(LOGRA_ERR_NULL, "entries must be non-null");
+    logra_payload_entry es[kPayloadMaxItems];
+    for (int32_t j = 0; j < h.count; ++j) {
+      std::memcpy(&es[j], static_cast<const char*>(header_host) + 32 + 48 * (size_t)j, sizeof(logra_payload_entry));
+      const logra_payload_entry& e = es[j];
+      const std::string tag = "entry " + std::to_string(j) + ": ";
+      if (e.d < 0 || e.k < 0 || e.d > ((int64_t)1 << 31) || e.k > ((int64_t)1 << 31))
+        return fail(LOGRA_ERR_SHAPE, tag + "d or k out of range");
+      if (e.reserved0 != 0 || e.reserved1 != 0) return fail(LOGRA_ERR_SHAPE, tag + "reserved words are not zero");
+      if (!isfinite(e.scale)) return fail(LOGRA_ERR_SHAPE, tag + "scale is not finite");
+      const uint64_t n = (uint64_t)e.d * (uint64_t)h.r * 4;
+      if (e.u_offset % 256 || e.u_offset < hb || e.u_offset > h.total_bytes || n > h.total_bytes - e.u_offset)
+        return fail(LOGRA_ERR_SHAPE, tag + "factor outside the payload or misaligned");
+      for (int32_t i = 0; i < j; ++i) {
+        const uint64_t ni = (uint64_t)es[i].d * (uint64_t)h.r * 4;
+        if (n && ni && e.u_offset < es[i].u_offset + ni && es[i].u_offset < e.u_offset + n)
+          return fail(LOGRA_ERR_SHAPE, tag + "factor overlaps entry " + std::to_string(i) + "'s");
+      }
+    }
+    *header = h;
+    std::memcpy(entries, es, sizeof(logra_payload_entry) * (size_t)h.count);
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+logra_status logra_payload_apply(const void* payload, size_t payload_bytes, const logra_payload_header* header,
+                                 const logra_payload_entry* entries, void* const* W, const int64_t* ldw,
+                                 hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (!payload || !header || !entries || !W || !ldw)
+      return fail(LOGRA_ERR_NULL, "payload, header, entries, W and ldw must be non-null");
+    if (header->magic != LOGRA_PAYLOAD_MAGIC || header->version != LOGRA_PAYLOAD_VERSION)
+      return fail(LOGRA_ERR_SHAPE, "header is not a parsed payload header");
+    if (header->count < 1 || header->count > LOGRA_PAYLOAD_MAX_ITEMS || header->r < 1 || header->r > LOGRA_MAX_RANK)
+      return fail(LOGRA_ERR_SHAPE, "header count or rank out of range");
+    if (payload_bytes < header->total_bytes) return fail(LOGRA_ERR_SHAPE, "payload_bytes below the header's total");
+    if ((uintptr_t)payload & 255) return fail(LOGRA_ERR_ALIGN, "payload must be 256-byte aligned");
+    logra_merge_item items[kPayloadMaxItems];
+    for (int32_t j = 0; j < header->count; ++j) {
+      const logra_payload_entry& e = entries[j];
+      const uint64_t n = (uint64_t)e.d * (uint64_t)header->r * 4;
+      if (e.d < 0 || e.k < 0 || e.u_offset > header->total_bytes || n > header->total_bytes - e.u_offset)
+        return fail(LOGRA_ERR_SHAPE, "entry " + std::to_string(j) + ": factor outside the payload");
+      items[j].W = W[j];
+      items[j].ldw = ldw[j];
+      items[j].U = reinterpret_cast<const float*>(static_cast<const char*>(payload) + e.u_offset);
+      items[j].ldu = header->r;
+      items[j].d = e.d;
+      items[j].k = e.k;
+      items[j].seed = e.seed;
+      items[j].scale = e.scale;
+    }
+    return logra_merge_update_grouped(items, header->count, header->r, stream);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }

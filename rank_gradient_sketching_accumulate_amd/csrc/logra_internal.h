@@ -129,6 +129,26 @@ struct MergeGroup {
 bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s);
 
 // ---------------------------------------------------------------------------
+// Sync payload packing: header and entry words (little-endian u32 words of
+// the documented layout), and per factor its source, rows, byte offset and
+// slot size in the payload.
+// ---------------------------------------------------------------------------
+constexpr int kPayloadMaxItems = 32;
+constexpr int kPayloadHeadWords = (32 + 48 * kPayloadMaxItems) / 4;
+struct PayloadPackArgs {
+  uint32_t head[kPayloadHeadWords];
+  int n_head_words;  // words of header + entries actually used
+  int header_words;  // words of the header region (a 256-byte multiple)
+  int count, r;
+  const float* U[kPayloadMaxItems];
+  int64_t ldu[kPayloadMaxItems];
+  int64_t d[kPayloadMaxItems];
+  uint64_t off[kPayloadMaxItems];   // byte offset of the factor's slot
+  uint64_t span[kPayloadMaxItems];  // bytes of the slot (d r 4 rounded up to 256)
+};
+void payload_pack_launch(const PayloadPackArgs& a, void* payload, hipStream_t s);
+
+// ---------------------------------------------------------------------------
 // Predicted KL (equation 6): per-row softmax-weighted variance of the score
 // rates, then q.
 // ---------------------------------------------------------------------------

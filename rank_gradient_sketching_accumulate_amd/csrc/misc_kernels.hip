@@ -255,4 +255,40 @@ void zero_fill_launch(void* dst, int64_t n16, hipStream_t s) {
   hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<u32x4*>(dst), n16);
 }
 
+// Payload packing (the sync payload of the merge: header, entries, factors).
+// Block row j copies factor j (d_j x r fp32, row stride ldu_j) into its
+// packed slot (row stride r) and zeroes the slot's 256-byte tail; block
+// (0, 0) also writes the header and entry words from the kernel arguments
+// and zeroes the rest of the header region, so every byte of the payload is
+// defined.
+__global__ __launch_bounds__(256) void payload_pack_kernel(PayloadPackArgs a, uint8_t* __restrict__ payload) {
+  const int j = blockIdx.y;
+  if (blockIdx.x == 0 && j == 0) {
+    uint32_t* hw = reinterpret_cast<uint32_t*>(payload);
+    for (int w = threadIdx.x; w < a.header_words; w += 256) hw[w] = w < a.n_head_words ? a.head[w] : 0u;
+  }
+  const int64_t n = a.d[j] * a.r;            // floats of the factor
+  const int64_t span = a.span[j] / 4;        // floats of its slot (256-byte multiple)
+  float* dst = reinterpret_cast<float*>(payload + a.off[j]);
+  const float* src = a.U[j];
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < span; e += (int64_t)gridDim.x * 256) {
+    float v = 0.f;
+    if (e < n) {
+      const int64_t row = e / a.r;
+      v = src[row * a.ldu[j] + (e - row * a.r)];
+    }
+    dst[e] = v;
+  }
+}
+
+void payload_pack_launch(const PayloadPackArgs& a, void* payload, hipStream_t s) {
+  int64_t most = 1;
+  for (int j = 0; j < a.count; ++j) most = a.span[j] / 4 > most ? a.span[j] / 4 : most;
+  int64_t gx = (most + 255) / 256;
+  if (gx > 1024) gx = 1024;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL(payload_pack_kernel, dim3((unsigned)gx, (unsigned)a.count), dim3(256), 0, s, a,
+                     static_cast<uint8_t*>(payload));
+}
+
 }  // namespace logra

@@ -295,3 +295,110 @@ def test_python_wrapper_type_checks(lib):
         lg.sketch_accumulate(X, X, 0, 4, S)  # host tensors are refused
     with pytest.raises(TypeError):
         lg.sketch_accumulate(X.float(), X, 0, 4, S)
+
+
+# ---------------------------------------------------------------------------
+# Sync payload: host-side layout and checks (no device work).
+# ---------------------------------------------------------------------------
+import struct  # noqa: E402
+
+
+def _payload_header(count=2, r=64, entries=None, magic=0x5052474C, version=1, total=None, reserved=0):
+    """The documented layout written out with struct: header, then entries."""
+    hb = (32 + 48 * count + 255) // 256 * 256
+    if entries is None:
+        entries = []
+        off = hb
+        for j in range(count):
+            d, k = 100 + j, 300 + j
+            entries.append((1000 + j, d, k, 1e-3 * (j + 1), 0, off, 0))
+            off += (d * r * 4 + 255) // 256 * 256
+        total = off if total is None else total
+    b = struct.pack("<IIiiQQ", magic, version, count, r, total, reserved)
+    for e in entries:
+        b += struct.pack("<qqqfIQQ", *e)
+    return b + bytes(hb - len(b)), entries, total
+
+
+def _parse(lib, b, max_entries=32):
+    from rank_gradient_sketching_accumulate_amd import PayloadEntry, PayloadHeader
+
+    h = PayloadHeader()
+    es = (PayloadEntry * 32)()
+    st = lib.logra_payload_parse(b, len(b), ctypes.byref(h), es, max_entries)
+    return st, h, es
+
+
+def test_payload_layout_sizes(lib):
+    from rank_gradient_sketching_accumulate_amd import MergeItem
+
+    assert lib.logra_payload_header_bytes(0) == 0
+    assert lib.logra_payload_header_bytes(1) == 256
+    assert lib.logra_payload_header_bytes(4) == 256  # 32 + 192 bytes
+    assert lib.logra_payload_header_bytes(5) == 512  # 32 + 240 bytes
+    assert lib.logra_payload_header_bytes(33) == 0
+    items = (MergeItem * 2)()
+    items[0].d, items[0].k, items[1].d, items[1].k = 100, 300, 7, 5
+    assert lib.logra_payload_bytes(items, 2, 64) == 256 + 25600 + 1792
+    assert lib.logra_payload_bytes(items, 2, 0) == 0
+    assert lib.logra_payload_bytes(items, 0, 64) == 0
+    items[1].d = -1
+    assert lib.logra_payload_bytes(items, 2, 64) == 0
+
+
+def test_payload_parse_reads_documented_layout(lib):
+    b, entries, total = _payload_header()
+    st, h, es = _parse(lib, b)
+    assert st == OK, lib.logra_last_error()
+    assert (h.magic, h.version, h.count, h.r, h.total_bytes) == (0x5052474C, 1, 2, 64, total)
+    for j, e in enumerate(entries):
+        assert (es[j].seed, es[j].d, es[j].k, es[j].u_offset) == (e[0], e[1], e[2], e[5])
+        assert es[j].scale == pytest.approx(e[3], rel=1e-7)
+
+
+def test_payload_parse_rejects_malformed(lib):
+    good, entries, total = _payload_header()
+    assert _parse(lib, good[:31])[0] == ERR_SHAPE  # shorter than a header
+    assert _parse(lib, good[:32 + 48])[0] == ERR_SHAPE  # second entry cut off
+    assert _parse(lib, _payload_header(magic=0x12345678)[0])[0] == ERR_SHAPE
+    assert _parse(lib, _payload_header(version=2)[0])[0] == ERR_SHAPE
+    assert _parse(lib, _payload_header(reserved=1)[0])[0] == ERR_SHAPE
+    assert _parse(lib, _payload_header(r=513)[0])[0] == ERR_SHAPE
+    assert _parse(lib, good, max_entries=1)[0] == ERR_RANGE
+    bad = list(entries)
+    bad[1] = bad[1][:5] + (bad[1][5] + 8,) + bad[1][6:]  # misaligned factor
+    assert _parse(lib, _payload_header(entries=bad, total=total)[0])[0] == ERR_SHAPE
+    bad = list(entries)
+    bad[1] = bad[1][:5] + (entries[0][5],) + bad[1][6:]  # overlaps entry 0's factor
+    assert _parse(lib, _payload_header(entries=bad, total=total)[0])[0] == ERR_SHAPE
+    assert _parse(lib, _payload_header(entries=entries, total=total - 256)[0])[0] == ERR_SHAPE  # past the end
+    bad = list(entries)
+    bad[0] = (bad[0][0], -1) + bad[0][2:]
+    assert _parse(lib, _payload_header(entries=bad, total=total)[0])[0] == ERR_SHAPE
+    bad = list(entries)
+    bad[0] = bad[0][:3] + (float("inf"),) + bad[0][4:]
+    assert _parse(lib, _payload_header(entries=bad, total=total)[0])[0] == ERR_SHAPE
+
+
+def test_payload_pack_and_apply_validation(lib):
+    from rank_gradient_sketching_accumulate_amd import MergeItem, PayloadEntry, PayloadHeader
+
+    items = (MergeItem * 2)()
+    for j in range(2):
+        items[j].U, items[j].ldu, items[j].d, items[j].k, items[j].scale = FAKE * (1 + j), 64, 10, 20, 1e-3
+    assert lib.logra_payload_pack(items, 0, 64, FAKE * 64, 1 << 20, None) == ERR_RANGE
+    assert lib.logra_payload_pack(items, 2, 513, FAKE * 64, 1 << 20, None) == ERR_RANGE
+    assert lib.logra_payload_pack(None, 2, 64, FAKE * 64, 1 << 20, None) == ERR_NULL
+    assert lib.logra_payload_pack(items, 2, 64, FAKE * 64 + 16, 1 << 20, None) == ERR_ALIGN
+    assert lib.logra_payload_pack(items, 2, 64, FAKE * 64, 100, None) == ERR_SHAPE
+    items[1].ldu = 32
+    assert lib.logra_payload_pack(items, 2, 64, FAKE * 64, 1 << 20, None) == ERR_SHAPE
+    items[1].ldu = 64
+    items[1].U = FAKE * 64 + 256  # inside the payload
+    assert lib.logra_payload_pack(items, 2, 64, FAKE * 64, 1 << 20, None) == ERR_ALIAS
+    h = PayloadHeader()
+    es = (PayloadEntry * 2)()
+    W = (ctypes.c_void_p * 2)(FAKE, FAKE * 2)
+    ld = (ctypes.c_int64 * 2)(20, 20)
+    assert lib.logra_payload_apply(FAKE * 64, 1 << 20, ctypes.byref(h), es, W, ld, None) == ERR_SHAPE  # unparsed
+    assert lib.logra_payload_apply(None, 1 << 20, ctypes.byref(h), es, W, ld, None) == ERR_NULL

@@ -98,15 +98,61 @@ def test_grouped_matches_oracle():
         assert_weight_close(f64(W), ref, bound=update_error_bound(f64(U), r, scale))
 
 
-def test_sync_apply_trainer_and_receiver_agree():
-    """Trainer and rollout copies of a layer, merged from the same factors
-    and seeds (one grouped call each), stay bitwise identical."""
+def test_sync_payload_receiver_ends_bitwise_equal_to_trainer():
+    """Algorithm 1's synchronisation through the payload: the trainer merges
+    a 1.5B-class layer's seven matrices (grouped), packs each factor U with
+    its seed, shape and alpha*eta, and the bytes travel through host memory
+    to a separate device buffer; the receiver parses the header from its host
+    copy, applies the payload to its own copy of the weights and ends
+    bitwise equal to the trainer, and both match the oracle."""
     r = 128
     items = _items(LAYER_1P5B, r, 5)
-    recv = [(W.clone(), U.clone(), seed, scale) for W, U, seed, scale in items]
-    lg.merge_update_grouped(items, r)
-    lg.merge_update_grouped(recv, r)
+    recv_W = [W.clone() for W, _, _, _ in items]
+    W0 = [f64(W) for W, _, _, _ in items]
+    factors = [(U, seed, scale, W.shape[1]) for W, U, seed, scale in items]
+    lg.merge_update_grouped(items, r)  # the trainer's update
+    payload = lg.payload_pack(factors, r)
+    again = lg.payload_pack(factors, r)
     torch.cuda.synchronize()
-    for (W, _, _, _), (Wr, _, _, _) in zip(items, recv):
+    assert torch.equal(payload, again), "packing is not deterministic"
+    wire = payload.cpu().numpy().tobytes()  # the transport
+    assert len(wire) == lg.payload_bytes(factors, r)
+    received = torch.frombuffer(bytearray(wire), dtype=torch.uint8).to(DEV)
+    header, entries = lg.payload_parse(wire[: lg.payload_header_bytes(len(factors))])
+    assert (header.count, header.r, header.total_bytes) == (len(items), r, len(wire))
+    for j, (W, U, seed, scale) in enumerate(items):
+        e = entries[j]
+        assert (e.seed, e.d, e.k) == (seed, W.shape[0], W.shape[1])
+        assert e.scale == np.float32(scale)
+        # the factor travels bit for bit, rows packed
+        got = np.frombuffer(wire, dtype=np.float32, count=W.shape[0] * r, offset=e.u_offset).reshape(-1, r)
+        np.testing.assert_array_equal(got, U.cpu().numpy())
+    lg.payload_apply(received, header, entries, recv_W)
+    torch.cuda.synchronize()
+    for j, ((W, U, seed, scale), Wr) in enumerate(zip(items, recv_W)):
+        assert torch.equal(W, Wr), f"matrix {j}: receiver differs from trainer"
+    for j in (0, 4, 6):
+        W, U, seed, scale = items[j]
+        rows = np.arange(0, W.shape[0], 17)
+        A = oracle.rademacher_projection(seed, r, W.shape[1])
+        Ur = f64(U)[rows]
+        assert_weight_close(f64(recv_W[j])[rows], oracle.merge_update(W0[j][rows], Ur, A, scale),
+                            bound=update_error_bound(Ur, r, scale))
+
+
+def test_sync_payload_rank_512_and_empty_rows():
+    """A payload at r = 512 with a matrix of zero rows among the others."""
+    r = 512
+    shapes = [(300, 1032, 1e-3), (0, 520, 1e-3), (64, 2048, -5e-4)]
+    items = _items([s for s in shapes if s[0] > 0], r, 77)
+    items.insert(1, (torch.empty((0, 520), dtype=torch.bfloat16, device=DEV),
+                     torch.empty((0, r), dtype=torch.float32, device=DEV), 9, 1e-3))
+    recv_W = [W.clone() for W, _, _, _ in items]
+    lg.merge_update_grouped(items, r)
+    payload = lg.payload_pack([(U, seed, scale, W.shape[1]) for W, U, seed, scale in items], r)
+    received = payload.clone()
+    header, entries = lg.payload_parse(payload.cpu().numpy().tobytes())
+    lg.payload_apply(received, header, entries, recv_W)
+    torch.cuda.synchronize()
+    for (W, _, _, _), Wr in zip(items, recv_W):
         assert torch.equal(W, Wr)
-    np.testing.assert_array_equal(f64(items[0][1]), f64(recv[0][1]))
