@@ -20,6 +20,9 @@ from .logra_oracle import (  # noqa: F401
     sign_bits,
     sign_matrix,
     rademacher_projection,
+    gaussian_normals,
+    gaussian_projection,
+    GAUSS_PER_BLOCK,
     bf16_bits_to_f64,
     round_to_bf16,
     f64_to_bf16_bits,

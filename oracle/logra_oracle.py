@@ -117,6 +117,59 @@ def rademacher_projection(seed: int, r: int, k: int) -> np.ndarray:
     return sign_matrix(seed, r, k).astype(np.float64) / math.sqrt(r)
 
 
+GAUSS_PER_BLOCK = 8  # normals per Philox4x64 block: four Box-Muller pairs
+
+
+def gaussian_normals(seed: int, r: int, k: int) -> np.ndarray:
+    """Z[i, j] ~ N(0, 1) for i < r, j < k (float64): the entries of the
+    refreshed Gaussian basis that the LoGRA paper compares with the
+    Rademacher one (section 3.4.1, Figure 5c: "refreshed Rademacher and
+    Gaussian projections resample at every update").  The pages name no
+    generator; this library's choice, drawn from the same Philox stream as the
+    signs but a separate counter range (counter word 2 = 1):
+
+      block    = Philox4x64-10(counter = (j // 8, i, 1, 0), key = (seed, 0))
+      halves   h[2m] = low 32 bits of output word m, h[2m+1] = high 32 bits
+      pair     p = (j % 8) // 2 uses h[2p] and h[2p+1]
+      uniforms u1 = ((h[2p] >> 8) + 1) / 2^24 in (0, 1],
+               u2 = (h[2p+1] >> 8) / 2^24 in [0, 1)   (24-bit, exact in fp32)
+      Box-Muller (Box and Muller, 1958): R = sqrt(-2 ln u1), theta = 2 pi u2,
+               Z = R cos(theta) for even j % 8, R sin(theta) for odd.
+    """
+    if r < 0 or k < 0:
+        raise ValueError("r and k must be non-negative")
+    if r == 0 or k == 0:
+        return np.zeros((r, k))
+    nblk = (k + GAUSS_PER_BLOCK - 1) // GAUSS_PER_BLOCK
+    rows = np.empty((r, nblk), dtype=object)
+    cols = np.empty((r, nblk), dtype=object)
+    one = np.empty((r, nblk), dtype=object)
+    zero = np.empty((r, nblk), dtype=object)
+    for i in range(r):
+        for c in range(nblk):
+            rows[i, c] = i
+            cols[i, c] = c
+            one[i, c] = 1
+            zero[i, c] = 0
+    words = philox4x64_10((cols, rows, one, zero), (seed & MASK64, 0))
+    w = np.stack([np.asarray(wd, dtype=np.uint64) for wd in words], axis=-1)  # (r, nblk, 4)
+    halves = w.astype("<u8").view("<u4").reshape(r, nblk, 8).astype(np.int64)  # h[2m] = low half of word m
+    u1 = ((halves[:, :, 0::2] >> 8) + 1).astype(np.float64) / 2.0**24
+    u2 = (halves[:, :, 1::2] >> 8).astype(np.float64) / 2.0**24
+    R = np.sqrt(-2.0 * np.log(u1))
+    theta = 2.0 * math.pi * u2
+    z = np.empty((r, nblk, 8))
+    z[:, :, 0::2] = R * np.cos(theta)
+    z[:, :, 1::2] = R * np.sin(theta)
+    return np.ascontiguousarray(z.reshape(r, nblk * 8)[:, :k])
+
+
+def gaussian_projection(seed: int, r: int, k: int) -> np.ndarray:
+    """A = Z / sqrt(r) (entries N(0, 1/r), so E[A^T A] = I as for the
+    Rademacher basis); see ``gaussian_normals``."""
+    return gaussian_normals(seed, r, k) / math.sqrt(r)
+
+
 # ---------------------------------------------------------------------------
 # bfloat16 helpers (the layer tensors are bf16, as in the pages' BF16 runs,
 # LoGRA appendix D.1).
