@@ -130,6 +130,36 @@ logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx,
                                              hipStream_t stream);
 
 /*
+ * Projection basis (a setting of the calling thread; returns the previous
+ * one).  LOGRA_BASIS_RADEMACHER (default): A = s / sqrt(r) with the signs
+ * above.  LOGRA_BASIS_GAUSSIAN: the refreshed Gaussian basis the paper
+ * compares with it (section 3.4.1, Figure 5c), A = Z / sqrt(r) with Z[i][j]
+ * ~ N(0, 1) drawn from the same Philox stream in its own counter range:
+ *   block  = Philox4x64-10(counter = (j / 8, i, 1, 0), key = (seed, 0)),
+ *            halves h[2m] = low and h[2m+1] = high 32 bits of word m;
+ *   pair p = (j mod 8) / 2: u1 = ((h[2p] >> 8) + 1) / 2^24,
+ *            u2 = (h[2p+1] >> 8) / 2^24;
+ *   Z = sqrt(-2 ln u1) cos(2 pi u2) for even j mod 8, sin for odd (Box and
+ *   Muller, 1958), computed in fp32 and carried as bf16 hi/lo pairs.
+ * Applies to logra_sketch_accumulate, logra_project, logra_merge_update,
+ * logra_merge_update_grouped and logra_payload_pack (which records it per
+ * entry).  With the Gaussian basis those calls generate the basis planes
+ * (2 bf16 per entry of A, 4 r k bytes for the projection or the merge) into
+ * a per-stream region like the other scratch, so the merges then allocate on
+ * first use too (see logra_workspace_reserve); logra_sketch_accumulate_noalloc
+ * refuses it (LOGRA_ERR_RANGE).  The grouped merge runs one launch per
+ * matrix under this basis.
+ *
+ * logra_basis_normals: writes Z (fp32, r x k, row-major, unscaled) of the
+ * Gaussian basis for `seed` into the device buffer `out` (test and debug aid,
+ * like logra_signs).
+ */
+#define LOGRA_BASIS_RADEMACHER 0
+#define LOGRA_BASIS_GAUSSIAN 1
+int logra_set_basis(int basis);
+logra_status logra_basis_normals(uint64_t seed, int32_t r, int64_t k, float* out, hipStream_t stream);
+
+/*
  * Bitwise-reproducible sketches (off by default; a setting of the calling
  * thread).  Atomic adds from several workgroups into the same S entries
  * make S depend on their order at the level of fp32 rounding; any such
@@ -280,7 +310,8 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
  *                  (LOGRA_PAYLOAD_VERSION), i32 count, i32 r, u64 total
  *                  bytes, u64 zero;
  *   bytes 32..     count entries of 48 bytes (logra_payload_entry): u64 seed,
- *                  i64 d, i64 k, f32 scale (alpha * eta), u32 zero, u64 byte
+ *                  i64 d, i64 k, f32 scale (alpha * eta), u32 basis (the
+ *                  packing thread's logra_set_basis setting), u64 byte
  *                  offset of the entry's factor, u64 zero;
  *   from logra_payload_header_bytes(count) (a multiple of 256): each factor U
  *                  as fp32 d x r, rows packed (row stride r), at its offset
@@ -306,7 +337,8 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
  *   room).  LOGRA_ERR_SHAPE for a malformed or truncated header,
  *   LOGRA_ERR_RANGE when count exceeds max_entries.
  * logra_payload_apply: the receiver's merge: W_j <- RNE_bf16(W_j - scale_j
- *   (1/sqrt(r)) U_j s(seed_j)) for every entry, through
+ *   (1/sqrt(r)) U_j A(seed_j)) for every entry, in the entry's basis
+ *   (whatever the calling thread's setting), through
  *   logra_merge_update_grouped with U_j read from the device payload
  *   (`payload_bytes` bytes) at entry j's offset.  W[j] and ldw[j] are the
  *   receiver's weights (host arrays of count pointers and strides); the
@@ -325,7 +357,7 @@ typedef struct {
   uint64_t seed;
   int64_t d, k;
   float scale;
-  uint32_t reserved0;
+  uint32_t basis;   /* LOGRA_BASIS_RADEMACHER or LOGRA_BASIS_GAUSSIAN */
   uint64_t u_offset;
   uint64_t reserved1;
 } logra_payload_entry;

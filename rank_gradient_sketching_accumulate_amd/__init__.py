@@ -35,6 +35,10 @@ __all__ = [
     "merge_update",
     "merge_update_grouped",
     "payload_bytes",
+    "set_basis",
+    "basis_normals",
+    "BASIS_RADEMACHER",
+    "BASIS_GAUSSIAN",
     "payload_header_bytes",
     "payload_pack",
     "payload_parse",
@@ -64,6 +68,8 @@ EXPORTED_SYMBOLS = (
     "logra_sketch_accumulate_noalloc",
     "logra_set_deterministic",
     "logra_set_precision",
+    "logra_set_basis",
+    "logra_basis_normals",
     "logra_projection_bytes",
     "logra_project",
     "logra_contract",
@@ -138,7 +144,7 @@ class PayloadEntry(ctypes.Structure):
 
     _fields_ = [
         ("seed", ctypes.c_uint64), ("d", ctypes.c_int64), ("k", ctypes.c_int64),
-        ("scale", ctypes.c_float), ("reserved0", ctypes.c_uint32),
+        ("scale", ctypes.c_float), ("basis", ctypes.c_uint32),
         ("u_offset", ctypes.c_uint64), ("reserved1", ctypes.c_uint64),
     ]
 
@@ -166,6 +172,10 @@ def _declare(lib):
     lib.logra_merge_update.restype = ctypes.c_int
     lib.logra_merge_update_grouped.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32, c_vp]
     lib.logra_merge_update_grouped.restype = ctypes.c_int
+    lib.logra_set_basis.argtypes = [ctypes.c_int]
+    lib.logra_set_basis.restype = ctypes.c_int
+    lib.logra_basis_normals.argtypes = [c_u64, c_i32, c_i64, c_vp, c_vp]
+    lib.logra_basis_normals.restype = ctypes.c_int
     lib.logra_payload_header_bytes.argtypes = [c_i32]
     lib.logra_payload_header_bytes.restype = ctypes.c_size_t
     lib.logra_payload_bytes.argtypes = [ctypes.POINTER(MergeItem), c_i32, c_i32]
@@ -323,6 +333,26 @@ def set_deterministic(enable: bool) -> bool:
     """Bitwise-reproducible sketches on the calling thread (one workgroup per
     row tile of S, no atomic adds; slower).  Returns the previous setting."""
     return bool(load_library().logra_set_deterministic(1 if enable else 0))
+
+
+BASIS_RADEMACHER = 0
+BASIS_GAUSSIAN = 1
+
+
+def set_basis(basis: int) -> int:
+    """Projection basis of the calling thread (BASIS_RADEMACHER or
+    BASIS_GAUSSIAN); returns the previous one."""
+    return int(load_library().logra_set_basis(int(basis)))
+
+
+def basis_normals(seed: int, r: int, k: int, device="cuda"):
+    """Z (r, k) float32 of the Gaussian basis for `seed` (unscaled)."""
+    import torch
+
+    out = torch.empty((r, k), dtype=torch.float32, device=device)
+    _check(load_library().logra_basis_normals(ctypes.c_uint64(seed & (2**64 - 1)), r, k,
+                                              out.data_ptr() if out.numel() else None, _stream_handle(out)))
+    return out
 
 
 PRECISION_BF16X2 = 0

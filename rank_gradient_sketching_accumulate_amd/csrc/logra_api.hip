@@ -49,7 +49,14 @@ size_t span_bytes(int64_t rows, int64_t cols, int64_t ld, size_t elem) {
 // it.  Retired and current buffers are freed only by logra_workspace_release.
 // Growing is refused while the stream is being captured (allocation and
 // clearing are not capturable); logra_workspace_reserve grows it beforehand.
-enum ArenaKind { kArenaSketch = 0, kArenaRowAdam = 1, kArenaKL = 2, kArenaCounters = 3, kArenaKinds = 4 };
+enum ArenaKind {
+  kArenaSketch = 0,
+  kArenaRowAdam = 1,
+  kArenaKL = 2,
+  kArenaCounters = 3,
+  kArenaBasis = 4,  // Gaussian basis planes
+  kArenaKinds = 5
+};
 struct Arena {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -132,7 +139,11 @@ SketchPlan sketch_plan_for(int64_t T, int64_t k, int64_t d, int r, bool ho) {
   return pl;
 }
 
+// Per-thread switch of logra_set_basis: the Gaussian basis instead of signs.
+thread_local bool g_basis_gauss = false;
+
 MergePlan merge_plan_for(int64_t d, int64_t k, int r) {
+  if (g_basis_gauss) return plan_merge(d, k, r, true);
   if (plan_overrides_present()) return plan_merge(d, k, r);
   thread_local std::map<std::tuple<int64_t, int64_t, int>, MergePlan> plans;
   const auto key = std::make_tuple(d, k, r);
@@ -177,6 +188,42 @@ logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t ld
   return LOGRA_OK;
 }
 
+// Gaussian basis planes (bf16 hi and lo) of rp rows x kpad columns: bytes,
+// and generation into the basis region (which the caller has already grown
+// to at least that size).
+size_t basis_bytes(int rp, int64_t kpad) { return (size_t)2 * rp * (size_t)kpad * 2; }
+int64_t basis_kpad_proj(int64_t k) { return (k + 31) / 32 * 32; }
+int64_t basis_kpad_merge(int64_t k) { return (k + 127) / 128 * 128; }
+
+logra_status basis_generate(uint64_t seed, int row0, int rr, int rp, int64_t k, int64_t kpad, bool col_major,
+                            hipStream_t stream, uint16_t** hi, uint16_t** lo) {
+  void* p = nullptr;
+  logra_status st = arena_get(kArenaBasis, stream, basis_bytes(rp, kpad), &p);
+  if (st != LOGRA_OK) return st;
+  GaussBasisParams gp{};
+  gp.seed = seed;
+  gp.row0 = row0;
+  gp.rr = rr;
+  gp.RP = rp;
+  gp.k = k;
+  gp.kpad = kpad;
+  uint16_t* h = static_cast<uint16_t*>(p);
+  uint16_t* l = h + (size_t)rp * (size_t)kpad;
+  if (col_major) {
+    gp.Athi = h;
+    gp.Atlo = l;
+  } else {
+    gp.Ahi = h;
+    gp.Alo = l;
+  }
+  gauss_basis_launch(gp, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "basis launch");
+  *hi = h;
+  *lo = l;
+  return LOGRA_OK;
+}
+
 // P = X s^T into the hi/lo planes (Pk order); tokens in [T, Tpad) get zeros.
 // hi_only: the fused call contracts with P rounded once to bf16: its
 // projection writes no low plane when the contraction reads none (the
@@ -186,9 +233,32 @@ logra_status check_plan(const SketchPlan& pl, int64_t T, int64_t ldx, int64_t ld
 // them from the library's per-stream region.
 // row0: the sign row of P's first column (256 for the upper half of a rank
 // above 256).
+// With the Gaussian basis (g_basis_gauss) the basis planes of this half are
+// generated into the basis region first and proj_gauss_kernel runs instead.
 logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X, int64_t ldx, int64_t T, int64_t k,
                                 uint64_t seed, int r, int row0, uint16_t* Phi, uint16_t* Plo, bool hi_only,
                                 hipStream_t stream, unsigned* counters = nullptr) {
+  if (g_basis_gauss) {
+    const int rp = 16 * pl.NB;
+    const int64_t kpad = basis_kpad_proj(k);
+    uint16_t *ah = nullptr, *al = nullptr;
+    logra_status st = basis_generate(seed, row0, r, rp, k, kpad, false, stream, &ah, &al);
+    if (st != LOGRA_OK) return st;
+    ProjParams gp{};
+    gp.X = static_cast<const uint16_t*>(X);
+    gp.ldx = ldx; gp.T = T; gp.k = k; gp.seed = seed; gp.r = r; gp.row0 = row0;
+    gp.Phi = Phi;
+    gp.Plo = Plo;
+    gp.Ahi = ah;
+    gp.Alo = al;
+    gp.kpad = kpad;
+    gp.Tw = (T + 31) / 32 * 32;
+    gp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
+    if (!proj_gauss_launch(pl, gp, stream)) return fail(LOGRA_ERR_RANGE, "no Gaussian projection kernel for this rank");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "Gaussian projection launch");
+    return LOGRA_OK;
+  }
   ProjParams pp{};
   pp.X = static_cast<const uint16_t*>(X);
   pp.ldx = ldx; pp.T = T; pp.k = k; pp.seed = seed; pp.r = r; pp.row0 = row0;
@@ -307,6 +377,8 @@ size_t cache_bytes(int64_t T, int r) {
 }
 size_t cache_half_offset(int64_t T, int h) { return h == 0 ? 0 : projection_cache_bytes(T, kHalfRank); }
 
+
+
 // Argument checks of the fused sketch calls; *empty: nothing to do.
 logra_status check_sketch_args(const void* X, int64_t ldx, const void* dY, int64_t lddy, int64_t T, int64_t k,
                                int64_t d, int32_t r, const float* S, int64_t lds, bool* empty) {
@@ -374,6 +446,8 @@ logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx, const v
     bool empty = false;
     logra_status st = check_sketch_args(X, ldx, dY, lddy, T, k, d, r, S, lds, &empty);
     if (st != LOGRA_OK || empty) return st;
+    if (g_basis_gauss)
+      return fail(LOGRA_ERR_RANGE, "the Gaussian basis needs scratch for its planes: use logra_sketch_accumulate");
     // The plan of logra_sketch_accumulate, except that token splits of the
     // contraction add into S directly instead of parking partial tiles (the
     // scratch then holds P, the projection's column-split partials and the
@@ -457,6 +531,11 @@ logra_status logra_sketch_accumulate(const void* X, int64_t ldx, const void* dY,
       st = counters_get(stream, n_cnt, &cnt);
       if (st != LOGRA_OK) return st;
     }
+    if (g_basis_gauss) {
+      void* bp = nullptr;
+      st = arena_get(kArenaBasis, stream, basis_bytes(16 * pls[0].NB, basis_kpad_proj(k)), &bp);
+      if (st != LOGRA_OK) return st;
+    }
     char* base = static_cast<char*>(ws);
     for (int h = 0; h < n_halves(r); ++h) {
       const SketchPlan& pl = pls[h];
@@ -479,6 +558,38 @@ int logra_set_precision(int mode) {
   const int prev = g_precision_hi_only ? LOGRA_PRECISION_BF16 : LOGRA_PRECISION_BF16X2;
   g_precision_hi_only = mode == LOGRA_PRECISION_BF16;
   return prev;
+}
+
+int logra_set_basis(int basis) {
+  const int prev = g_basis_gauss ? LOGRA_BASIS_GAUSSIAN : LOGRA_BASIS_RADEMACHER;
+  g_basis_gauss = basis == LOGRA_BASIS_GAUSSIAN;
+  return prev;
+}
+
+logra_status logra_basis_normals(uint64_t seed, int32_t r, int64_t k, float* out, hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (k < 0) return fail(LOGRA_ERR_SHAPE, "k must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
+    if (k == 0) return LOGRA_OK;
+    if (!out) return fail(LOGRA_ERR_NULL, "out must be non-null");
+    if ((uintptr_t)out & 3) return fail(LOGRA_ERR_ALIGN, "out must be 4-byte aligned");
+    if ((uint64_t)r * (uint64_t)k >= ((uint64_t)1 << 31)) return fail(LOGRA_ERR_SHAPE, "r * k must be below 2^31");
+    GaussBasisParams gp{};
+    gp.seed = seed;
+    gp.row0 = 0;
+    gp.rr = r;
+    gp.RP = r;
+    gp.k = k;
+    gp.kpad = (k + 7) / 8 * 8;
+    gp.Z = out;
+    gauss_basis_launch(gp, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "basis launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
 }
 
 int logra_set_deterministic(int enable) {
@@ -534,6 +645,11 @@ logra_status logra_project(const void* X, int64_t ldx, int64_t T, int64_t k, uin
     if (n_cnt > 0) {
       unsigned* cnt = nullptr;
       st = counters_get(stream, n_cnt, &cnt);
+      if (st != LOGRA_OK) return st;
+    }
+    if (g_basis_gauss) {
+      void* bp = nullptr;
+      st = arena_get(kArenaBasis, stream, basis_bytes(16 * pls[0].NB, basis_kpad_proj(k)), &bp);
       if (st != LOGRA_OK) return st;
     }
     for (int h = 0; h < n_halves(r); ++h) {
@@ -603,6 +719,13 @@ logra_status logra_merge_update(void* W, int64_t ldw, const float* U, int64_t ld
     bool skip = false;
     logra_status st = prepare_merge(W, ldw, U, ldu, d, k, seed, r, scale, mp, pl, skip);
     if (st != LOGRA_OK || skip) return st;
+    if (g_basis_gauss) {
+      uint16_t *ah = nullptr, *al = nullptr;
+      st = basis_generate(seed, 0, r, 32 * pl.NK, k, basis_kpad_merge(k), true, stream, &ah, &al);
+      if (st != LOGRA_OK) return st;
+      mp.Athi = ah;
+      mp.Atlo = al;
+    }
     if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "merge launch");
@@ -651,6 +774,30 @@ logra_status logra_merge_update_grouped(const logra_merge_item* items, int32_t c
       mp.n_cr = pl.n_cr;
       mp.cr_cols = pl.cr_cols;
       mps.push_back(mp);
+    }
+    if (g_basis_gauss) {
+      // One merge per matrix, each after its basis planes (one region, reused
+      // in stream order; grown to the largest first).
+      size_t most = 0;
+      for (const MergeParams& mp : mps) most = std::max(most, basis_bytes(32 * pl0.NK, basis_kpad_merge(mp.k)));
+      void* bp = nullptr;
+      logra_status st = arena_get(kArenaBasis, stream, most, &bp);
+      if (st != LOGRA_OK) return st;
+      for (MergeParams mp : mps) {
+        uint16_t *ah = nullptr, *al = nullptr;
+        st = basis_generate(mp.seed, 0, r, 32 * pl0.NK, mp.k, basis_kpad_merge(mp.k), true, stream, &ah, &al);
+        if (st != LOGRA_OK) return st;
+        mp.Athi = ah;
+        mp.Atlo = al;
+        MergePlan pl = pl0;
+        pl.n_rb = mp.n_rb;
+        pl.n_cr = mp.n_cr;
+        pl.cr_cols = mp.cr_cols;
+        if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "merge launch");
+      }
+      return LOGRA_OK;
     }
     for (size_t b = 0; b < mps.size(); b += kMaxMergeGroup) {
       MergeGroup g{};
@@ -759,6 +906,7 @@ logra_status logra_payload_pack(const logra_merge_item* items, int32_t count, in
       e.d = items[j].d;
       e.k = items[j].k;
       e.scale = items[j].scale;
+      e.basis = g_basis_gauss ? LOGRA_BASIS_GAUSSIAN : LOGRA_BASIS_RADEMACHER;
       e.u_offset = a.off[j];
       std::memcpy(reinterpret_cast<char*>(a.head) + 32 + 48 * (size_t)j, &e, sizeof(e));
     }
@@ -798,7 +946,9 @@ logra_status logra_payload_parse(const void* header_host, size_t bytes, logra_pa
       const std::string tag = "entry " + std::to_string(j) + ": ";
       if (e.d < 0 || e.k < 0 || e.d > ((int64_t)1 << 31) || e.k > ((int64_t)1 << 31))
         return fail(LOGRA_ERR_SHAPE, tag + "d or k out of range");
-      if (e.reserved0 != 0 || e.reserved1 != 0) return fail(LOGRA_ERR_SHAPE, tag + "reserved words are not zero");
+      if (e.reserved1 != 0) return fail(LOGRA_ERR_SHAPE, tag + "reserved word is not zero");
+      if (e.basis != LOGRA_BASIS_RADEMACHER && e.basis != LOGRA_BASIS_GAUSSIAN)
+        return fail(LOGRA_ERR_SHAPE, tag + "unknown basis");
       if (!isfinite(e.scale)) return fail(LOGRA_ERR_SHAPE, tag + "scale is not finite");
       const uint64_t n = (uint64_t)e.d * (uint64_t)h.r * 4;
       if (e.u_offset % 256 || e.u_offset < hb || e.u_offset > h.total_bytes || n > h.total_bytes - e.u_offset)
@@ -845,7 +995,19 @@ logra_status logra_payload_apply(const void* payload, size_t payload_bytes, cons
       items[j].seed = e.seed;
       items[j].scale = e.scale;
     }
-    return logra_merge_update_grouped(items, header->count, header->r, stream);
+    // Each entry with its own basis: consecutive entries of one basis go to
+    // one grouped call under that basis.
+    const bool saved = g_basis_gauss;
+    logra_status st = LOGRA_OK;
+    for (int32_t j0 = 0; j0 < header->count && st == LOGRA_OK;) {
+      int32_t j1 = j0 + 1;
+      while (j1 < header->count && entries[j1].basis == entries[j0].basis) ++j1;
+      g_basis_gauss = entries[j0].basis == LOGRA_BASIS_GAUSSIAN;
+      st = logra_merge_update_grouped(items + j0, j1 - j0, header->r, stream);
+      j0 = j1;
+    }
+    g_basis_gauss = saved;
+    return st;
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
   }
@@ -992,7 +1154,7 @@ namespace {
 // thread's settings: the sketch region (the fused call's plan covers the
 // split calls' partials too), the split counters, and RowAdam's for d rows.
 struct WorkspaceNeed {
-  size_t sketch = 0, counters = 0, rowadam = 0;
+  size_t sketch = 0, counters = 0, rowadam = 0, basis = 0;
 };
 
 WorkspaceNeed workspace_need(int64_t T, int64_t k, int64_t d, int r) {
@@ -1010,6 +1172,11 @@ WorkspaceNeed workspace_need(int64_t T, int64_t k, int64_t d, int r) {
     scratch_layout(pc, d, false, true);
     w.sketch = std::max(w.sketch, pc.total);
   }
+  if (g_basis_gauss) {
+    const int nb0 = sketch_plan_for(T, k, d, half_rank(r, 0), g_precision_hi_only).NB;
+    const MergePlan mpl = merge_plan_for(d, k, r);
+    w.basis = std::max(basis_bytes(16 * nb0, basis_kpad_proj(k)), basis_bytes(32 * mpl.NK, basis_kpad_merge(k)));
+  }
   size_t a, b, c, e;
   w.rowadam = rowadam_layout(d, a, b, c, e);
   return w;
@@ -1023,7 +1190,7 @@ size_t logra_workspace_bytes(int64_t T, int64_t d, int64_t k, int32_t r) {
   if (T <= 0 || d <= 0 || k <= 0 || r < 1 || r > LOGRA_MAX_RANK) return 0;
   try {
     const WorkspaceNeed w = workspace_need(T, k, d, r);
-    return w.sketch + w.counters + w.rowadam;
+    return w.sketch + w.counters + w.rowadam + w.basis;
   } catch (...) {
     return 0;
   }
@@ -1041,6 +1208,10 @@ logra_status logra_workspace_reserve(int64_t T, int64_t d, int64_t k, int32_t r,
     if (st != LOGRA_OK) return st;
     st = arena_get(kArenaCounters, stream, w.counters, &p);
     if (st != LOGRA_OK) return st;
+    if (w.basis) {
+      st = arena_get(kArenaBasis, stream, w.basis, &p);
+      if (st != LOGRA_OK) return st;
+    }
     return arena_get(kArenaRowAdam, stream, w.rowadam, &p);
   } catch (...) {
     return fail(LOGRA_ERR_HIP, "unexpected C++ exception");

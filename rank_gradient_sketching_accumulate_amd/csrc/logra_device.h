@@ -44,13 +44,10 @@ __device__ __forceinline__ void mul_wide64(uint64_t a, uint64_t b, uint64_t& hi,
   lo = (p10 << 32) | (uint32_t)p00;
 }
 
-// 256 sign bits of sign row `row`, columns [256*cblk, 256*cblk + 256):
-// Philox4x64-10(counter = (cblk, row, 0, 0), key = (seed, 0)).  Word q of the
-// output holds columns 64q .. 64q+63, least significant bit first; w[2q] is
-// the low half of word q.  Bit 1 means sign -1.
-__device__ __forceinline__ void philox_sign_block(uint64_t seed, uint32_t row, uint32_t cblk,
-                                                  uint32_t w[8]) {
-  uint64_t x0 = cblk, x1 = row, x2 = 0, x3 = 0;
+// One Philox4x64-10 block for counter (c0, c1, c2, 0) and key (seed, 0), as
+// eight 32-bit halves: w[2q] is the low half of output word q.
+__device__ __forceinline__ void philox_block(uint64_t seed, uint64_t c0, uint64_t c1, uint64_t c2, uint32_t w[8]) {
+  uint64_t x0 = c0, x1 = c1, x2 = c2, x3 = 0;
   uint64_t k0 = seed, k1 = 0;
 #pragma unroll
   for (int rnd = 0; rnd < 10; ++rnd) {
@@ -72,6 +69,37 @@ __device__ __forceinline__ void philox_sign_block(uint64_t seed, uint32_t row, u
   w[2] = (uint32_t)x1; w[3] = (uint32_t)(x1 >> 32);
   w[4] = (uint32_t)x2; w[5] = (uint32_t)(x2 >> 32);
   w[6] = (uint32_t)x3; w[7] = (uint32_t)(x3 >> 32);
+}
+
+// 256 sign bits of sign row `row`, columns [256*cblk, 256*cblk + 256):
+// Philox4x64-10(counter = (cblk, row, 0, 0), key = (seed, 0)).  Word q of the
+// output holds columns 64q .. 64q+63, least significant bit first; w[2q] is
+// the low half of word q.  Bit 1 means sign -1.
+__device__ __forceinline__ void philox_sign_block(uint64_t seed, uint32_t row, uint32_t cblk,
+                                                  uint32_t w[8]) {
+  philox_block(seed, cblk, row, 0, w);
+}
+
+// Eight N(0, 1) values of the Gaussian basis, row `row`, columns
+// 8*blk .. 8*blk+7: the block Philox4x64-10(counter = (blk, row, 1, 0), key =
+// (seed, 0)) gives four Box-Muller pairs (Box and Muller, 1958), pair p from
+// halves 2p and 2p+1 as 24-bit uniforms u1 = ((h >> 8) + 1) / 2^24 (in
+// (0, 1], never 0) and u2 = (h >> 8) / 2^24; z[2p] = R cos(2 pi u2),
+// z[2p+1] = R sin(2 pi u2) with R = sqrt(-2 ln u1).  Both uniforms are exact
+// in fp32; sincospi takes 2 u2 exactly.
+__device__ __forceinline__ void gauss_block(uint64_t seed, uint32_t row, uint64_t blk, float z[8]) {
+  uint32_t w[8];
+  philox_block(seed, blk, row, 1, w);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float u1 = (float)((w[2 * p] >> 8) + 1u) * 0x1p-24f;
+    const float t = (float)(w[2 * p + 1] >> 8) * 0x1p-23f;  // 2 u2
+    const float R = sqrtf(-2.0f * logf(u1));
+    float sn, cs;
+    sincospif(t, &sn, &cs);
+    z[2 * p] = R * cs;
+    z[2 * p + 1] = R * sn;
+  }
 }
 
 // Eight sign bits (bit e -> element e, 1 = negative) to eight bf16 values

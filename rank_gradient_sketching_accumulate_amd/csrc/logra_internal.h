@@ -28,6 +28,11 @@ struct ProjParams {
   int hi_only;      // 0: write P's high and low planes; 1: the high plane only (the
                     // contraction reads no low plane); 2: high plane, zero low plane
   int row0;         // sign row of P's column 0 (256 for the upper half at ranks above 256)
+  // Gaussian basis (proj_gauss_kernel): A as bf16 hi/lo planes, 16*NB rows x
+  // kpad columns, row-major; P is written for tokens < Tw.
+  const uint16_t* Ahi;
+  const uint16_t* Alo;
+  int64_t kpad, Tw;
 };
 
 struct ContractParams {
@@ -103,6 +108,10 @@ struct MergeParams {
   int u_vec;        // U rows 16-byte aligned (ldu % 4 == 0, aligned base)
   uint64_t seed;
   float scale_eff;  // scale / sqrt(r)
+  // Gaussian basis: A^T as bf16 hi/lo planes, one row of 32*NK entries per
+  // column of W (rows up to the last chunk's end); null for signs.
+  const uint16_t* Athi;
+  const uint16_t* Atlo;
   int n_rb, n_cr;   // row blocks, column ranges
   int64_t cr_cols;  // columns per range (a multiple of the chunk width)
 };
@@ -115,7 +124,8 @@ struct MergePlan {
   int64_t cr_cols;
 };
 
-MergePlan plan_merge(int64_t d, int64_t k, int r);
+// gauss: the Gaussian basis (default tiling only; no tuning variables).
+MergePlan plan_merge(int64_t d, int64_t k, int r, bool gauss = false);
 bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s);
 
 // Up to kMaxMergeGroup matrices of one rank merged by one launch; matrix j
@@ -127,6 +137,26 @@ struct MergeGroup {
   MergeParams p[kMaxMergeGroup];
 };
 bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Gaussian basis (the refreshed Gaussian projection): Z for sign rows
+// row0 .. row0 + rr - 1 (rows up to RP - 1 and columns k .. kpad - 1 are
+// zero) as bf16 hi/lo planes, row-major A (RP x kpad) and/or column-major
+// At (kpad x RP), and/or fp32 Z (rr x k, row stride k).
+// ---------------------------------------------------------------------------
+struct GaussBasisParams {
+  uint64_t seed;
+  int row0, rr, RP;
+  int64_t k, kpad;
+  uint16_t* Ahi;
+  uint16_t* Alo;
+  uint16_t* Athi;
+  uint16_t* Atlo;
+  float* Z;
+};
+void gauss_basis_launch(const GaussBasisParams& p, hipStream_t s);
+// The projection with a Gaussian basis (P = X Z^T into the hi/lo planes).
+bool proj_gauss_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Sync payload packing: header and entry words (little-endian u32 words of

@@ -43,7 +43,10 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
 
 // The work of one workgroup: tile `lin` (row block lin / n_cr, column range
 // lin % n_cr) of the matrix p describes.
-template <int NBW, int CB, int NK, int PD>
+// GAUSS: the basis is the dense Gaussian one; its column-major bf16 hi/lo
+// planes (p.Athi, p.Atlo) feed the MFMA A operand directly and each product
+// takes three MFMAs (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-32 relative).
+template <int NBW, int CB, int NK, int PD, bool GAUSS = false>
 __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   constexpr int STR = 9;        // dwords per row of row-major bits (8 + 1 pad)
   constexpr int CSTR = NK < 8 ? 9 : NK + 1;  // dwords per column of column-major bits (odd)
@@ -155,7 +158,9 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
     __syncthreads();
   };
 
-  if (nch > 0) build_block(c_begin);
+  if constexpr (!GAUSS) {
+    if (nch > 0) build_block(c_begin);
+  }
 
   u32x4 uh[NK][NBW], ul[NK][NBW];
 #pragma unroll
@@ -180,7 +185,9 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
       const int ch = ch0 + u;
       if (ch < nch) {
         const int64_t col0 = c_begin + (int64_t)ch * CW;
-        if (ch > 0 && (col0 & 255) == 0) build_block(col0);
+        if constexpr (!GAUSS) {
+          if (ch > 0 && (col0 & 255) == 0) build_block(col0);
+        }
         const int cib = (int)(col0 & 255);
 
         f32x4 acc[CB][NBW];
@@ -192,11 +199,23 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
         for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
           for (int mb = 0; mb < CB; ++mb) {
-            const u32x4 a = ex(colbits[(cib + 16 * mb + i) * CSTR + kk]);
+            if constexpr (GAUSS) {
+              const int64_t o = (col0 + 16 * mb + i) * (int64_t)KR + 32 * kk + 8 * g;
+              const u32x4 ah = *reinterpret_cast<const u32x4*>(p.Athi + o);
+              const u32x4 al = *reinterpret_cast<const u32x4*>(p.Atlo + o);
 #pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-              acc[mb][nb] = mfma_16x16x32(a, uh[kk][nb], acc[mb][nb]);
-              acc[mb][nb] = mfma_16x16x32(a, ul[kk][nb], acc[mb][nb]);
+              for (int nb = 0; nb < NBW; ++nb) {
+                acc[mb][nb] = mfma_16x16x32(ah, uh[kk][nb], acc[mb][nb]);
+                acc[mb][nb] = mfma_16x16x32(ah, ul[kk][nb], acc[mb][nb]);
+                acc[mb][nb] = mfma_16x16x32(al, uh[kk][nb], acc[mb][nb]);
+              }
+            } else {
+              const u32x4 a = ex(colbits[(cib + 16 * mb + i) * CSTR + kk]);
+#pragma unroll
+              for (int nb = 0; nb < NBW; ++nb) {
+                acc[mb][nb] = mfma_16x16x32(a, uh[kk][nb], acc[mb][nb]);
+                acc[mb][nb] = mfma_16x16x32(a, ul[kk][nb], acc[mb][nb]);
+              }
             }
           }
 
@@ -237,9 +256,9 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   }
 }
 
-template <int NBW, int CB, int NK, int PD>
+template <int NBW, int CB, int NK, int PD, bool GAUSS = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_kernel(MergeParams p) {
-  merge_tile<NBW, CB, NK, PD>(p, xcd_linear_id_m(blockIdx.x, gridDim.x));
+  merge_tile<NBW, CB, NK, PD, GAUSS>(p, xcd_linear_id_m(blockIdx.x, gridDim.x));
 }
 
 // Several matrices in one launch (same rank, so the same tiling): the
@@ -258,7 +277,7 @@ namespace {
 size_t align_up_m(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
-MergePlan plan_merge(int64_t d, int64_t k, int r) {
+MergePlan plan_merge(int64_t d, int64_t k, int r, bool gauss) {
   MergePlan pl{};
   pl.NK = r <= 32 ? 1 : (r <= 64 ? 2 : (r <= 128 ? 4 : (r <= 256 ? 8 : 16)));
   // Tile per wave and chunk (two waves fit per SIMD): one 16-row block x 64
@@ -268,9 +287,12 @@ MergePlan plan_merge(int64_t d, int64_t k, int r) {
   // with GPU-only timing over layers from 1536 x 1536 to 17408 x 5120.
   // Above r = 256 (NK = 16) one 16-row block x 64 columns: the U operands
   // alone take 128 registers.
+  // The Gaussian basis runs the default tiling only.
   int NBW = pl.NK == 8 ? 2 : 1, CB = 4;
-  NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
-  CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
+  if (!gauss) {
+    NBW = env_int("LOGRA_MERGE_NBW", NBW) == 2 ? 2 : 1;
+    CB = env_int("LOGRA_MERGE_CB", CB) == 4 ? 4 : 8;
+  }
   if (NBW == 2 && CB == 8 && pl.NK >= 4) CB = 4;  // would not fit two waves per SIMD
   if (pl.NK == 16) NBW = 1, CB = 4;
   pl.NBW = NBW;
@@ -292,6 +314,17 @@ MergePlan plan_merge(int64_t d, int64_t k, int r) {
 
 bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s) {
   const int grid = (int)align_up_m((size_t)pl.n_cr * pl.n_rb, 8);
+  if (mp.Athi) {
+#define LOGRA_MERGE_GAUSS(nbw, cb, nk)                                                          \
+    if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                          \
+      hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2, true>), dim3(grid), dim3(256), 0, s, mp); \
+      return true;                                                                              \
+    }
+    LOGRA_MERGE_GAUSS(1, 4, 1) LOGRA_MERGE_GAUSS(1, 4, 2) LOGRA_MERGE_GAUSS(1, 4, 4)
+    LOGRA_MERGE_GAUSS(2, 4, 8) LOGRA_MERGE_GAUSS(1, 4, 16)
+#undef LOGRA_MERGE_GAUSS
+    return false;
+  }
 #define LOGRA_MERGE(nbw, cb, nk)                                                            \
   if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                        \
     hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, mp);    \

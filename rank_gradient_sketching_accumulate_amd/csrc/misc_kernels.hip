@@ -291,4 +291,60 @@ void payload_pack_launch(const PayloadPackArgs& a, void* payload, hipStream_t s)
                      static_cast<uint8_t*>(payload));
 }
 
+// Gaussian basis planes (see GaussBasisParams).  One thread per (row, block
+// of eight columns); with col_major the rows of a block are consecutive
+// threads (the At stores coalesce), otherwise the blocks of a row are.
+__global__ __launch_bounds__(256) void gauss_basis_kernel(GaussBasisParams p, int col_major) {
+  const int64_t nblk = p.kpad / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.RP * nblk) return;
+  int i;
+  int64_t b;
+  if (col_major) {
+    b = idx / p.RP;
+    i = (int)(idx - b * p.RP);
+  } else {
+    i = (int)(idx / nblk);
+    b = idx - (int64_t)i * nblk;
+  }
+  float z[8];
+  if (i < p.rr && 8 * b < p.k) {
+    gauss_block(p.seed, (uint32_t)(p.row0 + i), (uint64_t)b, z);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (8 * b + e >= p.k) z[e] = 0.f;
+  if (p.Z && i < p.rr) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (8 * b + e < p.k) p.Z[(int64_t)i * p.k + 8 * b + e] = z[e];
+  }
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_hi_lo2(z[2 * q], z[2 * q + 1], h[q], l[q]);
+  if (p.Ahi) {
+    const int64_t o = (int64_t)i * p.kpad + 8 * b;
+    *reinterpret_cast<u32x4*>(p.Ahi + o) = u32x4{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4*>(p.Alo + o) = u32x4{l[0], l[1], l[2], l[3]};
+  }
+  if (p.Athi) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t o = (8 * b + e) * p.RP + i;
+      p.Athi[o] = (uint16_t)(h[e >> 1] >> (16 * (e & 1)));
+      p.Atlo[o] = (uint16_t)(l[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+void gauss_basis_launch(const GaussBasisParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.RP * (p.kpad / 8);
+  const int64_t grid = (n + 255) / 256;
+  hipLaunchKernelGGL(gauss_basis_kernel, dim3((unsigned)(grid > 0 ? grid : 1)), dim3(256), 0, s, p,
+                     p.Athi ? 1 : 0);
+}
+
 }  // namespace logra

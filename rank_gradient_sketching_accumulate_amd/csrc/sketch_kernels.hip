@@ -639,6 +639,111 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
 }
 
 // ===========================================================================
+// Projection with the Gaussian basis: P = X Z^T with Z dense (the refreshed
+// Gaussian projection), Z's bf16 hi/lo planes generated per call by
+// gauss_basis_kernel.  Four waves of 16 tokens (64 per workgroup) x all 16*NB
+// columns; k in 32-column steps.  A step's Z columns (hi and lo, 16*NB rows x
+// 32) are staged through a two-buffer LDS ring shared by the four waves; X
+// is read straight into the MFMA A operand (rows past T read as zero, columns
+// past k are zeroed).  Each product takes two MFMAs (X times hi, X times lo).
+// ===========================================================================
+template <int NB>
+__global__ __launch_bounds__(256) void proj_gauss_kernel(ProjParams p) {
+  constexpr int RP = 16 * NB;
+  constexpr int SW = RP * 4;                  // u32x4 words per plane and step
+  constexpr int PER = (2 * SW + 255) / 256;   // words each thread stages per step
+  __shared__ u32x4 st[2][2 * SW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int nsteps = (int)(p.kpad / 32);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
+  const uint32_t xrow = (uint32_t)((t0 + 16 * wave + i) * p.ldx * 2);
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Staged word w of a step: plane w / SW, row (w % SW) / 4, quad w % 4
+  // (columns 8*quad .. 8*quad+7 of the step).
+  u32x4 stg[PER];
+  auto load_a = [&](int m) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int w = threadIdx.x + 256 * j;
+      if (2 * SW % 256 == 0 || w < 2 * SW) {
+        const int q = w % SW;
+        const uint16_t* src = (w < SW ? p.Ahi : p.Alo) + (int64_t)(q >> 2) * p.kpad + 32 * (int64_t)m + 8 * (q & 3);
+        stg[j] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int w = threadIdx.x + 256 * j;
+      if (2 * SW % 256 == 0 || w < 2 * SW) st[buf][w] = stg[j];
+    }
+  };
+
+  if (nsteps > 0) {
+    load_a(0);
+    store_a(0);
+  }
+  __syncthreads();
+  for (int m = 0; m < nsteps; ++m) {
+    const int buf = m & 1;
+    if (m + 1 < nsteps) load_a(m + 1);
+    const int64_t c0 = 32 * (int64_t)m + 8 * g;
+    u32x4 xa = buf_load16(rx, xrow + (uint32_t)(c0 * 2));
+    if (c0 + 8 > p.k) {
+      const int64_t nv = p.k - c0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t mk = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+        xa[q] &= mk;
+      }
+    }
+    const u32x4* ah = &st[buf][0];
+    const u32x4* al = &st[buf][SW];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[nb] = mfma_16x16x32(xa, ah[(16 * nb + i) * 4 + g], acc[nb]);
+      acc[nb] = mfma_16x16x32(xa, al[(16 * nb + i) * 4 + g], acc[nb]);
+    }
+    if (m + 1 < nsteps) store_a(buf ^ 1);
+    __syncthreads();
+  }
+  // acc[nb][e] = P[t0 + 16*wave + 4g + e][16*nb + i]: four consecutive tokens
+  // of one column, consecutive in Pk order.
+  const int64_t t = t0 + 16 * wave + 4 * g;
+  if (t < p.Tw) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t e0 = pk_index(t, 16 * nb + i, NB);
+      uint32_t h0, l0, h1, l1;
+      split_hi_lo2(acc[nb][0], acc[nb][1], h0, l0);
+      split_hi_lo2(acc[nb][2], acc[nb][3], h1, l1);
+      *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+      if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+    }
+  }
+}
+
+bool proj_gauss_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
+  const int grid = (int)((p.Tw + 63) / 64);
+  if (grid < 1) return true;
+  switch (pl.NB) {
+    case 1: hipLaunchKernelGGL((proj_gauss_kernel<1>), dim3(grid), dim3(256), 0, s, p); return true;
+    case 2: hipLaunchKernelGGL((proj_gauss_kernel<2>), dim3(grid), dim3(256), 0, s, p); return true;
+    case 4: hipLaunchKernelGGL((proj_gauss_kernel<4>), dim3(grid), dim3(256), 0, s, p); return true;
+    case 8: hipLaunchKernelGGL((proj_gauss_kernel<8>), dim3(grid), dim3(256), 0, s, p); return true;
+    case 16: hipLaunchKernelGGL((proj_gauss_kernel<16>), dim3(grid), dim3(256), 0, s, p); return true;
+  }
+  return false;
+}
+
+// ===========================================================================
 // Contraction S += (1/sqrt r) dY^T P.
 // MFMA: A = dY^T (M = 16 rows of S), B = P (N = 16 columns), K = 32 tokens.
 // A lane loads four consecutive columns of dY from eight token rows and a

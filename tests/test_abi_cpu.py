@@ -402,3 +402,22 @@ def test_payload_pack_and_apply_validation(lib):
     ld = (ctypes.c_int64 * 2)(20, 20)
     assert lib.logra_payload_apply(FAKE * 64, 1 << 20, ctypes.byref(h), es, W, ld, None) == ERR_SHAPE  # unparsed
     assert lib.logra_payload_apply(None, 1 << 20, ctypes.byref(h), es, W, ld, None) == ERR_NULL
+
+
+def test_basis_setting_and_validation(lib):
+    assert lib.logra_set_basis(1) == 0
+    assert lib.logra_set_basis(0) == 1
+    assert lib.logra_set_basis(0) == 0
+    assert lib.logra_basis_normals(1, 0, 16, FAKE, None) == ERR_RANGE
+    assert lib.logra_basis_normals(1, 513, 16, FAKE, None) == ERR_RANGE
+    assert lib.logra_basis_normals(1, 4, -1, FAKE, None) == ERR_SHAPE
+    assert lib.logra_basis_normals(1, 4, 16, None, None) == ERR_NULL
+    assert lib.logra_basis_normals(1, 4, 16, FAKE + 2, None) == ERR_ALIGN
+    assert lib.logra_basis_normals(1, 4, 0, None, None) == OK
+    # the no-allocation sketch refuses the Gaussian basis before any device work
+    lib.logra_set_basis(1)
+    try:
+        st = lib.logra_sketch_accumulate_noalloc(FAKE, 512, FAKE * 64, 256, 16, 512, 256, 0, 16, FAKE * 4096, 16, None)
+        assert st == ERR_RANGE and b"Gaussian" in lib.logra_last_error()
+    finally:
+        lib.logra_set_basis(0)
