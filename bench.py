@@ -531,6 +531,20 @@ def main():
             lg.set_precision(prev)
         extras["sketch_" + other] = {"avg_call_us": t_other * 1e6, "achieved": sb / t_other / 1e9,
                                      "frac": sb / t_other / 1e9 / HBM_PEAK_GBS, "tokens_per_s": T / t_other}
+        # The Gaussian basis on the same inputs (sketch call, and the merge
+        # including its basis generation).
+        prev = lg.set_basis(lg.BASIS_GAUSSIAN)
+        try:
+            t_gs, _ = gpu_time(sketch_call, n_calls)
+            t_gm, _ = gpu_time(lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale), n_merges)
+        finally:
+            lg.set_basis(prev)
+        extras["basis_gaussian"] = {
+            "what": "refreshed Gaussian basis (Box-Muller normals, bf16 hi/lo planes generated per call)",
+            "sketch_call_us": t_gs * 1e6, "sketch_frac": sb / t_gs / 1e9 / HBM_PEAK_GBS,
+            "merge_us": t_gm * 1e6, "merge_frac": mb / t_gm / 1e9 / HBM_PEAK_GBS,
+            "rademacher_sketch_call_us": t_call * 1e6, "rademacher_merge_us": t_merge * 1e6,
+        }
         # Split calls: the projection of every microbatch into its own cache
         # (forward time), then the contractions from the caches (backward).
         caches = [[lg.project(X, seed, r) for X, _ in mbs] for mbs in sets]

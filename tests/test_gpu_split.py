@@ -256,3 +256,72 @@ def test_counters_handoff_between_plans():
         S2 = torch.zeros_like(S)
         lg.contract(dY, P, r, S2)
         assert_sketch_close(f64(S2)[rows], ref, what=f"split calls {j}")
+
+
+def test_fail_alloc_hook_reports_nomem_and_touches_nothing(monkeypatch):
+    """With LOGRA_TEST_FAIL_ALLOC=1 any growth of the library's scratch is
+    refused: on a stream whose scratch was released, the calls that need
+    scratch (the fused sketch: P; RowAdam: row statistics; a Gaussian-basis
+    merge: the basis planes) return LOGRA_ERR_NOMEM and leave their outputs
+    unchanged."""
+    T, k, d, r = 700, 1300, 300, 64
+    X, dY = _inputs(T, k, d, 31)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    lg.workspace_release(side)
+    S = torch.full((d, r), 2.0, dtype=torch.float32, device=DEV)
+    v = torch.zeros(d, dtype=torch.float32, device=DEV)
+    W = wl.gaussian_bf16((d, k + 4), 0.02, 8, device=DEV)[:, :k]
+    W0 = W.clone()
+    monkeypatch.setenv("LOGRA_TEST_FAIL_ALLOC", "1")
+    prev = lg.set_basis(lg.BASIS_RADEMACHER)
+    try:
+        with torch.cuda.stream(side):
+            for j, call in enumerate((lambda: lg.sketch_accumulate(X, dY, 3, r, S),
+                                      lambda: lg.rowadam_scale(S, v, 1, 0.95, 1e-8),
+                                      lambda: (lg.set_basis(lg.BASIS_GAUSSIAN), lg.merge_update(W, S, 3, r, 1e-3)))):
+                with pytest.raises(lg.LograError) as ei:
+                    call()
+                assert ei.value.status == lg.LOGRA_ERR_NOMEM, j
+                assert "LOGRA_TEST_FAIL_ALLOC" in str(ei.value)
+    finally:
+        lg.set_basis(prev)
+        monkeypatch.delenv("LOGRA_TEST_FAIL_ALLOC")
+    torch.cuda.synchronize()
+    assert bool((S == 2.0).all()) and not bool(v.any()) and torch.equal(W, W0)
+    with torch.cuda.stream(side):
+        lg.sketch_accumulate(X, dY, 3, r, S)  # allocation allowed again
+    torch.cuda.synchronize()
+    ref = oracle.sketch_accumulate(np.full((d, r), 2.0), [f64(X)], [f64(dY)], oracle.rademacher_projection(3, r, k))
+    assert_sketch_close(f64(S), ref)
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_checkpoint_host_round_trip_of_s(det):
+    """Two microbatches, S copied to host memory and back into a new device
+    buffer (a checkpoint mid-step), two more: the same S as four straight
+    calls (bitwise in the deterministic mode), and the oracle's."""
+    T, k, d, r = 1000, 1536, 700, 128
+    mbs = [_inputs(T, k, d, 900 + 2 * m) for m in range(4)]
+    prev = lg.set_deterministic(det)
+    try:
+        S = torch.zeros((d, r), dtype=torch.float32, device=DEV)
+        for X, dY in mbs[:2]:
+            lg.sketch_accumulate(X, dY, 21, r, S)
+        host = S.cpu().numpy().copy()
+        S2 = torch.from_numpy(host).to(DEV)
+        for X, dY in mbs[2:]:
+            lg.sketch_accumulate(X, dY, 21, r, S2)
+        Sref = torch.zeros_like(S)
+        for X, dY in mbs:
+            lg.sketch_accumulate(X, dY, 21, r, Sref)
+        torch.cuda.synchronize()
+    finally:
+        lg.set_deterministic(prev)
+    if det:
+        assert torch.equal(S2, Sref)
+    else:
+        assert rel_frob(f64(S2), f64(Sref)) <= 1e-6
+    ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X) for X, _ in mbs], [f64(dY) for _, dY in mbs],
+                                   oracle.rademacher_projection(21, r, k))
+    assert_sketch_close(f64(S2), ref)
