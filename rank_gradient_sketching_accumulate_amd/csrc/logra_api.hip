@@ -1248,7 +1248,12 @@ logra_status logra_workspace_release(hipStream_t stream) {
 }
 
 const char* logra_status_string(logra_status s) {
-  switch (s) {
+  // A C caller may pass any int; in C++ a value outside the enumerators'
+  // range may not be read as the enum, so read the bits as an int.
+  int v;
+  static_assert(sizeof(v) == sizeof(s), "logra_status is int-sized");
+  std::memcpy(&v, &s, sizeof(v));
+  switch (v) {
     case LOGRA_OK: return "ok";
     case LOGRA_ERR_NULL: return "null pointer";
     case LOGRA_ERR_SHAPE: return "bad shape";
