@@ -399,6 +399,21 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v,
                                  hipStream_t stream);
 
 /*
+ * RowAdam folded into the merge: W <- RNE_bf16(W - scale (1/sqrt(r)) U A)
+ * with U = RowAdam(S) as logra_rowadam_scale defines it, without writing U:
+ * the RowAdam statistics give one fp32 factor per row and the merge
+ * multiplies each entry of S by its row's factor as it loads it.  v is
+ * updated as by logra_rowadam_scale; S is only read.  W and v end bitwise
+ * equal to logra_rowadam_scale on a copy of S followed by logra_merge_update
+ * (same basis setting), and one read and write of S fewer.  Arguments and
+ * checks are those of the two calls (S in the role of U; W may overlap
+ * neither S nor v); k == 0 updates v only.
+ */
+logra_status logra_rowadam_merge(void* W, int64_t ldw, const float* S, int64_t lds, float* v,
+                                 int64_t d, int64_t k, uint64_t seed, int32_t r, int64_t step,
+                                 float beta2, float eps_rel, float scale, hipStream_t stream);
+
+/*
  * Predicted KL of a proposed update (paper section 2.3, equation 6; derived in
  * appendix A.1):
  *

@@ -44,6 +44,7 @@ __all__ = [
     "payload_parse",
     "payload_apply",
     "rowadam_scale",
+    "rowadam_merge",
     "predicted_kl",
     "kl_step_scale",
     "kl_budget",
@@ -81,6 +82,7 @@ EXPORTED_SYMBOLS = (
     "logra_payload_parse",
     "logra_payload_apply",
     "logra_rowadam_scale",
+    "logra_rowadam_merge",
     "logra_predicted_kl",
     "logra_kl_step_scale",
     "logra_kl_budget",
@@ -189,6 +191,9 @@ def _declare(lib):
                                         ctypes.POINTER(PayloadEntry), ctypes.POINTER(c_vp),
                                         ctypes.POINTER(c_i64), c_vp]
     lib.logra_payload_apply.restype = ctypes.c_int
+    lib.logra_rowadam_merge.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_u64, c_i32, c_i64, c_f, c_f,
+                                        c_f, c_vp]
+    lib.logra_rowadam_merge.restype = ctypes.c_int
     lib.logra_rowadam_scale.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_f, c_f, c_vp]
     lib.logra_rowadam_scale.restype = ctypes.c_int
     lib.logra_predicted_kl.argtypes = [c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_f, c_vp, c_vp, c_vp]
@@ -535,6 +540,24 @@ def payload_apply(payload, header, entries, Ws):
         lds[j] = _ld(W)
     _check(lib.logra_payload_apply(payload.data_ptr(), payload.numel(), ctypes.byref(header), entries, ptrs, lds,
                                    _stream_handle(payload)))
+
+
+def rowadam_merge(W, S, v, seed: int, r: int, step: int, beta2: float, eps_rel: float, scale: float):
+    """W <- merge of RowAdam(S) without writing U (S unchanged, v updated);
+    W: (d, k) bf16, S: (d, r) float32, v: (d,) float32.  Returns W."""
+    import torch
+
+    lib = load_library()
+    _need(W, torch.bfloat16, "W")
+    _need(S, torch.float32, "S")
+    _need(v, torch.float32, "v", ndim=1)
+    d, k = W.shape
+    if tuple(S.shape) != (d, r) or v.numel() != d:
+        raise ValueError(f"S must be ({d}, {r}) and v ({d},)")
+    _check(lib.logra_rowadam_merge(W.data_ptr() if W.numel() else None, _ld(W), S.data_ptr(), _ld(S), v.data_ptr(),
+                                   d, k, ctypes.c_uint64(seed & (2**64 - 1)), r, step, beta2, eps_rel, scale,
+                                   _stream_handle(S)))
+    return W
 
 
 def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):

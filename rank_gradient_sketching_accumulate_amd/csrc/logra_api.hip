@@ -1046,6 +1046,68 @@ logra_status logra_rowadam_scale(float* S, int64_t lds, float* v, int64_t d, int
   }
 }
 
+logra_status logra_rowadam_merge(void* W, int64_t ldw, const float* S, int64_t lds, float* v, int64_t d, int64_t k,
+                                 uint64_t seed, int32_t r, int64_t step, float beta2, float eps_rel, float scale,
+                                 hipStream_t stream) {
+  try {
+    g_last_error.clear();
+    if (d < 0 || k < 0) return fail(LOGRA_ERR_SHAPE, "d and k must be >= 0");
+    if (r < 1 || r > LOGRA_MAX_RANK) return fail(LOGRA_ERR_RANGE, "r must be in [1, 512]");
+    if (lds < r) return fail(LOGRA_ERR_SHAPE, "lds must be >= r");
+    if (step < 1) return fail(LOGRA_ERR_RANGE, "step counts RowAdam updates and starts at 1");
+    if (!(beta2 >= 0.0f && beta2 < 1.0f)) return fail(LOGRA_ERR_RANGE, "beta2 must be in [0, 1)");
+    if (!(eps_rel >= 0.0f) || !isfinite(eps_rel)) return fail(LOGRA_ERR_RANGE, "eps_rel must be finite and >= 0");
+    if (d == 0) return LOGRA_OK;
+    if (!S || !v) return fail(LOGRA_ERR_NULL, "S and v must be non-null");
+    if (((uintptr_t)S & 3) || ((uintptr_t)v & 3)) return fail(LOGRA_ERR_ALIGN, "S and v must be 4-byte aligned");
+    if (overlaps(S, span_bytes(d, r, lds, 4), v, (size_t)d * 4)) return fail(LOGRA_ERR_ALIAS, "v overlaps S");
+    // The merge's own checks (W against S as its U), before anything is
+    // enqueued; k == 0 still updates v.
+    MergeParams mp{};
+    MergePlan pl{};
+    bool skip = false;
+    logra_status st = prepare_merge(W, ldw, S, lds, d, k, seed, r, scale, mp, pl, skip);
+    if (st != LOGRA_OK) return st;
+    if (!skip && overlaps(W, span_bytes(d, k, ldw, 2), v, (size_t)d * 4)) return fail(LOGRA_ERR_ALIAS, "W overlaps v");
+    size_t off_root, off_ssq, off_part, off_part2;
+    const size_t total = rowadam_layout(d, off_root, off_ssq, off_part, off_part2);
+    const size_t off_mul = total;
+    void* ws = nullptr;
+    st = arena_get(kArenaRowAdam, stream, total + (size_t)d * 4, &ws);
+    if (st != LOGRA_OK) return st;
+    if (!skip && g_basis_gauss) {
+      void* bp = nullptr;
+      st = arena_get(kArenaBasis, stream, basis_bytes(32 * pl.NK, basis_kpad_merge(k)), &bp);
+      if (st != LOGRA_OK) return st;
+    }
+    char* base = static_cast<char*>(ws);
+    float* rowmul = reinterpret_cast<float*>(base + off_mul);
+    const double inv_bias = 1.0 / (1.0 - pow((double)beta2, (double)step));
+    // S is only read: the rescale writes the row factors instead.
+    rowadam_launch(const_cast<float*>(S), lds, v, d, r, beta2, inv_bias, eps_rel,
+                   reinterpret_cast<float*>(base + off_root), reinterpret_cast<float*>(base + off_ssq),
+                   reinterpret_cast<double*>(base + off_part), reinterpret_cast<double*>(base + off_part2), stream,
+                   rowmul);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "rowadam launch");
+    if (skip) return LOGRA_OK;
+    mp.rowmul = rowmul;
+    if (g_basis_gauss) {
+      uint16_t *ah = nullptr, *al = nullptr;
+      st = basis_generate(seed, 0, r, 32 * pl.NK, k, basis_kpad_merge(k), true, stream, &ah, &al);
+      if (st != LOGRA_OK) return st;
+      mp.Athi = ah;
+      mp.Atlo = al;
+    }
+    if (!merge_launch(pl, mp, stream)) return fail(LOGRA_ERR_RANGE, "no merge kernel for this tile");
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return LOGRA_OK;
+  } catch (...) {
+    return fail(LOGRA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 logra_status logra_predicted_kl(const void* z, int64_t ldz, const void* zdot, int64_t ldzd, int64_t n, int64_t V,
                                 int32_t dtype, float temperature, float* row_var, float* q, hipStream_t stream) {
   try {

@@ -112,6 +112,9 @@ struct MergeParams {
   // column of W (rows up to the last chunk's end); null for signs.
   const uint16_t* Athi;
   const uint16_t* Atlo;
+  // RowAdam folded into the merge: U = S with row i multiplied by rowmul[i]
+  // (fp32) as it is loaded; null for a plain U.
+  const float* rowmul;
   int n_rb, n_cr;   // row blocks, column ranges
   int64_t cr_cols;  // columns per range (a multiple of the chunk width)
 };
@@ -211,7 +214,8 @@ void kl_launch(const KLPlan& pl, const KLParams& p, int bf16, float* row_var, fl
 // 2 * kRowAdamBlocks doubles, partial2 kRowAdamBlocks.
 constexpr int kRowAdamBlocks = 512;
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias,
-                    float eps_rel, float* root, float* ssq, double* partial, double* partial2, hipStream_t s);
+                    float eps_rel, float* root, float* ssq, double* partial, double* partial2, hipStream_t s,
+                    float* rowmul = nullptr);
 void signs_launch(uint64_t seed, int r, int64_t k, int8_t* out, hipStream_t s);
 void stream_read_launch(const void* ptr, int64_t n16, uint32_t* sink, hipStream_t s);
 // dst[0 .. 16*n16) = 0 (dst 16-byte aligned).

@@ -76,6 +76,15 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   // lane.  Entries past r are zeroed; rows past d read as zero through the
   // descriptor.  Queued first, split after the first sign block is built.
   const __amdgpu_buffer_rsrc_t ru = make_rsrc(p.U, (uint32_t)(p.d * p.ldu * 4));
+  // RowAdam folded in: the row factors of this wave's rows (rows past d read
+  // as zero; without a factor buffer the descriptor is empty and 1 is used).
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(p.rowmul, p.rowmul ? (uint32_t)(p.d * 4) : 0u);
+  float fr[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const float f = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)((rw + 16 * nb + i) * 4), 0, 0));
+    fr[nb] = p.rowmul ? f : 1.0f;
+  }
   float uraw[NK][NBW][8];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
@@ -103,6 +112,10 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (j0 + e >= p.r) uraw[kk][nb][e] = 0.f;
+      }
+      if (p.rowmul) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) uraw[kk][nb][e] *= fr[nb];
       }
     }
 

@@ -117,7 +117,8 @@ template <bool VEC, bool FUSED>
 __global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t lds, int64_t d, int r, int L,
                                                            const float* root, const float* ssq,
                                                            const double* partial, int nparts,
-                                                           const double* partial2, int nparts2, float eps_rel) {
+                                                           const double* partial2, int nparts2, float eps_rel,
+                                                           float* rowmul) {
   __shared__ double sh[256];
   const double sum_root = sum_partials(partial, nparts, 2, sh);
   const double norm_s2 = sum_partials(partial + 1, nparts, 2, sh);
@@ -142,6 +143,12 @@ __global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t ld
     const int64_t row = base + wave * rpw + lane / L;
     if (row >= d) continue;
     const float f = (float)(fac / ((double)root[row] + eps));
+    if (rowmul) {
+      // Folded into the merge: the row factor only (the merge multiplies
+      // each S entry by it in fp32, exactly as below).
+      if (sub == 0) rowmul[row] = f;
+      continue;
+    }
     float* dst = S + row * lds;
     if constexpr (VEC) {
       for (int j = 4 * sub; j < r; j += 4 * L) {
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t ld
 }
 
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias, float eps_rel,
-                    float* root, float* ssq, double* partial, double* partial2, hipStream_t s) {
+                    float* root, float* ssq, double* partial, double* partial2, hipStream_t s, float* rowmul) {
   const bool vec = (((uintptr_t)S & 15) == 0) && (lds % 4 == 0) && (r % 4 == 0);
   int L = 1;
   while (L < 64 && 4 * L < r) L <<= 1;  // float4 lanes per row (the scalar path uses the same grouping)
@@ -178,20 +185,20 @@ void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float bet
   if (d <= 2048) {
     if (vec)
       hipLaunchKernelGGL((rowadam_apply_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel);
+                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel, rowmul);
     else
       hipLaunchKernelGGL((rowadam_apply_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel);
+                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel, rowmul);
     return;
   }
   hipLaunchKernelGGL(rowadam_norm_kernel, dim3((unsigned)nblocks), dim3(256), 0, s, partial, (int)blocks, root, ssq, d,
                      eps_rel, partial2);
   if (vec)
     hipLaunchKernelGGL((rowadam_apply_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel);
+                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel, rowmul);
   else
     hipLaunchKernelGGL((rowadam_apply_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel);
+                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel, rowmul);
 }
 
 // Signs s (r x k) as int8 +-1; one thread per (row, 256-column block).

@@ -421,3 +421,22 @@ def test_basis_setting_and_validation(lib):
         assert st == ERR_RANGE and b"Gaussian" in lib.logra_last_error()
     finally:
         lib.logra_set_basis(0)
+
+
+def test_rowadam_merge_validation(lib):
+    args = dict(W=FAKE, ldw=512, S=FAKE * 64, lds=16, v=FAKE * 128, d=256, k=512, seed=0, r=16, step=1,
+                beta2=0.95, eps=1e-8, scale=1e-3)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.logra_rowadam_merge(a["W"], a["ldw"], a["S"], a["lds"], a["v"], a["d"], a["k"], a["seed"], a["r"],
+                                       a["step"], a["beta2"], a["eps"], a["scale"], None)
+
+    assert call(r=0) == ERR_RANGE
+    assert call(step=0) == ERR_RANGE
+    assert call(beta2=1.0) == ERR_RANGE
+    assert call(lds=8) == ERR_SHAPE
+    assert call(v=None) == ERR_NULL
+    assert call(ldw=500) == ERR_SHAPE
+    assert call(W=FAKE * 64 + 64) == ERR_ALIAS  # W over S
+    assert call(d=0) == OK

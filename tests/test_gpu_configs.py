@@ -175,3 +175,30 @@ def test_rowadam_then_merge_three_steps(key, li, r):
                             bound=update_error_bound(Ur, r, scale), what=f"W at t={t}")
         del W, S
     assert math.isfinite(float(v.sum()))
+
+
+@pytest.mark.parametrize("d,k,r,basis", [(300, 1032, 64, 0), (3584, 3584, 256, 0), (1000, 2048, 512, 0),
+                                         (7, 520, 256, 0), (4000, 1024, 128, 1)])
+def test_rowadam_folded_into_merge_is_bitwise_the_two_calls(d, k, r, basis):
+    """logra_rowadam_merge over steps t = 1, 2, 3: W and v bitwise equal to
+    RowAdam on a copy of S followed by the merge, S untouched."""
+    _say("rowadam fold", d, k, r, basis)
+    prev = lg.set_basis(basis)
+    try:
+        W1 = wl.gaussian_bf16((d, k), 0.02, 11, device=DEV)
+        W2 = W1.clone()
+        v1 = torch.zeros(d, dtype=torch.float32, device=DEV)
+        v2 = torch.zeros_like(v1)
+        for t in (1, 2, 3):
+            S = wl.random_tensor((d, r), 20 + t, device=DEV, std=0.5 * t)
+            S_keep = S.clone()
+            U = S.clone()
+            lg.rowadam_scale(U, v1, t, 0.999, 1e-8)
+            lg.merge_update(W1, U, 5 + t, r, 1e-4)
+            lg.rowadam_merge(W2, S, v2, 5 + t, r, t, 0.999, 1e-8, 1e-4)
+            torch.cuda.synchronize()
+            assert torch.equal(v1, v2), f"v at t={t}"
+            assert torch.equal(W1, W2), f"W at t={t}"
+            assert torch.equal(S, S_keep), "S was written"
+    finally:
+        lg.set_basis(prev)
