@@ -95,3 +95,37 @@ def test_split_contract_keeps_both_planes(bf16_mode):
     lg.contract(dY, P, r, S)
     ref = oracle.sketch_accumulate(np.zeros((d, r)), [f64(X)], [f64(dY)], oracle.rademacher_projection(5, r, k))
     assert rel_frob(f64(S), ref) <= 1e-4
+
+
+def _layer_cases():
+    out = []
+    for key in ("mlp1536", "set7b", "layer27b"):
+        w = wl.WORKLOADS[key]
+        for li in range(len(w.layers)):
+            for r in w.ranks:
+                out.append((key, li, r))
+    return out
+
+
+@pytest.mark.parametrize("key,li,r", _layer_cases(),
+                         ids=[f"{k}-{wl.WORKLOADS[k].layers[l].name}-r{r}" for k, l, r in _layer_cases()])
+def test_bf16_mode_every_layer(key, li, r, bf16_mode):
+    """The single-bf16 mode at every 1.5B/7B/27B-class layer and rank (one
+    microbatch, sampled rows of S): within the 2e-3 bar of the method, and
+    within 1e-4 of the oracle that rounds P the same way."""
+    w = wl.WORKLOADS[key]
+    L = w.layers[li]
+    seed = wl.sign_seed(li)
+    X, dY = wl.layer_inputs(w, li, 0, device=DEV)
+    S = torch.zeros((L.d, r), dtype=torch.float32, device=DEV)
+    lg.sketch_accumulate(X, dY, seed, r, S)
+    rows = np.sort(np.random.default_rng(li + r).choice(L.d, size=min(96, L.d), replace=False))
+    rows_t = torch.as_tensor(rows, device=DEV)
+    got = f64(S[rows_t])
+    Xh, dYr = f64(X), f64(dY[:, rows_t])
+    exact = oracle.sketch_from_gradient(dYr.T @ Xh, oracle.rademacher_projection(seed, r, L.k))
+    rounded = oracle.sketch_accumulate_rounded_projection(np.zeros((len(rows), r)), [Xh], [dYr], seed, r)
+    e_m, e_r = rel_frob(got, exact), rel_frob(got, rounded)
+    print(f"[case] bf16 mode {key} {L.name} r={r}: vs method {e_m:.3e}, vs rounded-P oracle {e_r:.3e}", flush=True)
+    assert e_m <= S_TOL
+    assert e_r <= 1e-4
