@@ -1146,20 +1146,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
       off += rowstep;
     }
   };
-  // Thread q moves words q, q + 512, ... of the step's [hi | lo] tile.
+  // Thread q moves words q, q + 512, ... of the step's hi plane, then the
+  // same words of its lo plane (PER / 2 of each), through buffer loads
+  // (SGPR base, 32-bit offsets: the planes span less than 4 GiB).
+  constexpr int PH = PER / 2;
+  static_assert(PH * 512 == PV, "whole planes per step");
+  const __amdgpu_buffer_rsrc_t rph = make_rsrc(p.Phi, 0xFFFFFFF0u);
+  const __amdgpu_buffer_rsrc_t rpl = make_rsrc(p.Plo, 0xFFFFFFF0u);
   auto load_p = [&](u32x4 (&sl)[PER], int m) {
     m = min(m, nsteps - 1);
-    const int64_t base = (ks_beg + m) * (int64_t)PV;
+    const uint32_t base = (uint32_t)(((ks_beg + m) * (int64_t)PV + threadIdx.x) * 16);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int w = threadIdx.x + 512 * j;
-      const uint16_t* src = (w < PV) ? p.Phi + (base + w) * 8 : p.Plo + (base + w - PV) * 8;
-      sl[j] = *reinterpret_cast<const u32x4*>(src);
+    for (int j = 0; j < PH; ++j) {
+      sl[j] = buf_load16(rph, base + 512 * 16 * j);
+      sl[PH + j] = buf_load16(rpl, base + 512 * 16 * j);
     }
   };
   auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) pt[buf][threadIdx.x + 512 * j] = sl[j];
+    for (int j = 0; j < PH; ++j) {
+      pt[buf][threadIdx.x + 512 * j] = sl[j];
+      pt[buf][PV + threadIdx.x + 512 * j] = sl[PH + j];
+    }
   };
 
   // Steps 0 .. DP - 1 in flight; step 0 staged.  P of step m lives in
@@ -1202,6 +1210,115 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
   }
   }
   store_s_tile<NBW>(p, acc, d0w, wn * NBW, g, i, ts);
+}
+
+// Rank 256, two workgroups per CU: the 256 x 256 tile of contract_big_kernel
+// cut into two column halves, each a workgroup of four waves (one per SIMD,
+// 64 rows x 128 columns each, 128 accumulator registers).  The two
+// workgroups on a CU have barriers of their own, so one can multiply while
+// the other waits on its loads or its barrier; the two halves of a tile are
+// consecutive logical ids (one XCD), so the second read of the tile's dY
+// rows comes from L2.
+template <int DP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void contract_half_kernel(ContractParams p) {
+  constexpr int NB = 16;
+  constexpr int NBW = 8;                 // column blocks per wave (half of the tile)
+  constexpr int PVH = NBW * 64;          // u32x4 words per plane and step for the half
+  constexpr int PER = 2 * PVH / 256;     // words each thread moves per step
+  constexpr int PH = PER / 2;
+  static_assert(PH * 256 == PVH, "whole planes per step");
+  __shared__ u32x4 pt[2][2 * PVH];
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int half = lin & 1;
+  const int rest = lin >> 1;
+  const int dt = rest / p.n_ts;
+  const int ts = rest - dt * p.n_ts;
+  if (dt >= p.n_dt) return;
+
+  const int lane = threadIdx.x & 63, wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t d0w = ((int64_t)dt * 4 + wm) * 16 * kDC;
+  const uint32_t coloff = (uint32_t)((d0w + kDC * i) * 2);
+  const int64_t nks = (p.T + 31) >> 5;
+  const int64_t ks_beg = ts * p.ksp;
+  const int64_t ks_end = min(nks, ks_beg + p.ksp);
+  const int nsteps = ks_end > ks_beg ? (int)(ks_end - ks_beg) : 0;
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY, (uint32_t)(p.T * p.lddy * 2));
+  const uint32_t rowstep = (uint32_t)(p.lddy * 2);
+
+  f32x4 acc[kDC][NBW];
+#pragma unroll
+  for (int c = 0; c < kDC; ++c)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) acc[c][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x2 y[DP + 1][8];
+  u32x4 stg[DP][PER];
+  auto load_y = [&](u32x2 (&slot)[8], int m) {
+    m = min(m, nsteps - 1);
+    uint32_t off = (uint32_t)((32 * (ks_beg + m) + 8 * g) * p.lddy * 2) + coloff;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      slot[e] = buf_load8(ry, off);
+      off += rowstep;
+    }
+  };
+  // The half's column blocks are contiguous within a step of each plane.
+  const __amdgpu_buffer_rsrc_t rph = make_rsrc(p.Phi, 0xFFFFFFF0u);
+  const __amdgpu_buffer_rsrc_t rpl = make_rsrc(p.Plo, 0xFFFFFFF0u);
+  auto load_p = [&](u32x4 (&sl)[PER], int m) {
+    m = min(m, nsteps - 1);
+    const uint32_t base = (uint32_t)((((ks_beg + m) * NB + NBW * half) * 64 + threadIdx.x) * 16);
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+      sl[j] = buf_load16(rph, base + 256 * 16 * j);
+      sl[PH + j] = buf_load16(rpl, base + 256 * 16 * j);
+    }
+  };
+  auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+      pt[buf][threadIdx.x + 256 * j] = sl[j];
+      pt[buf][PVH + threadIdx.x + 256 * j] = sl[PH + j];
+    }
+  };
+
+  if (nsteps > 0) {
+#pragma unroll
+  for (int q = 0; q < DP; ++q) {
+    load_p(stg[q], q);
+    load_y(y[q], q);
+  }
+  store_p(stg[0], 0);
+  __syncthreads();
+  constexpr int L = DP * (DP + 1);
+  for (int m0 = 0; m0 < nsteps; m0 += L) {
+#pragma unroll
+    for (int u = 0; u < L; ++u) {
+      const int m = m0 + u;
+      load_p(stg[u % DP], m + DP);
+      load_y(y[(u + DP) % (DP + 1)], m + DP);
+      if (m < nsteps) {
+        u32x4 a[kDC];
+        transpose_dy(y[u % (DP + 1)], a);
+        const u32x4* ph = &pt[u & 1][0];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const u32x4 bh = ph[nb * 64 + lane];
+          const u32x4 bl = ph[PVH + nb * 64 + lane];
+#pragma unroll
+          for (int c = 0; c < kDC; ++c) {
+            acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
+            acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
+          }
+        }
+        if (m + 1 < nsteps) store_p(stg[(u + 1) % DP], (u + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+  }
+  store_s_tile<NBW>(p, acc, d0w, NBW * half, g, i, ts);
 }
 
 // Rank 256 on large layers: four waves, one per SIMD, each owning 64 rows x
@@ -1805,7 +1922,13 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // (With P as a hi/lo pair contract_big_kernel is as fast; the shared-
     // operand kernel serves the single-bf16 contraction.)
     const int wide = (!det && pl.NB == 16) ? env_int("LOGRA_CON_WIDE", (hi_only && (tall || use_big)) ? 1 : 0) : 0;
-    if (wide) {
+    // Otherwise the 256 x 256 tiles as two 256 x 128 workgroups per CU
+    // (27B up layer 336 -> 314 us, attention 110 -> 105, 7B up 185 -> 174).
+    const int halfk = (!det && !wide && pl.NB == 16 && (tall || use_big)) ? env_int("LOGRA_CON_HALF", 1) : 0;
+    if (halfk) {
+      pl.cvar = 7;  // contract_half_kernel: 256 x 128 tiles, two workgroups per CU
+      BD = 256;
+    } else if (wide) {
       pl.cvar = 6;
       pl.cwide = wide;  // 1: contract_share_kernel (eight waves), 2: contract_wide_kernel (four)
       BD = 256;
@@ -1837,6 +1960,11 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // One round of one workgroup per CU at most.
     n_ts = 256 / pl.n_dt;
     if (n_ts < 1) n_ts = 1;
+  } else if (pl.cvar == 7) {
+    // One round of two workgroups (the two column halves) per CU at most.
+    n_ts = 512 / (2 * pl.n_dt);
+    if (n_ts < 1) n_ts = 1;
+    if (n_ts > 8 && pl.few_ts) n_ts = 8;
   } else if (pl.cvar >= 3 && pl.few_ts) {
     n_ts = 256 / pl.n_dt;  // one round of 256 eight-wave workgroups at most
     if (n_ts < 1) n_ts = 1;
@@ -1910,8 +2038,8 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.
-  pl.use_part = !det && env_int("LOGRA_CON_PART", (pl.n_ts >= 3 || pl.cvar == 6) ? 1 : 0) && pl.n_ts > 1 &&
-                (pl.cvar == 3 || pl.cvar == 4 || pl.cvar == 6);
+  pl.use_part = !det && env_int("LOGRA_CON_PART", (pl.n_ts >= 3 || pl.cvar >= 6) ? 1 : 0) && pl.n_ts > 1 &&
+                (pl.cvar == 3 || pl.cvar == 4 || pl.cvar == 6 || pl.cvar == 7);
   pl.bigdp = env_int("LOGRA_CON_BIGDP", 2) == 1 ? 1 : 2;
   pl.off_cpart = off;
   if (pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
@@ -1998,6 +2126,10 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
     case 4:
       if (pl.bigdp == 2) hipLaunchKernelGGL((contract_big_kernel<16, 2, 2>), dim3(grid), dim3(512), 0, s, p);
       else hipLaunchKernelGGL((contract_big_kernel<16, 2, 1>), dim3(grid), dim3(512), 0, s, p);
+      return true;
+    case 7:
+      hipLaunchKernelGGL((contract_half_kernel<2>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts * 2, 8)),
+                         dim3(256), 0, s, p);
       return true;
     case 6:
       if (pl.cwide == 2) {

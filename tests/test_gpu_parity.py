@@ -246,6 +246,9 @@ R256_PLANS = [
     {"LOGRA_CON_WIDE": 2},
     {"LOGRA_CON_WIDE": 1, "LOGRA_CON_TS": 1},
     {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_BIGDP": 1},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_HALF": 0},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_HALF": 1, "LOGRA_CON_TS": 5},
+    {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_HALF": 1, "LOGRA_CON_PART": 0, "LOGRA_CON_TS": 3},
     {"LOGRA_CON_TILE": 0, "LOGRA_CON_BIG": 1, "LOGRA_CON_TS": 2, "LOGRA_CON_PART": 0},
     {"LOGRA_CON_TILE": 1},
     {"LOGRA_CON_TILE": 1, "LOGRA_CON_WM": 2},
