@@ -242,6 +242,16 @@ __device__ __forceinline__ void mfma4_b(f32x4& c0, f32x4& c1, f32x4& c2, f32x4& 
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b));
 }
 // Eight accumulators sharing one B operand: c_q += a_q * b.
+// Two MFMAs sharing the B operand (see mfma4_b).
+__device__ __forceinline__ void mfma2_b(f32x4& c0, f32x4& c1, const u32x4& a0, const u32x4& a1, const u32x4& b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
+      : "+a"(c0), "+a"(c1)
+      : "v"(a0), "v"(a1), "v"(b));
+}
+
 __device__ __forceinline__ void mfma8_b(f32x4 (&c)[8], const u32x4 (&a)[8], const u32x4& b) {
   asm volatile(
       "s_nop 2\n\t"

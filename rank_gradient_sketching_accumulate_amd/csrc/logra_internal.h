@@ -61,6 +61,7 @@ struct SketchPlan {
   int PNW;                // projection (round-based): waves per workgroup (4 or 8)
   int pwide;              // 1: proj_wide_kernel (NB = 8 or 16, 128-token tiles, one wave per SIMD)
   int pnx;                // proj_wide_kernel: X ring depth in 32-column steps (4 or 8)
+  int pts;                // 1: proj_wide2_kernel (waves split by tokens, not columns)
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)

@@ -638,6 +638,232 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (threadIdx.x == 0) p.counters[tt] = 0u;
 }
 
+// The same projection with the waves split by tokens instead of columns:
+// wave (wt, wk) holds 32 tokens (two 16-token blocks) x all of P's columns,
+// so the two waves of a k block load disjoint rows of X (two waves loading
+// the same bytes from one CU halve its streaming rate), at the price of one
+// sign expansion per two MFMAs instead of four.
+template <int NB, int NX>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_wide2_kernel(ProjParams p) {
+  constexpr int RP = 16 * NB;
+  constexpr int NBW = NB;               // column blocks per wave: all of them
+  constexpr int MT = 2;                 // 16-token blocks per wave: half the tile
+  constexpr int TT = 64;                // tokens per workgroup
+  constexpr int WK = 4;                 // blocks per round
+  constexpr int SROW = 9;               // 8 dwords of sign bits + 1 pad dword per row
+  constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
+  constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
+  constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
+  constexpr int NGEN = RP * WK / 512;   // Philox blocks per thread and round
+  static_assert(NGEN * 512 == RP * WK, "one or two sign blocks per thread");
+  // A block's eight steps use ring slots s % NX, and the loads issued in its
+  // last NX - 1 steps belong to the next block's first steps: NX must divide
+  // 8 for both to name the same slots.
+  static_assert(NX >= 2 && 8 % NX == 0, "ring depth divides a block's eight steps");
+  static_assert(MT == 2, "one asm block of two MFMAs per column block");
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
+  __shared__ int s_last;
+
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int tt = lin / p.n_k;
+  const int ksp = lin - tt * p.n_k;
+  if (tt >= p.n_tt) return;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int wt = wave & 1, wk = wave >> 1;  // token half, k block of the round
+  const int64_t t0 = (int64_t)tt * TT;
+  const int cbb = ksp * p.cbs_per;
+  const int cbe = min(p.ncb, cbb + p.cbs_per);
+  const int nrounds = (cbe - cbb + WK - 1) / WK;
+
+  f32x4 acc[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) into
+  // sign buffer buf.  Blocks past the range are generated all the same
+  // (their X operands are zeroed) so that the code has no branch.
+  auto gen = [&](int j, int buf) {
+#pragma unroll 1
+    for (int q = 0; q < NGEN; ++q) {
+      const int b = threadIdx.x + 512 * q;
+      const int row = b % RP, wkk = b / RP;
+      uint32_t w[8];
+      philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
+      uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = w[e];
+    }
+  };
+
+  // X through a buffer descriptor (token rows past T read as zero).  Loads
+  // are unconditional: a block past the range re-reads the range's last block
+  // (in cache) and is zeroed where used, so the compiler's wait counts never
+  // take a path without the load.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
+  uint32_t rowoff[MT];
+#pragma unroll
+  for (int mb = 0; mb < MT; ++mb) rowoff[mb] = (uint32_t)((t0 + 32 * wt + 16 * mb + i) * p.ldx * 2);
+  u32x4 xr[NX][MT];
+  auto issue = [&](u32x4 (&slot)[MT], int cb, int s) {
+    const int cbl = min(cb, cbe - 1);
+    const uint32_t coff = (uint32_t)(((int64_t)cbl * 256 + 32 * s + 8 * g) * 2);
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + coff);
+  };
+  // Zero the X entries of step (cb, s) whose columns are past k or whose
+  // block is past the range (wave-uniform test; no loads inside).
+  auto xmask = [&](u32x4 (&slot)[MT], int cb, int s) {
+    const int64_t c0 = (int64_t)cb * 256 + 32 * s;
+    if (cb < cbe && c0 + 32 <= p.k) return;
+    const int64_t nv = cb < cbe ? p.k - (c0 + 8 * g) : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) slot[mb][q] &= m;
+    }
+  };
+
+  gen(0, 0);
+#pragma unroll
+  for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
+  __syncthreads();
+
+  const SignExpander ex(g);
+  for (int j = 0; j < nrounds; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
+    const int cb = cbb + WK * j + wk;
+    const uint32_t* sb = smem + buf * SBUF + (wk * RP + i) * SROW;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int t = s + NX - 1;  // the step whose loads go out now
+      issue(xr[t % NX], t < 8 ? cb : cb + WK, t & 7);
+      xmask(xr[s % NX], cb, s);
+      const u32x4(&xs)[MT] = xr[s % NX];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
+        mfma2_b(acc[nb][0], acc[nb][1], xs[0], xs[1], bsg);
+      }
+    }
+    __syncthreads();
+  }
+  // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
+  // sums are worked on in VGPRs.
+  mfma_drain();
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) mfma_touch(acc[nb][mb]);
+  f32x4 v[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) v[nb][mb] = acc[nb][mb];
+  // (Columns >= r, from sign rows the caller did not ask for, are left in P:
+  // they only feed columns of S that are never stored.)
+
+  // Sum the four wave columns in two halving rounds through LDS (the sign
+  // buffers are free: the last round ended with a barrier): wk = 2, 3 park
+  // and wk = 0, 1 add, then wk = 1 parks and wk = 0 adds.
+  float* const red = reinterpret_cast<float*>(smem);
+  auto slot = [&](int half, int nb, int mb) {
+    return red + (((half * 2 + wt) * NBW + nb) * MT + mb) * 256 + 4 * lane;
+  };
+#pragma unroll
+  for (int level = 2; level >= 1; level >>= 1) {
+    if (wk >= level && wk < 2 * level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) *reinterpret_cast<f32x4*>(slot(wk - level, nb, mb)) = v[nb][mb];
+    }
+    __syncthreads();
+    if (wk < level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) v[nb][mb] += *reinterpret_cast<const f32x4*>(slot(wk, nb, mb));
+    }
+    __syncthreads();
+  }
+  const int cb0 = 0;          // this wave holds every column block
+  const int64_t tw = t0 + 32 * wt;  // first token of this wave
+
+  if (p.n_k == 1) {
+    if (wk == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          const f32x4 o = v[nb][mb];
+          const int64_t e0 = pk_index(tw + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+          uint32_t h0, l0, h1, l1;
+          split_hi_lo2(o[0], o[1], h0, l0);
+          split_hi_lo2(o[2], o[3], h1, l1);
+          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+        }
+    }
+    return;
+  }
+
+  // Column splits across workgroups (the splits of a token tile are
+  // consecutive logical ids, all on one XCD): each split stores its fp32
+  // partial with agent-coherent (sc1) stores; the last to arrive sums them
+  // in split order and writes P, with all of a thread's loads in flight at
+  // once.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Ppart, (uint32_t)((int64_t)p.n_k * p.part_stride * 4));
+  if (wk == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) {
+        const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(tw + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+        store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
+      }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(p.counters + tt, 1u);
+    s_last = (prev == (unsigned)(p.n_k - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
+  f32x4 sum[ITEMS];
+  int64_t e0[ITEMS];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int v = threadIdx.x + 512 * q;
+    e0[q] = pk_index(t0 + 4 * (int64_t)(v / RP), v % RP, NB);
+    sum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp = 0; sp < p.n_k; ++sp) {
+    f32x4 part[ITEMS];
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q)
+      part[q] = __builtin_bit_cast(f32x4, load16_agent(rs, (uint32_t)(((int64_t)sp * p.part_stride + e0[q]) * 4)));
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) sum[q] += part[q];
+  }
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    uint32_t h0, l0, h1, l1;
+    split_hi_lo2(sum[q][0], sum[q][1], h0, l0);
+    split_hi_lo2(sum[q][2], sum[q][3], h1, l1);
+    *reinterpret_cast<u32x2*>(p.Phi + e0[q]) = u32x2{h0, h1};
+    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0[q]) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+  }
+  if (threadIdx.x == 0) p.counters[tt] = 0u;
+}
+
 // ===========================================================================
 // Projection with the Gaussian basis: P = X Z^T with Z dense (the refreshed
 // Gaussian projection), Z's bf16 hi/lo planes generated per call by
@@ -1805,6 +2031,11 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   pl.pwide = (pl.NB >= 8 && pl.ncb >= 2) ? 1 : 0;
   pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 8 ? 1 : 0;
   pl.pnx = (pl.NB == 8 && env_int("LOGRA_PROJ_NX", 4) == 8) ? 8 : 4;
+  // Waves split by tokens at NB = 8 (7B down r = 128: 101 -> 79 us; 1.5B
+  // down: 58 -> 46); at NB = 16 the doubled sign expansion costs what the
+  // disjoint X loads save (27B layers within 3 %).
+  pl.pts = env_int("LOGRA_PROJ_TS", pl.NB == 8 ? 1 : 0) ? 1 : 0;
+  if (pl.pts) pl.pnx = 4;
   pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
   pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
@@ -2050,7 +2281,9 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   if (pl.pwide) {
     const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
-    if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
+    if (pl.pts && pl.NB == 16) hipLaunchKernelGGL((proj_wide2_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.pts && pl.NB == 8) hipLaunchKernelGGL((proj_wide2_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 8 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 8) hipLaunchKernelGGL((proj_wide_kernel<8, 8>), dim3(grid), dim3(512), 0, s, p);
     else return false;

@@ -214,8 +214,10 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_BANDS": 4},
     {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 24},
     {"LOGRA_CON_BANDS": 4, "LOGRA_CON_GRID": 12},
-    {"LOGRA_PROJ_NX": 8},
-    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_TS": 0},
+    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_NK": 2, "LOGRA_PROJ_TS": 0},
+    {"LOGRA_PROJ_TS": 0},
+    {"LOGRA_PROJ_TS": 1, "LOGRA_PROJ_NK": 2},
 ]
 
 
@@ -238,6 +240,8 @@ R256_PLANS = [
     {"LOGRA_PROJ_NK": 2},
     {"LOGRA_PROJ_NK": 4},
     {"LOGRA_PROJ_NK": 3},
+    {"LOGRA_PROJ_TS": 1},
+    {"LOGRA_PROJ_TS": 1, "LOGRA_PROJ_NK": 4},
     {"LOGRA_PROJ_WIDE": 0},
     {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 4},
     {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_NK": 2},
