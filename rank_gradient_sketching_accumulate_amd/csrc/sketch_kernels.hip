@@ -2268,8 +2268,12 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   if (pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
-  // atomic adds at about one element per channel and clock.
-  pl.use_part = !det && env_int("LOGRA_CON_PART", (pl.n_ts >= 3 || pl.cvar >= 6) ? 1 : 0) && pl.n_ts > 1 &&
+  // atomic adds at about one element per channel and clock.  The half-tile
+  // contraction at three splits (the tall 17408- and 18944-row layers) is
+  // the exception: there the atomic adds overlap the other half's MFMA work
+  // and the extra pass over the partials costs more (27B up 311 -> 300 us).
+  const bool part_default = pl.cvar == 7 ? pl.n_ts >= 4 : (pl.n_ts >= 3 || pl.cvar >= 6);
+  pl.use_part = !det && env_int("LOGRA_CON_PART", part_default ? 1 : 0) && pl.n_ts > 1 &&
                 (pl.cvar == 3 || pl.cvar == 4 || pl.cvar == 6 || pl.cvar == 7);
   pl.bigdp = env_int("LOGRA_CON_BIGDP", 2) == 1 ? 1 : 2;
   pl.off_cpart = off;
