@@ -402,6 +402,63 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ===========================================================================
+// Rademacher sign table for the wide projections.  Every token tile of a call
+// multiplies by the same 16*NB x k signs; drawing them once per call (one
+// Philox4x64-10 block per row and 256-column block) instead of once per
+// token tile takes the 64-bit multiplies out of the projection's loop, where
+// they cost about as many VALU cycles as the loop has MFMA cycles.  Row i of
+// block b sits at dwords 9 (b * 16 NB + i) .. + 7 (the ninth dword pads the
+// row so that the sixteen rows an LDS read touches fall in distinct banks);
+// the kernels copy a round's four blocks into LDS as one contiguous run.
+// ===========================================================================
+constexpr int kSignRowDw = 9;
+
+size_t sign_table_bytes(int NB, int blocks) { return (size_t)blocks * 16 * NB * kSignRowDw * 4; }
+
+__global__ __launch_bounds__(256) void sign_table_kernel(uint64_t seed, int row0, int RP, int n, uint32_t* table) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int b = idx / RP, row = idx - b * RP;
+  uint32_t w[8];
+  philox_sign_block(seed, (uint32_t)(row0 + row), (uint32_t)b, w);
+  uint32_t* dst = table + (size_t)idx * kSignRowDw;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dst[e] = w[e];
+  dst[8] = 0u;
+}
+
+void sign_table_launch(uint64_t seed, int row0, int NB, int blocks, uint32_t* table, hipStream_t s) {
+  const int n = blocks * 16 * NB;
+  if (n <= 0) return;
+  hipLaunchKernelGGL(sign_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, seed, row0, 16 * NB, n, table);
+}
+
+// One round's sign rows (WK consecutive blocks from the table) through
+// registers into an LDS sign buffer of the same layout: 512 threads, u32x4
+// words.  The loads are issued whole-round ahead and stored before the
+// round's closing barrier; a word index past the run reloads the run's last
+// word and is not stored.
+template <int RP, int WK>
+struct SignRound {
+  static constexpr int N16 = WK * RP * kSignRowDw / 4;
+  static constexpr int PER = (N16 + 511) / 512;
+  static_assert(N16 * 4 == WK * RP * kSignRowDw, "whole u32x4 words per round");
+  u32x4 v[PER];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rt, int cb) {
+    const uint32_t base = (uint32_t)cb * (uint32_t)(RP * kSignRowDw / 4);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) v[q] = buf_load16(rt, (base + min((int)threadIdx.x + 512 * q, N16 - 1)) * 16u);
+  }
+  __device__ __forceinline__ void store(uint32_t* buf) const {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int w = threadIdx.x + 512 * q;
+      if (q + 1 < PER || w < N16) reinterpret_cast<u32x4*>(buf)[w] = v[q];
+    }
+  }
+};
+
+// ===========================================================================
 // Projection for ranks above 64 (NB = 8 or 16).  Eight waves, two per SIMD.
 // Wave (wn, wk) keeps the workgroup's 64 tokens x one half of P's 16*NB
 // columns in accumulators (8*NB*2 registers: 128 at NB = 16, pinned to the
@@ -410,10 +467,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // expanded sign operand feeds four MFMAs (the sign expansion is half the
 // VALU work it is when a wave holds every column), while the second wave of
 // each SIMD hides the first's VALU and memory latency.  wk picks which of a
-// round's four 256-column blocks the wave multiplies.  Each round
-// regenerates the signs of the next round's four blocks into LDS
-// (branch-free: two Philox blocks per thread at NB = 16, one at NB = 8) while
-// the current ones are multiplied; X streams through a ring of NX 32-column
+// round's four 256-column blocks the wave multiplies.  Each round copies
+// the signs of the next round's four blocks from the call's sign table into
+// registers and, at its end, into the other LDS sign buffer, while the
+// current ones are multiplied; X streams through a ring of NX 32-column
 // steps.  After the last round the four wave columns are summed through LDS
 // in two halving rounds, and the wk = 0 waves write P (or, with column
 // splits across workgroups, their fp32 partial).
@@ -429,8 +486,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
   constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
   constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
-  constexpr int NGEN = RP * WK / 512;   // Philox blocks per thread and round
-  static_assert(NGEN * 512 == RP * WK, "one or two sign blocks per thread");
+  static_assert(SROW == kSignRowDw, "the sign table's row layout");
   // A block's eight steps use ring slots s % NX, and the loads issued in its
   // last NX - 1 steps belong to the next block's first steps: NX must divide
   // 8 for both to name the same slots.
@@ -458,21 +514,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) into
-  // sign buffer buf.  Blocks past the range are generated all the same
-  // (their X operands are zeroed) so that the code has no branch.
-  auto gen = [&](int j, int buf) {
-#pragma unroll 1
-    for (int q = 0; q < NGEN; ++q) {
-      const int b = threadIdx.x + 512 * q;
-      const int row = b % RP, wkk = b / RP;
-      uint32_t w[8];
-      philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
-      uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = w[e];
-    }
-  };
+  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
+  // from the call's sign table.  Blocks past the range are copied all the
+  // same (the table covers every block a split may name; their X operands
+  // are zeroed) so that the code has no branch.
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
+  SignRound<RP, WK> sr;
 
   // X through a buffer descriptor (token rows past T read as zero).  Loads
   // are unconditional: a block past the range re-reads the range's last block
@@ -503,7 +550,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  gen(0, 0);
+  sr.load(rt, cbb);
+  sr.store(smem);
 #pragma unroll
   for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
   __syncthreads();
@@ -511,7 +559,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   const SignExpander ex(g);
   for (int j = 0; j < nrounds; ++j) {
     const int buf = j & 1;
-    if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
+    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
     const int cb = cbb + WK * j + wk;
     const uint32_t* sb = smem + buf * SBUF + (wk * RP + 16 * NBW * wn + i) * SROW;
 #pragma unroll
@@ -520,13 +568,254 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
       issue(xr[t % NX], t < 8 ? cb : cb + WK, t & 7);
       xmask(xr[s % NX], cb, s);
       const u32x4(&xs)[MT] = xr[s % NX];
+      // The step's sign dwords are read together, so that one LDS latency
+      // covers all of them.
+      uint32_t sw[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) sw[nb] = sb[16 * nb * SROW + s];
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
+        const u32x4 bsg = ex(sw[nb]);
         mfma4_b(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], xs[0], xs[1], xs[2], xs[3], bsg);
       }
     }
+    sr.store(smem + (buf ^ 1) * SBUF);
     __syncthreads();
+  }
+  // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
+  // sums are worked on in VGPRs.
+  mfma_drain();
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) mfma_touch(acc[nb][mb]);
+  f32x4 v[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) v[nb][mb] = acc[nb][mb];
+  // (Columns >= r, from sign rows the caller did not ask for, are left in P:
+  // they only feed columns of S that are never stored.)
+
+  // Sum the four wave columns in two halving rounds through LDS (the sign
+  // buffers are free: the last round ended with a barrier): wk = 2, 3 park
+  // and wk = 0, 1 add, then wk = 1 parks and wk = 0 adds.
+  float* const red = reinterpret_cast<float*>(smem);
+  auto slot = [&](int half, int nb, int mb) {
+    return red + (((half * 2 + wn) * NBW + nb) * MT + mb) * 256 + 4 * lane;
+  };
+#pragma unroll
+  for (int level = 2; level >= 1; level >>= 1) {
+    if (wk >= level && wk < 2 * level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) *reinterpret_cast<f32x4*>(slot(wk - level, nb, mb)) = v[nb][mb];
+    }
+    __syncthreads();
+    if (wk < level) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) v[nb][mb] += *reinterpret_cast<const f32x4*>(slot(wk, nb, mb));
+    }
+    __syncthreads();
+  }
+  const int cb0 = NBW * wn;  // first column block of this wave
+
+  if (p.n_k == 1) {
+    if (wk == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MT; ++mb) {
+          const f32x4 o = v[nb][mb];
+          const int64_t e0 = pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+          uint32_t h0, l0, h1, l1;
+          split_hi_lo2(o[0], o[1], h0, l0);
+          split_hi_lo2(o[2], o[3], h1, l1);
+          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
+          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+        }
+    }
+    return;
+  }
+
+  // Column splits across workgroups (the splits of a token tile are
+  // consecutive logical ids, all on one XCD): each split stores its fp32
+  // partial with agent-coherent (sc1) stores; the last to arrive sums them
+  // in split order and writes P, with all of a thread's loads in flight at
+  // once.
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Ppart, (uint32_t)((int64_t)p.n_k * p.part_stride * 4));
+  if (wk == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) {
+        const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
+        store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
+      }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(p.counters + tt, 1u);
+    s_last = (prev == (unsigned)(p.n_k - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
+  f32x4 sum[ITEMS];
+  int64_t e0[ITEMS];
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int v = threadIdx.x + 512 * q;
+    e0[q] = pk_index(t0 + 4 * (int64_t)(v / RP), v % RP, NB);
+    sum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int sp = 0; sp < p.n_k; ++sp) {
+    f32x4 part[ITEMS];
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q)
+      part[q] = __builtin_bit_cast(f32x4, load16_agent(rs, (uint32_t)(((int64_t)sp * p.part_stride + e0[q]) * 4)));
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) sum[q] += part[q];
+  }
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    uint32_t h0, l0, h1, l1;
+    split_hi_lo2(sum[q][0], sum[q][1], h0, l0);
+    split_hi_lo2(sum[q][2], sum[q][3], h1, l1);
+    *reinterpret_cast<u32x2*>(p.Phi + e0[q]) = u32x2{h0, h1};
+    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0[q]) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
+  }
+  if (threadIdx.x == 0) p.counters[tt] = 0u;
+}
+
+// ===========================================================================
+// Projection for ranks above 64 with X staged through LDS.  The same eight
+// waves and accumulators as proj_wide_kernel, but within a round of four
+// 256-column blocks the four k waves take interleaved 32-column slices of
+// one 128-column slab per step (wave wk: columns 128 s + 32 wk .. + 31 of the
+// round), and the workgroup loads each slab once: thread q moves 16-byte
+// chunk q % 16 of rows q / 16 and q / 16 + 32, so one load instruction covers
+// four rows x 256 contiguous bytes (two whole cache lines per row) instead of
+// sixteen rows x 64 bytes, and no X byte is loaded twice by one CU.  (With
+// the sixteen-row pattern the texture addresser took about 70 cycles per
+// load and set the kernel's pace.)  In LDS, chunk c of row t sits at slot
+// c ^ (t & 15) of the row's 256 bytes, so the sixteen rows of an MFMA operand
+// read fall in distinct banks.  Slab u + 2 is loaded into registers during
+// step u and slab u + 1 is stored into the other LDS buffer at the end of
+// step u, before the step's barrier.
+// ===========================================================================
+template <int NB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_lds_kernel(ProjParams p) {
+  constexpr int RP = 16 * NB;
+  constexpr int NBW = NB / 2;           // column blocks per wave
+  constexpr int MT = 4;                 // 16-token blocks per wave: the whole tile
+  constexpr int TT = 16 * MT;           // tokens per workgroup
+  constexpr int WK = 4;                 // blocks per round
+  constexpr int SROW = 9;               // 8 dwords of sign bits + 1 pad dword per row
+  constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
+  constexpr int XBUF = TT * 64;         // dwords of one X slab: 64 rows x 128 columns
+  constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
+  constexpr int MAIN = 2 * SBUF + 2 * XBUF;
+  constexpr int LDSW = (MAIN > RED) ? MAIN : RED;
+  static_assert(SROW == kSignRowDw, "the sign table's row layout");
+  static_assert((2 * SBUF) % 4 == 0, "X slabs on 16-byte boundaries");
+  __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
+  __shared__ int s_last;
+  uint32_t* const xlds = smem + 2 * SBUF;
+
+  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
+  const int tt = lin / p.n_k;
+  const int ksp = lin - tt * p.n_k;
+  if (tt >= p.n_tt) return;
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  const int wn = wave & 1, wk = wave >> 1;
+  const int64_t t0 = (int64_t)tt * TT;
+  const int cbb = ksp * p.cbs_per;
+  const int cbe = min(p.ncb, cbb + p.cbs_per);
+  const int nrounds = (cbe - cbb + WK - 1) / WK;
+
+  f32x4 acc[NBW][MT];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
+  // from the call's sign table (blocks past the range too: the table covers
+  // every block a split may name, and their X is zeroed).
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
+  SignRound<RP, WK> sr;
+
+  // X slabs.  Rows past T read as zero (buffer range); columns past k or
+  // past the split's blocks are zeroed when staged.  Loads are unconditional
+  // (a slab past the last round reads whatever lies there and is zeroed).
+  const int sc = threadIdx.x & 15, srow = threadIdx.x >> 4;  // chunk, row (and row + 32)
+  const int64_t xbytes = p.T * p.ldx * 2;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)xbytes);
+  const int64_t rowoff0 = (t0 + srow) * p.ldx * 2, rowoff1 = (t0 + srow + 32) * p.ldx * 2;
+  const int64_t lim = min(p.k, (int64_t)cbe * 256);  // first column that stages as zero
+  auto slab_col = [&](int u) { return (int64_t)(cbb + WK * (u >> 3)) * 256 + 128 * (u & 7) + 8 * sc; };
+  auto xload = [&](u32x4 (&v)[2], int u) {
+    const int64_t c2 = slab_col(u) * 2;
+    v[0] = buf_load16(rx, (uint32_t)min(rowoff0 + c2, (int64_t)0xFFFFFFF0));
+    v[1] = buf_load16(rx, (uint32_t)min(rowoff1 + c2, (int64_t)0xFFFFFFF0));
+  };
+  auto xstore = [&](u32x4 (&v)[2], int u) {
+    const int64_t col = slab_col(u);
+    if (col + 8 > lim) {
+      const int64_t nv = lim - col;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
+        v[0][q] &= m;
+        v[1][q] &= m;
+      }
+    }
+    uint32_t* b = xlds + (u & 1) * XBUF;
+    *reinterpret_cast<u32x4*>(b + srow * 64 + ((sc ^ (srow & 15)) * 4)) = v[0];
+    *reinterpret_cast<u32x4*>(b + (srow + 32) * 64 + ((sc ^ (srow & 15)) * 4)) = v[1];
+  };
+
+  u32x4 xv[2][2];
+  sr.load(rt, cbb);
+  xload(xv[0], 0);
+  xload(xv[1], 1);
+  sr.store(smem);
+  xstore(xv[0], 0);
+  __syncthreads();
+
+  const SignExpander ex(g);
+  const int xoff = ((4 * wk + g) ^ i) * 4;  // this lane's chunk slot in its rows
+  for (int j = 0; j < nrounds; ++j) {
+    const int buf = j & 1;
+    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int u = 8 * j + s;
+      xload(xv[s & 1], u + 2);  // slot of slab u (stored at the end of step u - 1)
+      const uint32_t* xb = xlds + (s & 1) * XBUF + i * 64 + xoff;
+      u32x4 a[MT];
+#pragma unroll
+      for (int mb = 0; mb < MT; ++mb) a[mb] = *reinterpret_cast<const u32x4*>(xb + 16 * mb * 64);
+      const uint32_t* sb = smem + buf * SBUF + ((s >> 1) * RP + 16 * NBW * wn + i) * SROW + 4 * (s & 1) + wk;
+      uint32_t sw[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) sw[nb] = sb[16 * nb * SROW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const u32x4 bsg = ex(sw[nb]);
+        mfma4_b(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], a[0], a[1], a[2], a[3], bsg);
+      }
+      xstore(xv[(s + 1) & 1], u + 1);
+      if (s == 7) sr.store(smem + (buf ^ 1) * SBUF);
+      __syncthreads();
+    }
   }
   // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
   // sums are worked on in VGPRs.
@@ -654,8 +943,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
   constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
   constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
-  constexpr int NGEN = RP * WK / 512;   // Philox blocks per thread and round
-  static_assert(NGEN * 512 == RP * WK, "one or two sign blocks per thread");
+  static_assert(SROW == kSignRowDw, "the sign table's row layout");
   // A block's eight steps use ring slots s % NX, and the loads issued in its
   // last NX - 1 steps belong to the next block's first steps: NX must divide
   // 8 for both to name the same slots.
@@ -683,21 +971,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) into
-  // sign buffer buf.  Blocks past the range are generated all the same
-  // (their X operands are zeroed) so that the code has no branch.
-  auto gen = [&](int j, int buf) {
-#pragma unroll 1
-    for (int q = 0; q < NGEN; ++q) {
-      const int b = threadIdx.x + 512 * q;
-      const int row = b % RP, wkk = b / RP;
-      uint32_t w[8];
-      philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
-      uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = w[e];
-    }
-  };
+  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
+  // from the call's sign table.  Blocks past the range are copied all the
+  // same (the table covers every block a split may name; their X operands
+  // are zeroed) so that the code has no branch.
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
+  SignRound<RP, WK> sr;
 
   // X through a buffer descriptor (token rows past T read as zero).  Loads
   // are unconditional: a block past the range re-reads the range's last block
@@ -728,7 +1007,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  gen(0, 0);
+  sr.load(rt, cbb);
+  sr.store(smem);
 #pragma unroll
   for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
   __syncthreads();
@@ -736,7 +1016,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   const SignExpander ex(g);
   for (int j = 0; j < nrounds; ++j) {
     const int buf = j & 1;
-    if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
+    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
     const int cb = cbb + WK * j + wk;
     const uint32_t* sb = smem + buf * SBUF + (wk * RP + i) * SROW;
 #pragma unroll
@@ -751,6 +1031,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
         mfma2_b(acc[nb][0], acc[nb][1], xs[0], xs[1], bsg);
       }
     }
+    sr.store(smem + (buf ^ 1) * SBUF);
     __syncthreads();
   }
   // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
@@ -2008,6 +2289,8 @@ void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part) {
   pl.off_phi = pl.off_plo = 0;
   pl.off_part = off;
   if (proj_part && pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
+  pl.off_signs = off;
+  if (proj_part) off += align_up(sign_table_bytes(pl.NB, pl.sign_blocks), 256);
   pl.off_cpart = off;
   if (con_part && pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
@@ -2036,6 +2319,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   // disjoint X loads save (27B layers within 3 %).
   pl.pts = env_int("LOGRA_PROJ_TS", pl.NB == 8 ? 1 : 0) ? 1 : 0;
   if (pl.pts) pl.pnx = 4;
+  // X staged through LDS (four rows x 256 bytes per load instruction): 27B
+  // layers 70 -> 57 (attention), 70 -> 60 (up), 191 -> 160 us (down); 7B
+  // down at r = 128 81 -> 71 us against the token-split kernel.
+  pl.plds = pl.pwide && env_int("LOGRA_PROJ_LDS", 1) ? 1 : 0;
   pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
   pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
@@ -2058,6 +2345,8 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // the grid must keep each tile's splits on one XCD: n_k a power of two
     // dividing the per-XCD share (the launch rounds the grid up to 8 * n_k)
     while (pl.n_k & (pl.n_k - 1)) ++pl.n_k;
+    // Every block a split may name, past k included (those have zeroed X).
+    pl.sign_blocks = pl.n_k * pl.cbs_per;
   } else if (pl.small_proj) {
     // More tokens per workgroup amortise the signs; keep >= 256 workgroups.
     int MBW = 4;
@@ -2266,6 +2555,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   off += align_up((size_t)pl.Tpad * RP * 2, 256);
   pl.off_part = off;
   if (pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
+  // The sign table precedes the contraction's partial tiles, so that callers
+  // that keep no partial tiles may place their own data from off_cpart on.
+  pl.off_signs = off;
+  off += align_up(sign_table_bytes(pl.NB, pl.sign_blocks), 256);
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.  The half-tile
@@ -2285,6 +2578,12 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   if (pl.pwide) {
     const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
+    if (pl.plds) {
+      if (pl.NB == 16) hipLaunchKernelGGL((proj_lds_kernel<16>), dim3(grid), dim3(512), 0, s, p);
+      else if (pl.NB == 8) hipLaunchKernelGGL((proj_lds_kernel<8>), dim3(grid), dim3(512), 0, s, p);
+      else return false;
+      return true;
+    }
     if (pl.pts && pl.NB == 16) hipLaunchKernelGGL((proj_wide2_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.pts && pl.NB == 8) hipLaunchKernelGGL((proj_wide2_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
