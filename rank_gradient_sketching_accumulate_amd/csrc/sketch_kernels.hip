@@ -1805,6 +1805,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
       const int m = m0 + u;
       load_p(stg[u % DP], m + DP);
       load_y(y[(u + DP) % (DP + 1)], m + DP);
+      // Keep the loads at the top of the step: left to itself the scheduler
+      // sinks them below the step's MFMAs (their registers then hold the
+      // transposed operands), which halves the prefetch distance.
+      __builtin_amdgcn_sched_barrier(0);
       if (m < nsteps) {
         u32x4 a[kDC];
         transpose_dy(y[u % (DP + 1)], a);
