@@ -64,10 +64,7 @@ struct SketchPlan {
   int small_proj;         // 1: proj_small_kernel (all signs of k in LDS)
   int MBW, WK;            // projection: 16-token blocks per wave, waves along k
   int PNW;                // projection (round-based): waves per workgroup (4 or 8)
-  int plds;               // 1 (with pwide): proj_lds_kernel, X staged through LDS
-  int pwide;              // 1: proj_wide_kernel (NB = 8 or 16, 128-token tiles, one wave per SIMD)
-  int pnx;                // proj_wide_kernel: X ring depth in 32-column steps (4 or 8)
-  int pts;                // 1: proj_wide2_kernel (waves split by tokens, not columns)
+  int pwide;              // 1: proj_lds_kernel (NB = 8 or 16, 64-token tiles, X staged through LDS)
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)

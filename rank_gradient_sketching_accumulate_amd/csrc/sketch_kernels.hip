@@ -459,254 +459,29 @@ struct SignRound {
 };
 
 // ===========================================================================
-// Projection for ranks above 64 (NB = 8 or 16).  Eight waves, two per SIMD.
-// Wave (wn, wk) keeps the workgroup's 64 tokens x one half of P's 16*NB
-// columns in accumulators (8*NB*2 registers: 128 at NB = 16, pinned to the
-// AGPR half of the wave's registers so that its VGPRs hold the X ring and
-// the sign work), so each
-// expanded sign operand feeds four MFMAs (the sign expansion is half the
-// VALU work it is when a wave holds every column), while the second wave of
-// each SIMD hides the first's VALU and memory latency.  wk picks which of a
-// round's four 256-column blocks the wave multiplies.  Each round copies
-// the signs of the next round's four blocks from the call's sign table into
-// registers and, at its end, into the other LDS sign buffer, while the
-// current ones are multiplied; X streams through a ring of NX 32-column
-// steps.  After the last round the four wave columns are summed through LDS
-// in two halving rounds, and the wk = 0 waves write P (or, with column
-// splits across workgroups, their fp32 partial).
-// ===========================================================================
-template <int NB, int NX>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_wide_kernel(ProjParams p) {
-  constexpr int RP = 16 * NB;
-  constexpr int NBW = NB / 2;           // column blocks per wave
-  constexpr int MT = 4;                 // 16-token blocks per wave: the whole tile
-  constexpr int TT = 16 * MT;           // tokens per workgroup
-  constexpr int WK = 4;                 // blocks per round
-  constexpr int SROW = 9;               // 8 dwords of sign bits + 1 pad dword per row
-  constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
-  constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
-  constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
-  static_assert(SROW == kSignRowDw, "the sign table's row layout");
-  // A block's eight steps use ring slots s % NX, and the loads issued in its
-  // last NX - 1 steps belong to the next block's first steps: NX must divide
-  // 8 for both to name the same slots.
-  static_assert(NX >= 2 && 8 % NX == 0, "ring depth divides a block's eight steps");
-  static_assert(MT == 4, "one asm block of four MFMAs per column block");
-  __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
-  __shared__ int s_last;
-
-  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int tt = lin / p.n_k;
-  const int ksp = lin - tt * p.n_k;
-  if (tt >= p.n_tt) return;
-
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, i = lane & 15;
-  const int wn = wave & 1, wk = wave >> 1;
-  const int64_t t0 = (int64_t)tt * TT;
-  const int cbb = ksp * p.cbs_per;
-  const int cbe = min(p.ncb, cbb + p.cbs_per);
-  const int nrounds = (cbe - cbb + WK - 1) / WK;
-
-  f32x4 acc[NBW][MT];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
-  // from the call's sign table.  Blocks past the range are copied all the
-  // same (the table covers every block a split may name; their X operands
-  // are zeroed) so that the code has no branch.
-  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
-  SignRound<RP, WK> sr;
-
-  // X through a buffer descriptor (token rows past T read as zero).  Loads
-  // are unconditional: a block past the range re-reads the range's last block
-  // (in cache) and is zeroed where used, so the compiler's wait counts never
-  // take a path without the load.
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
-  uint32_t rowoff[MT];
-#pragma unroll
-  for (int mb = 0; mb < MT; ++mb) rowoff[mb] = (uint32_t)((t0 + 16 * mb + i) * p.ldx * 2);
-  u32x4 xr[NX][MT];
-  auto issue = [&](u32x4 (&slot)[MT], int cb, int s) {
-    const int cbl = min(cb, cbe - 1);
-    const uint32_t coff = (uint32_t)(((int64_t)cbl * 256 + 32 * s + 8 * g) * 2);
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + coff);
-  };
-  // Zero the X entries of step (cb, s) whose columns are past k or whose
-  // block is past the range (wave-uniform test; no loads inside).
-  auto xmask = [&](u32x4 (&slot)[MT], int cb, int s) {
-    const int64_t c0 = (int64_t)cb * 256 + 32 * s;
-    if (cb < cbe && c0 + 32 <= p.k) return;
-    const int64_t nv = cb < cbe ? p.k - (c0 + 8 * g) : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int mb = 0; mb < MT; ++mb) slot[mb][q] &= m;
-    }
-  };
-
-  sr.load(rt, cbb);
-  sr.store(smem);
-#pragma unroll
-  for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
-  __syncthreads();
-
-  const SignExpander ex(g);
-  for (int j = 0; j < nrounds; ++j) {
-    const int buf = j & 1;
-    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
-    const int cb = cbb + WK * j + wk;
-    const uint32_t* sb = smem + buf * SBUF + (wk * RP + 16 * NBW * wn + i) * SROW;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int t = s + NX - 1;  // the step whose loads go out now
-      issue(xr[t % NX], t < 8 ? cb : cb + WK, t & 7);
-      xmask(xr[s % NX], cb, s);
-      const u32x4(&xs)[MT] = xr[s % NX];
-      // The step's sign dwords are read together, so that one LDS latency
-      // covers all of them.
-      uint32_t sw[NBW];
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) sw[nb] = sb[16 * nb * SROW + s];
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const u32x4 bsg = ex(sw[nb]);
-        mfma4_b(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], xs[0], xs[1], xs[2], xs[3], bsg);
-      }
-    }
-    sr.store(smem + (buf ^ 1) * SBUF);
-    __syncthreads();
-  }
-  // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
-  // sums are worked on in VGPRs.
-  mfma_drain();
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) mfma_touch(acc[nb][mb]);
-  f32x4 v[NBW][MT];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) v[nb][mb] = acc[nb][mb];
-  // (Columns >= r, from sign rows the caller did not ask for, are left in P:
-  // they only feed columns of S that are never stored.)
-
-  // Sum the four wave columns in two halving rounds through LDS (the sign
-  // buffers are free: the last round ended with a barrier): wk = 2, 3 park
-  // and wk = 0, 1 add, then wk = 1 parks and wk = 0 adds.
-  float* const red = reinterpret_cast<float*>(smem);
-  auto slot = [&](int half, int nb, int mb) {
-    return red + (((half * 2 + wn) * NBW + nb) * MT + mb) * 256 + 4 * lane;
-  };
-#pragma unroll
-  for (int level = 2; level >= 1; level >>= 1) {
-    if (wk >= level && wk < 2 * level) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) *reinterpret_cast<f32x4*>(slot(wk - level, nb, mb)) = v[nb][mb];
-    }
-    __syncthreads();
-    if (wk < level) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) v[nb][mb] += *reinterpret_cast<const f32x4*>(slot(wk, nb, mb));
-    }
-    __syncthreads();
-  }
-  const int cb0 = NBW * wn;  // first column block of this wave
-
-  if (p.n_k == 1) {
-    if (wk == 0) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) {
-          const f32x4 o = v[nb][mb];
-          const int64_t e0 = pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
-          uint32_t h0, l0, h1, l1;
-          split_hi_lo2(o[0], o[1], h0, l0);
-          split_hi_lo2(o[2], o[3], h1, l1);
-          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
-          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
-        }
-    }
-    return;
-  }
-
-  // Column splits across workgroups (the splits of a token tile are
-  // consecutive logical ids, all on one XCD): each split stores its fp32
-  // partial with agent-coherent (sc1) stores; the last to arrive sums them
-  // in split order and writes P, with all of a thread's loads in flight at
-  // once.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Ppart, (uint32_t)((int64_t)p.n_k * p.part_stride * 4));
-  if (wk == 0) {
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MT; ++mb) {
-        const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
-        store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
-      }
-  }
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(p.counters + tt, 1u);
-    s_last = (prev == (unsigned)(p.n_k - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
-  f32x4 sum[ITEMS];
-  int64_t e0[ITEMS];
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    const int v = threadIdx.x + 512 * q;
-    e0[q] = pk_index(t0 + 4 * (int64_t)(v / RP), v % RP, NB);
-    sum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int sp = 0; sp < p.n_k; ++sp) {
-    f32x4 part[ITEMS];
-#pragma unroll
-    for (int q = 0; q < ITEMS; ++q)
-      part[q] = __builtin_bit_cast(f32x4, load16_agent(rs, (uint32_t)(((int64_t)sp * p.part_stride + e0[q]) * 4)));
-#pragma unroll
-    for (int q = 0; q < ITEMS; ++q) sum[q] += part[q];
-  }
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    uint32_t h0, l0, h1, l1;
-    split_hi_lo2(sum[q][0], sum[q][1], h0, l0);
-    split_hi_lo2(sum[q][2], sum[q][3], h1, l1);
-    *reinterpret_cast<u32x2*>(p.Phi + e0[q]) = u32x2{h0, h1};
-    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0[q]) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
-  }
-  if (threadIdx.x == 0) p.counters[tt] = 0u;
-}
-
-// ===========================================================================
-// Projection for ranks above 64 with X staged through LDS.  The same eight
-// waves and accumulators as proj_wide_kernel, but within a round of four
-// 256-column blocks the four k waves take interleaved 32-column slices of
-// one 128-column slab per step (wave wk: columns 128 s + 32 wk .. + 31 of the
-// round), and the workgroup loads each slab once: thread q moves 16-byte
-// chunk q % 16 of rows q / 16 and q / 16 + 32, so one load instruction covers
-// four rows x 256 contiguous bytes (two whole cache lines per row) instead of
-// sixteen rows x 64 bytes, and no X byte is loaded twice by one CU.  (With
-// the sixteen-row pattern the texture addresser took about 70 cycles per
-// load and set the kernel's pace.)  In LDS, chunk c of row t sits at slot
-// c ^ (t & 15) of the row's 256 bytes, so the sixteen rows of an MFMA operand
-// read fall in distinct banks.  Slab u + 2 is loaded into registers during
-// step u and slab u + 1 is stored into the other LDS buffer at the end of
-// step u, before the step's barrier.
+// Projection for ranks above 64 (NB = 8 or 16), X staged through LDS.
+// Eight waves, two per SIMD.  Wave (wn, wk) keeps the workgroup's 64 tokens
+// x one half of P's 16*NB columns in accumulators (8*NB*2 registers: 128 at
+// NB = 16, pinned to the AGPR half of the wave's registers), so that each
+// expanded sign operand feeds four MFMAs.  The k range goes in rounds of
+// four 256-column blocks; within a round the four k waves take interleaved
+// 32-column slices of one 128-column slab per step (wave wk: columns
+// 128 s + 32 wk .. + 31 of the round).  The workgroup loads each slab once:
+// thread q moves 16-byte chunk q % 16 of rows q / 16 and q / 16 + 32, so one
+// load instruction covers four rows x 256 contiguous bytes (two whole cache
+// lines per row) and no X byte is loaded twice by one CU.  (Sixteen rows x
+// 64 bytes per instruction, the MFMA operand's own layout, kept the texture
+// addresser busy about 70 cycles per load and set the kernel's pace.)  In
+// LDS, chunk c of row t sits at slot c ^ (t & 15) of the row's 256 bytes, so
+// the sixteen rows of an MFMA operand read fall in distinct banks.  Slab
+// u + 2 is loaded into registers during step u and slab u + 1 is stored into
+// the other LDS buffer at the end of step u, before the step's barrier.
+// Each round copies the signs of the next round's four blocks from the
+// call's sign table into registers and, at its end, into the other LDS sign
+// buffer.  After the last round the four wave columns are summed through
+// LDS in two halving rounds, and the wk = 0 waves write P (or, with column
+// splits across workgroups, their fp32 partial; the last split to arrive
+// sums the partials).
 // ===========================================================================
 template <int NB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_lds_kernel(ProjParams p) {
@@ -763,8 +538,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto slab_col = [&](int u) { return (int64_t)(cbb + WK * (u >> 3)) * 256 + 128 * (u & 7) + 8 * sc; };
   auto xload = [&](u32x4 (&v)[2], int u) {
     const int64_t c2 = slab_col(u) * 2;
-    v[0] = buf_load16(rx, (uint32_t)min(rowoff0 + c2, (int64_t)0xFFFFFFF0));
-    v[1] = buf_load16(rx, (uint32_t)min(rowoff1 + c2, (int64_t)0xFFFFFFF0));
+    const int64_t o0 = rowoff0 + c2, o1 = rowoff1 + c2;  // past the range: clamped, reads zero
+    v[0] = buf_load16(rx, (uint32_t)(o0 < 0xFFFFFFF0ll ? o0 : 0xFFFFFFF0ll));
+    v[1] = buf_load16(rx, (uint32_t)(o1 < 0xFFFFFFF0ll ? o1 : 0xFFFFFFF0ll));
   };
   auto xstore = [&](u32x4 (&v)[2], int u) {
     const int64_t col = slab_col(u);
@@ -888,224 +664,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int mb = 0; mb < MT; ++mb) {
         const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(t0 + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
-        store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
-      }
-  }
-  wait_vmem();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(p.counters + tt, 1u);
-    s_last = (prev == (unsigned)(p.n_k - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
-  f32x4 sum[ITEMS];
-  int64_t e0[ITEMS];
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    const int v = threadIdx.x + 512 * q;
-    e0[q] = pk_index(t0 + 4 * (int64_t)(v / RP), v % RP, NB);
-    sum[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int sp = 0; sp < p.n_k; ++sp) {
-    f32x4 part[ITEMS];
-#pragma unroll
-    for (int q = 0; q < ITEMS; ++q)
-      part[q] = __builtin_bit_cast(f32x4, load16_agent(rs, (uint32_t)(((int64_t)sp * p.part_stride + e0[q]) * 4)));
-#pragma unroll
-    for (int q = 0; q < ITEMS; ++q) sum[q] += part[q];
-  }
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    uint32_t h0, l0, h1, l1;
-    split_hi_lo2(sum[q][0], sum[q][1], h0, l0);
-    split_hi_lo2(sum[q][2], sum[q][3], h1, l1);
-    *reinterpret_cast<u32x2*>(p.Phi + e0[q]) = u32x2{h0, h1};
-    if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0[q]) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
-  }
-  if (threadIdx.x == 0) p.counters[tt] = 0u;
-}
-
-// The same projection with the waves split by tokens instead of columns:
-// wave (wt, wk) holds 32 tokens (two 16-token blocks) x all of P's columns,
-// so the two waves of a k block load disjoint rows of X (two waves loading
-// the same bytes from one CU halve its streaming rate), at the price of one
-// sign expansion per two MFMAs instead of four.
-template <int NB, int NX>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void proj_wide2_kernel(ProjParams p) {
-  constexpr int RP = 16 * NB;
-  constexpr int NBW = NB;               // column blocks per wave: all of them
-  constexpr int MT = 2;                 // 16-token blocks per wave: half the tile
-  constexpr int TT = 64;                // tokens per workgroup
-  constexpr int WK = 4;                 // blocks per round
-  constexpr int SROW = 9;               // 8 dwords of sign bits + 1 pad dword per row
-  constexpr int SBUF = WK * RP * SROW;  // dwords of one sign buffer
-  constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
-  constexpr int LDSW = (2 * SBUF > RED) ? 2 * SBUF : RED;
-  static_assert(SROW == kSignRowDw, "the sign table's row layout");
-  // A block's eight steps use ring slots s % NX, and the loads issued in its
-  // last NX - 1 steps belong to the next block's first steps: NX must divide
-  // 8 for both to name the same slots.
-  static_assert(NX >= 2 && 8 % NX == 0, "ring depth divides a block's eight steps");
-  static_assert(MT == 2, "one asm block of two MFMAs per column block");
-  __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
-  __shared__ int s_last;
-
-  const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int tt = lin / p.n_k;
-  const int ksp = lin - tt * p.n_k;
-  if (tt >= p.n_tt) return;
-
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, i = lane & 15;
-  const int wt = wave & 1, wk = wave >> 1;  // token half, k block of the round
-  const int64_t t0 = (int64_t)tt * TT;
-  const int cbb = ksp * p.cbs_per;
-  const int cbe = min(p.ncb, cbb + p.cbs_per);
-  const int nrounds = (cbe - cbb + WK - 1) / WK;
-
-  f32x4 acc[NBW][MT];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
-  // from the call's sign table.  Blocks past the range are copied all the
-  // same (the table covers every block a split may name; their X operands
-  // are zeroed) so that the code has no branch.
-  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
-  SignRound<RP, WK> sr;
-
-  // X through a buffer descriptor (token rows past T read as zero).  Loads
-  // are unconditional: a block past the range re-reads the range's last block
-  // (in cache) and is zeroed where used, so the compiler's wait counts never
-  // take a path without the load.
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)(p.T * p.ldx * 2));
-  uint32_t rowoff[MT];
-#pragma unroll
-  for (int mb = 0; mb < MT; ++mb) rowoff[mb] = (uint32_t)((t0 + 32 * wt + 16 * mb + i) * p.ldx * 2);
-  u32x4 xr[NX][MT];
-  auto issue = [&](u32x4 (&slot)[MT], int cb, int s) {
-    const int cbl = min(cb, cbe - 1);
-    const uint32_t coff = (uint32_t)(((int64_t)cbl * 256 + 32 * s + 8 * g) * 2);
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) slot[mb] = buf_load16(rx, rowoff[mb] + coff);
-  };
-  // Zero the X entries of step (cb, s) whose columns are past k or whose
-  // block is past the range (wave-uniform test; no loads inside).
-  auto xmask = [&](u32x4 (&slot)[MT], int cb, int s) {
-    const int64_t c0 = (int64_t)cb * 256 + 32 * s;
-    if (cb < cbe && c0 + 32 <= p.k) return;
-    const int64_t nv = cb < cbe ? p.k - (c0 + 8 * g) : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int mb = 0; mb < MT; ++mb) slot[mb][q] &= m;
-    }
-  };
-
-  sr.load(rt, cbb);
-  sr.store(smem);
-#pragma unroll
-  for (int s = 0; s < NX - 1; ++s) issue(xr[s], cbb + wk, s);
-  __syncthreads();
-
-  const SignExpander ex(g);
-  for (int j = 0; j < nrounds; ++j) {
-    const int buf = j & 1;
-    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
-    const int cb = cbb + WK * j + wk;
-    const uint32_t* sb = smem + buf * SBUF + (wk * RP + i) * SROW;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int t = s + NX - 1;  // the step whose loads go out now
-      issue(xr[t % NX], t < 8 ? cb : cb + WK, t & 7);
-      xmask(xr[s % NX], cb, s);
-      const u32x4(&xs)[MT] = xr[s % NX];
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const u32x4 bsg = ex(sb[16 * nb * SROW + s]);
-        mfma2_b(acc[nb][0], acc[nb][1], xs[0], xs[1], bsg);
-      }
-    }
-    sr.store(smem + (buf ^ 1) * SBUF);
-    __syncthreads();
-  }
-  // The accumulators live in AGPRs (pinned by the MFMA asm); from here on the
-  // sums are worked on in VGPRs.
-  mfma_drain();
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) mfma_touch(acc[nb][mb]);
-  f32x4 v[NBW][MT];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-    for (int mb = 0; mb < MT; ++mb) v[nb][mb] = acc[nb][mb];
-  // (Columns >= r, from sign rows the caller did not ask for, are left in P:
-  // they only feed columns of S that are never stored.)
-
-  // Sum the four wave columns in two halving rounds through LDS (the sign
-  // buffers are free: the last round ended with a barrier): wk = 2, 3 park
-  // and wk = 0, 1 add, then wk = 1 parks and wk = 0 adds.
-  float* const red = reinterpret_cast<float*>(smem);
-  auto slot = [&](int half, int nb, int mb) {
-    return red + (((half * 2 + wt) * NBW + nb) * MT + mb) * 256 + 4 * lane;
-  };
-#pragma unroll
-  for (int level = 2; level >= 1; level >>= 1) {
-    if (wk >= level && wk < 2 * level) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) *reinterpret_cast<f32x4*>(slot(wk - level, nb, mb)) = v[nb][mb];
-    }
-    __syncthreads();
-    if (wk < level) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) v[nb][mb] += *reinterpret_cast<const f32x4*>(slot(wk, nb, mb));
-    }
-    __syncthreads();
-  }
-  const int cb0 = 0;          // this wave holds every column block
-  const int64_t tw = t0 + 32 * wt;  // first token of this wave
-
-  if (p.n_k == 1) {
-    if (wk == 0) {
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MT; ++mb) {
-          const f32x4 o = v[nb][mb];
-          const int64_t e0 = pk_index(tw + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
-          uint32_t h0, l0, h1, l1;
-          split_hi_lo2(o[0], o[1], h0, l0);
-          split_hi_lo2(o[2], o[3], h1, l1);
-          *reinterpret_cast<u32x2*>(p.Phi + e0) = u32x2{h0, h1};
-          if (p.hi_only != 1) *reinterpret_cast<u32x2*>(p.Plo + e0) = p.hi_only ? u32x2{0u, 0u} : u32x2{l0, l1};
-        }
-    }
-    return;
-  }
-
-  // Column splits across workgroups (the splits of a token tile are
-  // consecutive logical ids, all on one XCD): each split stores its fp32
-  // partial with agent-coherent (sc1) stores; the last to arrive sums them
-  // in split order and writes P, with all of a thread's loads in flight at
-  // once.
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Ppart, (uint32_t)((int64_t)p.n_k * p.part_stride * 4));
-  if (wk == 0) {
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < MT; ++mb) {
-        const int64_t e0 = (int64_t)ksp * p.part_stride + pk_index(tw + 16 * mb + 4 * g, 16 * (cb0 + nb) + i, NB);
         store16_agent(rs, (uint32_t)(e0 * 4), __builtin_bit_cast(u32x4, v[nb][mb]));
       }
   }
@@ -2313,25 +1871,18 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   const int64_t T32 = (T + 31) / 32 * 32;
 
   // Projection.  Ranks above 64 with at least two 256-column blocks: the
-  // wide kernel (128-token tiles, one wave per SIMD).  Small r*k otherwise:
-  // the whole k range's signs fit in 64 KB of LDS.
+  // LDS-staged kernel (64-token tiles, two waves per SIMD; against the same
+  // tiling with X loaded in the MFMA operand's layout, 27B layers 70 -> 57
+  // (attention), 70 -> 59 (up), 191 -> 155 us (down), 7B down at r = 128
+  // 81 -> 71 us).  Small r*k otherwise: the whole k range's signs fit in
+  // 64 KB of LDS.
   pl.pwide = (pl.NB >= 8 && pl.ncb >= 2) ? 1 : 0;
   pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 8 ? 1 : 0;
-  pl.pnx = (pl.NB == 8 && env_int("LOGRA_PROJ_NX", 4) == 8) ? 8 : 4;
-  // Waves split by tokens at NB = 8 (7B down r = 128: 101 -> 79 us; 1.5B
-  // down: 58 -> 46); at NB = 16 the doubled sign expansion costs what the
-  // disjoint X loads save (27B layers within 3 %).
-  pl.pts = env_int("LOGRA_PROJ_TS", pl.NB == 8 ? 1 : 0) ? 1 : 0;
-  if (pl.pts) pl.pnx = 4;
-  // X staged through LDS (four rows x 256 bytes per load instruction): 27B
-  // layers 70 -> 57 (attention), 70 -> 60 (up), 191 -> 160 us (down); 7B
-  // down at r = 128 81 -> 71 us against the token-split kernel.
-  pl.plds = pl.pwide && env_int("LOGRA_PROJ_LDS", 1) ? 1 : 0;
   pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
   pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
   if (pl.pwide) {
-    // 128-token tiles; column splits across workgroups (powers of two, so
+    // 64-token tiles; column splits across workgroups (powers of two, so
     // that a tile's splits are consecutive ids on one XCD) until there is a
     // workgroup per CU, each split at least one round of two blocks.
     TT = 64;
@@ -2582,17 +2133,8 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
   if (pl.pwide) {
     const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
-    if (pl.plds) {
-      if (pl.NB == 16) hipLaunchKernelGGL((proj_lds_kernel<16>), dim3(grid), dim3(512), 0, s, p);
-      else if (pl.NB == 8) hipLaunchKernelGGL((proj_lds_kernel<8>), dim3(grid), dim3(512), 0, s, p);
-      else return false;
-      return true;
-    }
-    if (pl.pts && pl.NB == 16) hipLaunchKernelGGL((proj_wide2_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
-    else if (pl.pts && pl.NB == 8) hipLaunchKernelGGL((proj_wide2_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
-    else if (pl.NB == 16) hipLaunchKernelGGL((proj_wide_kernel<16, 4>), dim3(grid), dim3(512), 0, s, p);
-    else if (pl.NB == 8 && pl.pnx == 4) hipLaunchKernelGGL((proj_wide_kernel<8, 4>), dim3(grid), dim3(512), 0, s, p);
-    else if (pl.NB == 8) hipLaunchKernelGGL((proj_wide_kernel<8, 8>), dim3(grid), dim3(512), 0, s, p);
+    if (pl.NB == 16) hipLaunchKernelGGL((proj_lds_kernel<16>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 8) hipLaunchKernelGGL((proj_lds_kernel<8>), dim3(grid), dim3(512), 0, s, p);
     else return false;
     return true;
   }

@@ -214,10 +214,8 @@ PLAN_OVERRIDES = [
     {"LOGRA_CON_BANDS": 4},
     {"LOGRA_CON_BANDS": 8, "LOGRA_CON_GRID": 24},
     {"LOGRA_CON_BANDS": 4, "LOGRA_CON_GRID": 12},
-    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_TS": 0},
-    {"LOGRA_PROJ_NX": 8, "LOGRA_PROJ_NK": 2, "LOGRA_PROJ_TS": 0},
-    {"LOGRA_PROJ_TS": 0},
-    {"LOGRA_PROJ_TS": 1, "LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_NK": 2},
+    {"LOGRA_PROJ_NK": 4, "LOGRA_CON_TS": 3},
 ]
 
 
@@ -226,7 +224,7 @@ def _plan_id(e):
 
 
 # Knobs of proj_kernel's tiling (waves along k, token blocks per wave, waves
-# per workgroup); proj_wide_kernel has a fixed tiling.
+# per workgroup); the LDS-staged projection has a fixed tiling.
 PROJ_KERNEL_KNOBS = ("LOGRA_PROJ_MB", "LOGRA_PROJ_WK", "LOGRA_PROJ_NW")
 
 # Tilings reachable at ranks 129-256 (NB = 16): the eight-wave projection
@@ -240,8 +238,7 @@ R256_PLANS = [
     {"LOGRA_PROJ_NK": 2},
     {"LOGRA_PROJ_NK": 4},
     {"LOGRA_PROJ_NK": 3},
-    {"LOGRA_PROJ_TS": 1},
-    {"LOGRA_PROJ_TS": 1, "LOGRA_PROJ_NK": 4},
+    {"LOGRA_PROJ_NK": 8},
     {"LOGRA_PROJ_WIDE": 0},
     {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 4},
     {"LOGRA_PROJ_WIDE": 0, "LOGRA_PROJ_NW": 8, "LOGRA_PROJ_MB": 2, "LOGRA_PROJ_WK": 2, "LOGRA_PROJ_NK": 2},
@@ -292,9 +289,9 @@ def test_sketch_launch_plans(r, env, monkeypatch):
     if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
         env = dict(env, LOGRA_PROJ_SMALL=0)  # rank 256 always takes the round-based projection
     if r >= 128 and any(k_ in env for k_ in PROJ_KERNEL_KNOBS):
-        # ranks above 64 with two or more 256-column blocks take
-        # proj_wide_kernel, whose tiling these knobs do not set: run them on
-        # proj_kernel
+        # ranks above 64 with two or more 256-column blocks take the
+        # LDS-staged projection, whose tiling these knobs do not set: run
+        # them on proj_kernel
         env = dict(env, LOGRA_PROJ_WIDE=0)
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, str(v_))

@@ -193,9 +193,9 @@ def test_split_launch_plans(r, env, monkeypatch):
     if r == 256 and env.get("LOGRA_PROJ_SMALL", 1):
         env = dict(env, LOGRA_PROJ_SMALL=0)
     if r >= 128 and any(k_ in env for k_ in PROJ_KERNEL_KNOBS):
-        # ranks above 64 with two or more 256-column blocks take
-        # proj_wide_kernel, whose tiling these knobs do not set: run them on
-        # proj_kernel
+        # ranks above 64 with two or more 256-column blocks take the
+        # LDS-staged projection, whose tiling these knobs do not set: run
+        # them on proj_kernel
         env = dict(env, LOGRA_PROJ_WIDE=0)
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, str(v_))
