@@ -610,8 +610,9 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "sketch_accumulate call: projection kernel, contraction kernel, and the sum of the "
-                      "contraction's token-split partial tiles (kernel names per layer in the committed trace summary)",
+            "kernel": "sketch_accumulate call: the call's sign table, the projection kernel, the contraction kernel, "
+                      "and (above three token splits) the sum of the contraction's partial tiles (kernel names per "
+                      "layer in the committed trace summary)",
             "bound": "hbm",
             "achieved": sk_gbs,
             "peak": HBM_PEAK_GBS,
