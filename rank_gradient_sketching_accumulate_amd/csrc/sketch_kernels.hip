@@ -533,19 +533,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int sc = threadIdx.x & 15, srow = threadIdx.x >> 4;  // chunk, row (and row + 32)
   const int64_t xbytes = p.T * p.ldx * 2;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.X, (uint32_t)xbytes);
-  const int64_t rowoff0 = (t0 + srow) * p.ldx * 2, rowoff1 = (t0 + srow + 32) * p.ldx * 2;
-  const int64_t lim = min(p.k, (int64_t)cbe * 256);  // first column that stages as zero
-  auto slab_col = [&](int u) { return (int64_t)(cbb + WK * (u >> 3)) * 256 + 128 * (u & 7) + 8 * sc; };
+  // Byte offsets fit 32 bits: the planner keeps (Tpad + 32) * ldx * 2 below
+  // 2^32 - 4096, and a slab column never passes ldx + 2304.
+  const uint32_t rowoff0 = (uint32_t)((t0 + srow) * p.ldx * 2), rowoff1 = (uint32_t)((t0 + srow + 32) * p.ldx * 2);
+  const int lim = (int)min(p.k, (int64_t)cbe * 256);  // first column that stages as zero
+  auto slab_base = [&](int u) { return (cbb + WK * (u >> 3)) * 256 + 128 * (u & 7); };  // wave-uniform
   auto xload = [&](u32x4 (&v)[2], int u) {
-    const int64_t c2 = slab_col(u) * 2;
-    const int64_t o0 = rowoff0 + c2, o1 = rowoff1 + c2;  // past the range: clamped, reads zero
-    v[0] = buf_load16(rx, (uint32_t)(o0 < 0xFFFFFFF0ll ? o0 : 0xFFFFFFF0ll));
-    v[1] = buf_load16(rx, (uint32_t)(o1 < 0xFFFFFFF0ll ? o1 : 0xFFFFFFF0ll));
+    const uint32_t c2 = (uint32_t)(slab_base(u) + 8 * sc) * 2u;
+    v[0] = buf_load16(rx, rowoff0 + c2);
+    v[1] = buf_load16(rx, rowoff1 + c2);
   };
   auto xstore = [&](u32x4 (&v)[2], int u) {
-    const int64_t col = slab_col(u);
-    if (col + 8 > lim) {
-      const int64_t nv = lim - col;
+    const int sbase = slab_base(u);
+    if (sbase + 128 > lim) {  // a slab that reaches past k or past the split's blocks (uniform test)
+      const int nv = lim - (sbase + 8 * sc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t m = (2 * q < nv ? 0x0000ffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
