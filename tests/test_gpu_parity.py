@@ -325,6 +325,29 @@ def test_sketch_rank256_plans(T, k, d, r, env, monkeypatch):
     assert_sketch_close(got, ref)
 
 
+LDS_PROJ_EDGES = [(1, 264, 8, 128), (17, 520, 33, 65), (63, 1029, 40, 256), (65, 777, 20, 200),
+                  (130, 264, 7, 256), (300, 2056, 50, 96), (64, 1031, 9, 129)]
+
+
+@pytest.mark.parametrize("T,k,d,r", LDS_PROJ_EDGES)
+@pytest.mark.parametrize("env", [{}, {"LOGRA_PROJ_NK": 2}, {"LOGRA_PROJ_NK": 8}], ids=_plan_id)
+def test_sketch_lds_projection_edges(T, k, d, r, env, monkeypatch):
+    """The LDS-staged projection (ranks above 64, k > 256) at its edges:
+    token tiles of 1 to 130 tokens (rows past T staged as zero), k with a
+    ragged last 256-column block and k % 8 != 0 (the slab's boundary chunk
+    masked element by element), r = 129 padded to 256 columns, and column splits
+    (with NK = 8 on small k most splits hold no block at all)."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, str(v_))
+    _say("lds projection edges", T, k, d, r, env)
+    seed = 900 + T + r
+    X, dY = _ragged_inputs(T, k, d, 300 + T)
+    S0 = wl.random_tensor((d, r), 7 + T, device=DEV)
+    S = S0.clone()
+    lg.sketch_accumulate(X, dY, seed, r, S)
+    assert_sketch_close(f64(S), _oracle_sketch(S0, [X], [dY], seed, r, k))
+
+
 @pytest.mark.parametrize("T,k,d,r", [(700, 1300, 300, 16), (4096, 1536, 1536, 64), (1000, 700, 900, 128),
                                      (2048, 3584, 3584, 256), (33, 264, 17, 5)])
 def test_sketch_deterministic_mode(T, k, d, r):
