@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 CSRC = os.path.join(ROOT, "rank_gradient_sketching_accumulate_amd", "csrc")
 KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
 MALL_BYTES = 256 * 2**20
@@ -49,6 +50,17 @@ def kernel_source_sha() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def padded_rank(r):
+    """Columns of P the kernels compute: 16-column blocks rounded up to a power
+    of two, ranks above 256 as a 256-column half plus the rest."""
+    def pow2_cols(n):
+        b = 1
+        while 16 * b < n:
+            b *= 2
+        return 16 * b
+    return pow2_cols(r) if r <= 256 else 256 + pow2_cols(r - 256)
 
 
 def sketch_bytes(T, k, d, r):
@@ -554,12 +566,23 @@ def main():
                                                   r, S), n_calls)
         del caches
         pb, cb = split_bytes(T, k, d, r)
+        rpad = padded_rank(r)
+        nplanes = 2 if args.precision == "bf16x2" else 1
         extras["split"] = {
             "what": "logra_project (forward, X -> cache: the projection kernel) and logra_contract (backward, dY "
                     "and cache -> S: the contraction kernels), per call",
             "project_us": t_proj * 1e6, "project_GBps": pb / t_proj / 1e9, "project_frac": pb / t_proj / 1e9 / HBM_PEAK_GBS,
             "contract_us": t_con * 1e6, "contract_GBps": cb / t_con / 1e9,
             "contract_frac": cb / t_con / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": [pb, cb],
+            # The contraction's MFMA rate: 2 T d R flops per plane of P (R the
+            # padded rank), two planes in the hi/lo mode, against the dense
+            # bf16 peak.
+            "contract_mfma": {
+                "flops": 2 * T * d * rpad * nplanes, "planes": nplanes,
+                "achieved_tflops": 2 * T * d * rpad * nplanes / t_con / 1e12,
+                "peak_tflops": BF16_PEAK_TFLOPS,
+                "frac": 2 * T * d * rpad * nplanes / t_con / 1e12 / BF16_PEAK_TFLOPS,
+            },
         }
         t_ra, h_ra = rowadam_time(torch, lg, stream, S, args.steps)
         extras["rowadam"] = {
