@@ -1285,18 +1285,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
 // the other waits on its loads or its barrier; the two halves of a tile are
 // consecutive logical ids (one XCD), so the second read of the tile's dY
 // rows comes from L2.
-template <int DP>
+// NB = 8 (ranks 65-128): the same workgroup holds all of P's columns (one
+// "half" per tile), two workgroups per CU from different (tile, split) pairs.
+template <int DP, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void contract_half_kernel(ContractParams p) {
-  constexpr int NB = 16;
+  static_assert(NB == 16 || NB == 8, "two halves of 128 columns, or one");
   constexpr int NBW = 8;                 // column blocks per wave (half of the tile)
+  constexpr int NHALF = NB / NBW;
   constexpr int PVH = NBW * 64;          // u32x4 words per plane and step for the half
   constexpr int PER = 2 * PVH / 256;     // words each thread moves per step
   constexpr int PH = PER / 2;
   static_assert(PH * 256 == PVH, "whole planes per step");
   __shared__ u32x4 pt[2][2 * PVH];
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
-  const int half = lin & 1;
-  const int rest = lin >> 1;
+  const int half = NHALF == 2 ? (lin & 1) : 0;
+  const int rest = NHALF == 2 ? (lin >> 1) : lin;
   const int dt = rest / p.n_ts;
   const int ts = rest - dt * p.n_ts;
   if (dt >= p.n_dt) return;
@@ -2000,9 +2003,15 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     const int wide = (!det && pl.NB == 16) ? env_int("LOGRA_CON_WIDE", (hi_only && (tall || use_big)) ? 1 : 0) : 0;
     // Otherwise the 256 x 256 tiles as two 256 x 128 workgroups per CU
     // (27B up layer 336 -> 314 us, attention 110 -> 105, 7B up 185 -> 174).
-    const int halfk = (!det && !wide && pl.NB == 16 && (tall || use_big)) ? env_int("LOGRA_CON_HALF", 1) : 0;
+    // At NB = 8 one such workgroup holds the whole rank: used where the
+    // 512 x 128 tiles would be too few for a round (1.5B up layer, r = 128:
+    // 78.8 -> 67.1 us); on tall S (7B up) the 512 x 128 tiles stay ahead
+    // (105.6 against 111.1 us).
+    const int halfk = (!det && !wide && (tall || use_big))
+                          ? env_int("LOGRA_CON_HALF", (pl.NB == 16 || !tall) ? 1 : 0)
+                          : 0;
     if (halfk) {
-      pl.cvar = 7;  // contract_half_kernel: 256 x 128 tiles, two workgroups per CU
+      pl.cvar = 7;  // contract_half_kernel: 256 x 128 workgroups, two per CU
       BD = 256;
     } else if (wide) {
       pl.cvar = 6;
@@ -2037,8 +2046,9 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     n_ts = 256 / pl.n_dt;
     if (n_ts < 1) n_ts = 1;
   } else if (pl.cvar == 7) {
-    // One round of two workgroups (the two column halves) per CU at most.
-    n_ts = 512 / (2 * pl.n_dt);
+    // One round of two workgroups per CU at most (at NB = 16 the two column
+    // halves of a tile).
+    n_ts = 512 / ((pl.NB / 8) * pl.n_dt);
     if (n_ts < 1) n_ts = 1;
     if (n_ts > 8 && pl.few_ts) n_ts = 8;
   } else if (pl.cvar >= 3 && pl.few_ts) {
@@ -2211,8 +2221,14 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
       else hipLaunchKernelGGL((contract_big_kernel<16, 2, 1>), dim3(grid), dim3(512), 0, s, p);
       return true;
     case 7:
-      hipLaunchKernelGGL((contract_half_kernel<2>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts * 2, 8)),
-                         dim3(256), 0, s, p);
+      if (pl.NB == 16)
+        hipLaunchKernelGGL((contract_half_kernel<2, 16>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts * 2, 8)),
+                           dim3(256), 0, s, p);
+      else if (pl.NB == 8)
+        hipLaunchKernelGGL((contract_half_kernel<2, 8>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts, 8)),
+                           dim3(256), 0, s, p);
+      else
+        return false;
       return true;
     case 6:
       if (pl.cwide == 2) {
