@@ -633,7 +633,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "sketch_accumulate call: the call's sign table, the projection kernel, the contraction kernel, "
+            "kernel": "sketch_accumulate call: the projection kernel (signs drawn in LDS), the contraction kernel, "
                       "and (above three token splits) the sum of the contraction's partial tiles (kernel names per "
                       "layer in the committed trace summary)",
             "bound": "hbm",

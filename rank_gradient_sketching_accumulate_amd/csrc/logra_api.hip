@@ -276,15 +276,6 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
     }
   }
   pp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
-  if (pl.pwide) {
-    // The wide kernels copy their signs from a table drawn once per call.
-    uint32_t* table = reinterpret_cast<uint32_t*>(base + pl.off_signs);
-    sign_table_launch(seed, row0, pl.NB, pl.sign_blocks, table, stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "sign table launch");
-    pp.signs = table;
-    pp.sign_blocks = pl.sign_blocks;
-  }
   if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "projection launch");

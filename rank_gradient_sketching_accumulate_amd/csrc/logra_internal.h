@@ -33,11 +33,6 @@ struct ProjParams {
   const uint16_t* Ahi;
   const uint16_t* Alo;
   int64_t kpad, Tw;
-  // Rademacher sign table (the wide kernels): for each 256-column block and
-  // each of the 16*NB rows, the row's 256 sign bits as 8 dwords plus one pad
-  // dword, block-major; sign_blocks blocks from column block 0.
-  const uint32_t* signs;
-  int sign_blocks;
 };
 
 struct ContractParams {
@@ -78,8 +73,7 @@ struct SketchPlan {
   int cbands;             // token bands of that split (1; 4 = one per XCD pair; 8 = one per XCD)
   int bigdp;              // contract_big: steps between requesting a step's operands and using them
   int64_t n_counters;     // split counters the projection needs (a separate zeroed region)
-  size_t off_phi, off_plo, off_part, off_signs, off_cpart, total;
-  int sign_blocks;        // 256-column blocks in the sign table (wide projection only)
+  size_t off_phi, off_plo, off_part, off_cpart, total;
 };
 
 // det: bitwise-reproducible contraction (one workgroup per row tile of S,
@@ -96,11 +90,6 @@ size_t projection_cache_bytes(int64_t T, int r);
 // the caller's cache), keeping the projection's column-split partials and/or
 // the contraction's token-split partials.
 void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part);
-// Bytes of the wide projection's sign table: 9 dwords per row and block.
-size_t sign_table_bytes(int NB, int blocks);
-// Fills the sign table: row i (of 16*NB) of block b holds the signs of sign
-// row row0 + i over columns 256 b .. 256 b + 255.
-void sign_table_launch(uint64_t seed, int row0, int NB, int blocks, uint32_t* table, hipStream_t s);
 bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s);
 bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t s);
 // S += sum over token splits of the stored partial tiles (use_part plans).

@@ -402,63 +402,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ===========================================================================
-// Rademacher sign table for the wide projections.  Every token tile of a call
-// multiplies by the same 16*NB x k signs; drawing them once per call (one
-// Philox4x64-10 block per row and 256-column block) instead of once per
-// token tile takes the 64-bit multiplies out of the projection's loop, where
-// they cost about as many VALU cycles as the loop has MFMA cycles.  Row i of
-// block b sits at dwords 9 (b * 16 NB + i) .. + 7 (the ninth dword pads the
-// row so that the sixteen rows an LDS read touches fall in distinct banks);
-// the kernels copy a round's four blocks into LDS as one contiguous run.
-// ===========================================================================
-constexpr int kSignRowDw = 9;
-
-size_t sign_table_bytes(int NB, int blocks) { return (size_t)blocks * 16 * NB * kSignRowDw * 4; }
-
-__global__ __launch_bounds__(256) void sign_table_kernel(uint64_t seed, int row0, int RP, int n, uint32_t* table) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= n) return;
-  const int b = idx / RP, row = idx - b * RP;
-  uint32_t w[8];
-  philox_sign_block(seed, (uint32_t)(row0 + row), (uint32_t)b, w);
-  uint32_t* dst = table + (size_t)idx * kSignRowDw;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = w[e];
-  dst[8] = 0u;
-}
-
-void sign_table_launch(uint64_t seed, int row0, int NB, int blocks, uint32_t* table, hipStream_t s) {
-  const int n = blocks * 16 * NB;
-  if (n <= 0) return;
-  hipLaunchKernelGGL(sign_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, seed, row0, 16 * NB, n, table);
-}
-
-// One round's sign rows (WK consecutive blocks from the table) through
-// registers into an LDS sign buffer of the same layout: 512 threads, u32x4
-// words.  The loads are issued whole-round ahead and stored before the
-// round's closing barrier; a word index past the run reloads the run's last
-// word and is not stored.
-template <int RP, int WK>
-struct SignRound {
-  static constexpr int N16 = WK * RP * kSignRowDw / 4;
-  static constexpr int PER = (N16 + 511) / 512;
-  static_assert(N16 * 4 == WK * RP * kSignRowDw, "whole u32x4 words per round");
-  u32x4 v[PER];
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rt, int cb) {
-    const uint32_t base = (uint32_t)cb * (uint32_t)(RP * kSignRowDw / 4);
-#pragma unroll
-    for (int q = 0; q < PER; ++q) v[q] = buf_load16(rt, (base + min((int)threadIdx.x + 512 * q, N16 - 1)) * 16u);
-  }
-  __device__ __forceinline__ void store(uint32_t* buf) const {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int w = threadIdx.x + 512 * q;
-      if (q + 1 < PER || w < N16) reinterpret_cast<u32x4*>(buf)[w] = v[q];
-    }
-  }
-};
-
-// ===========================================================================
 // Projection for ranks above 64 (NB = 8 or 16), X staged through LDS.
 // Eight waves, two per SIMD.  Wave (wn, wk) keeps the workgroup's 64 tokens
 // x one half of P's 16*NB columns in accumulators (8*NB*2 registers: 128 at
@@ -476,10 +419,10 @@ struct SignRound {
 // the sixteen rows of an MFMA operand read fall in distinct banks.  Slab
 // u + 2 is loaded into registers during step u and slab u + 1 is stored into
 // the other LDS buffer at the end of step u, before the step's barrier.
-// Each round copies the signs of the next round's four blocks from the
-// call's sign table into registers and, at its end, into the other LDS sign
-// buffer.  After the last round the four wave columns are summed through
-// LDS in two halving rounds, and the wk = 0 waves write P (or, with column
+// Each round first draws the signs of the next round's four blocks into the
+// other LDS sign buffer (two Philox blocks per thread at NB = 16, one at
+// NB = 8); the signs never leave registers and LDS.  After the last round
+// the four wave columns are summed through LDS in two halving rounds, and the wk = 0 waves write P (or, with column
 // splits across workgroups, their fp32 partial; the last split to arrive
 // sums the partials).
 // ===========================================================================
@@ -496,7 +439,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int RED = 2 * 2 * NBW * MT * 256;  // floats parked in the first halving round
   constexpr int MAIN = 2 * SBUF + 2 * XBUF;
   constexpr int LDSW = (MAIN > RED) ? MAIN : RED;
-  static_assert(SROW == kSignRowDw, "the sign table's row layout");
   static_assert((2 * SBUF) % 4 == 0, "X slabs on 16-byte boundaries");
   __shared__ __attribute__((aligned(16))) uint32_t smem[LDSW];
   __shared__ int s_last;
@@ -521,11 +463,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Signs of round j (rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1) come
-  // from the call's sign table (blocks past the range too: the table covers
-  // every block a split may name, and their X is zeroed).
-  const __amdgpu_buffer_rsrc_t rt = make_rsrc(p.signs, (uint32_t)p.sign_blocks * (RP * kSignRowDw * 4));
-  SignRound<RP, WK> sr;
+  // Signs of round j: rows 0 .. RP-1 of blocks cbb + WK*j .. + WK-1, one
+  // Philox block (256 columns of one row) per thread and pass, written to
+  // LDS row (wkk * RP + row) with the row stride SROW (the ninth dword only
+  // spreads the banks and is never read).  Blocks past k are drawn too;
+  // their X is zeroed.
+  constexpr int NGEN = RP * WK / 512;
+  auto gen = [&](int j, int buf) {
+#pragma unroll 1
+    for (int q = 0; q < NGEN; ++q) {
+      const int b = threadIdx.x + 512 * q;
+      const int row = b % RP, wkk = b / RP;
+      uint32_t w[8];
+      philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
+      uint32_t* dst = smem + buf * SBUF + (wkk * RP + row) * SROW;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = w[e];
+    }
+  };
 
   // X slabs.  Rows past T read as zero (buffer range); columns past k or
   // past the split's blocks are zeroed when staged.  Loads are unconditional
@@ -560,10 +515,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   u32x4 xv[2][2];
-  sr.load(rt, cbb);
   xload(xv[0], 0);
   xload(xv[1], 1);
-  sr.store(smem);
+  gen(0, 0);
   xstore(xv[0], 0);
   __syncthreads();
 
@@ -571,7 +525,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int xoff = ((4 * wk + g) ^ i) * 4;  // this lane's chunk slot in its rows
   for (int j = 0; j < nrounds; ++j) {
     const int buf = j & 1;
-    sr.load(rt, cbb + WK * min(j + 1, nrounds - 1));  // the next round (the last: itself again)
+    if (j + 1 < nrounds) gen(j + 1, buf ^ 1);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int u = 8 * j + s;
@@ -590,7 +544,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
         mfma4_b(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], a[0], a[1], a[2], a[3], bsg);
       }
       xstore(xv[(s + 1) & 1], u + 1);
-      if (s == 7) sr.store(smem + (buf ^ 1) * SBUF);
       __syncthreads();
     }
   }
@@ -1855,8 +1808,6 @@ void scratch_layout(SketchPlan& pl, int64_t d, bool proj_part, bool con_part) {
   pl.off_phi = pl.off_plo = 0;
   pl.off_part = off;
   if (proj_part && pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
-  pl.off_signs = off;
-  if (proj_part) off += align_up(sign_table_bytes(pl.NB, pl.sign_blocks), 256);
   pl.off_cpart = off;
   if (con_part && pl.use_part) off += align_up((size_t)pl.n_ts * d * RP * 4, 256);
   pl.total = off;
@@ -1904,8 +1855,6 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // the grid must keep each tile's splits on one XCD: n_k a power of two
     // dividing the per-XCD share (the launch rounds the grid up to 8 * n_k)
     while (pl.n_k & (pl.n_k - 1)) ++pl.n_k;
-    // Every block a split may name, past k included (those have zeroed X).
-    pl.sign_blocks = pl.n_k * pl.cbs_per;
   } else if (pl.small_proj) {
     // More tokens per workgroup amortise the signs; keep >= 256 workgroups.
     int MBW = 4;
@@ -2121,10 +2070,6 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   off += align_up((size_t)pl.Tpad * RP * 2, 256);
   pl.off_part = off;
   if (pl.n_k > 1) off += align_up((size_t)pl.n_k * pl.Tpad * RP * 4, 256);
-  // The sign table precedes the contraction's partial tiles, so that callers
-  // that keep no partial tiles may place their own data from off_cpart on.
-  pl.off_signs = off;
-  off += align_up(sign_table_bytes(pl.NB, pl.sign_blocks), 256);
   // Token splits of the large-rank tilings store partial tiles (a plain,
   // coalesced stream) that one small kernel sums into S: L2 retires fp32
   // atomic adds at about one element per channel and clock.  The half-tile
