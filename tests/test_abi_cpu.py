@@ -440,3 +440,20 @@ def test_rowadam_merge_validation(lib):
     assert call(ldw=500) == ERR_SHAPE
     assert call(W=FAKE * 64 + 64) == ERR_ALIAS  # W over S
     assert call(d=0) == OK
+
+
+def test_workspace_holds_no_signs(lib):
+    # The Rademacher signs are regenerated from the seed inside the kernels
+    # and never kept in device memory [LoGRA §2.2, "Memory and
+    # synchronization"], so no part of the scratch grows with the signs' r x k
+    # bits.  Once k is long enough that the projection's column splits no
+    # longer change (at 16384 tokens there are none), the scratch is the same
+    # for every k; a sign table would add r * k / 8 bytes (2 MiB at r = 256,
+    # k = 65536).
+    for T, d in ((16384, 17408), (16384, 5120), (8192, 3584), (4096, 1536)):
+        for r in (64, 128, 200, 256, 512):
+            sizes = {lib.logra_workspace_bytes(T, d, k, r) for k in (17408, 32768, 65536)}
+            assert len(sizes) == 1, (T, d, r, sizes)
+    for r in (64, 128, 256):
+        sizes = {lib.logra_workspace_bytes(16384, 17408, k, r) for k in (1024, 5120, 17408, 65536)}
+        assert len(sizes) == 1, (r, sizes)
