@@ -1956,7 +1956,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // 512 x 128 tiles would be too few for a round (1.5B up layer, r = 128:
     // 78.8 -> 67.1 us); on tall S (7B up) the 512 x 128 tiles stay ahead
     // (105.6 against 111.1 us).
-    const int halfk = (!det && !wide && (tall || use_big))
+    // Above rank 128 the half tiles also beat the token-lane tiles on shorter
+    // S (3584-row layers at 8192 tokens: 58-66 -> 49 us).
+    const bool half16 = pl.NB == 16 && ((d + bd8 - 1) / bd8) * (nks / 16) >= 128;
+    const int halfk = (!det && !wide && (tall || use_big || half16))
                           ? env_int("LOGRA_CON_HALF", (pl.NB == 16 || !tall) ? 1 : 0)
                           : 0;
     if (halfk) {
@@ -2000,6 +2003,10 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     n_ts = 512 / ((pl.NB / 8) * pl.n_dt);
     if (n_ts < 1) n_ts = 1;
     if (n_ts > 8 && pl.few_ts) n_ts = 8;
+    // At NB = 16, at least 32 steps per workgroup: shorter splits spend more
+    // on the prologue and the partial tiles than the fuller grid gains
+    // (3584-row layers at 8192 tokens: 16 splits 53 us, 8 splits 49 us).
+    if (pl.NB == 16 && n_ts > nks / 32) n_ts = nks / 32 > 1 ? nks / 32 : 1;
   } else if (pl.cvar >= 3 && pl.few_ts) {
     n_ts = 256 / pl.n_dt;  // one round of 256 eight-wave workgroups at most
     if (n_ts < 1) n_ts = 1;
