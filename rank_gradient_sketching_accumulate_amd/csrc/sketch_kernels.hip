@@ -1956,10 +1956,12 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     // 512 x 128 tiles would be too few for a round (1.5B up layer, r = 128:
     // 78.8 -> 67.1 us); on tall S (7B up) the 512 x 128 tiles stay ahead
     // (105.6 against 111.1 us).
-    // Above rank 128 the half tiles also beat the token-lane tiles on shorter
-    // S (3584-row layers at 8192 tokens: 58-66 -> 49 us).
-    const bool half16 = pl.NB == 16 && ((d + bd8 - 1) / bd8) * (nks / 16) >= 128;
-    const int halfk = (!det && !wide && (tall || use_big || half16))
+    // The half tiles also beat the token-lane tiles on shorter S: 3584-row
+    // layers at 8192 tokens, 58-66 -> 49 us above rank 128 and 37 -> 32.5 us
+    // at rank 128 (at 1536 rows, 20 -> 26 us: not taken there).
+    const int64_t span = ((d + bd8 - 1) / bd8) * (nks / 16);
+    const bool half_short = pl.NB == 16 ? span >= 128 : span >= 96;
+    const int halfk = (!det && !wide && (tall || use_big || half_short))
                           ? env_int("LOGRA_CON_HALF", (pl.NB == 16 || !tall) ? 1 : 0)
                           : 0;
     if (halfk) {
