@@ -325,6 +325,23 @@ def test_sketch_rank256_plans(T, k, d, r, env, monkeypatch):
     assert_sketch_close(got, ref)
 
 
+@pytest.mark.parametrize("T,k,d,r", [(8192, 520, 2125, 256), (8192 - 37, 264, 2125, 200), (8192, 264, 3100, 128)])
+def test_sketch_half_tiles_on_shorter_s(T, k, d, r):
+    """The default plan at these sizes contracts with the half tiles (two
+    256 x 128 workgroups per CU) on S of a few thousand rows: eight token
+    splits of at least 32 steps above rank 128, sixteen at rank 128, partial
+    tiles summed by the reduction kernel, a ragged last row tile, and a
+    ragged last token step in the second case."""
+    _say("half tiles", T, k, d, r)
+    X, dY = _ragged_inputs(T, k, d, 9090 + r)
+    S0 = wl.random_tensor((d, r), 9191, device=DEV)
+    S = S0.clone()
+    lg.sketch_accumulate(X, dY, 77, r, S)
+    rows = np.arange(0, d, 11)
+    ref = _oracle_sketch(S0, [X], [dY], 77, r, k, rows=rows)
+    assert_sketch_close(f64(S)[rows], ref)
+
+
 LDS_PROJ_EDGES = [(1, 264, 8, 128), (17, 520, 33, 65), (63, 1029, 40, 256), (65, 777, 20, 200),
                   (130, 264, 7, 256), (300, 2056, 50, 96), (64, 1031, 9, 129)]
 
