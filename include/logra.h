@@ -18,7 +18,10 @@
  *   - Every pointer is a DEVICE pointer on the current HIP device, owned by the
  *     caller; the library keeps no reference after the call returns.
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
- *     without synchronising.  Scalar arguments are captured by value.
+ *     without synchronising.  Scalar arguments are captured by value.  The
+ *     stream must belong to the current device: the calls that take library
+ *     scratch (allocated on the current device) return LOGRA_ERR_RANGE for a
+ *     stream of another device.
  *   - Validation runs before anything is enqueued; on any error nothing is
  *     written and a nonzero status is returned.  logra_last_error() then gives
  *     a thread-local description.  No C++ exception crosses this boundary.
@@ -56,7 +59,7 @@ typedef enum {
   LOGRA_ERR_NULL = 1,   /* a required pointer is NULL                            */
   LOGRA_ERR_SHAPE = 2,  /* negative size, ld < columns, or sizes that disagree   */
   LOGRA_ERR_ALIGN = 3,  /* base pointer or ld breaks the stated alignment        */
-  LOGRA_ERR_RANGE = 4,  /* r, step, beta2 or eps_rel out of range                */
+  LOGRA_ERR_RANGE = 4,  /* r, step, beta2 or eps_rel out of range; stream of another device */
   LOGRA_ERR_ALIAS = 5,  /* an output overlaps an input it must not overlap       */
   LOGRA_ERR_HIP = 6,    /* a HIP runtime call or kernel launch failed            */
   LOGRA_ERR_NOMEM = 7   /* the library could not obtain its scratch memory       */

@@ -301,6 +301,45 @@ def _need(t, dtype, name, ndim=2):
         raise ValueError(f"{name} must be contiguous")
 
 
+class _OnDevice:
+    """Makes the device of the call's device tensors current while the C ABI
+    runs (it takes pointers on the current device and allocates its scratch
+    there) and refuses device tensors on different devices.  Host tensors and
+    None are ignored."""
+
+    __slots__ = ("dev", "prev")
+
+    def __init__(self, *tensors):
+        dev = None
+        for t in tensors:
+            if t is None or not t.is_cuda:
+                continue
+            di = t.get_device()
+            if dev is None:
+                dev = di
+            elif di != dev:
+                raise ValueError("the device tensors of one call must be on the same device")
+        self.dev = dev
+        self.prev = None
+
+    def __enter__(self):
+        if self.dev is not None:
+            import torch
+
+            cur = torch._C._cuda_getDevice()
+            if cur != self.dev:
+                self.prev = cur
+                torch._C._cuda_setDevice(self.dev)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            import torch
+
+            torch._C._cuda_setDevice(self.prev)
+        return False
+
+
 def _ld(t) -> int:
     return int(t.stride(0)) if t.size(0) > 1 else max(int(t.stride(0)), int(t.size(1)))
 
@@ -325,12 +364,13 @@ def sketch_accumulate(X, dY, seed: int, r: int, S, noalloc: bool = False):
     d = dY.size(1)
     if tuple(S.shape) != (d, r):
         raise ValueError(f"S must be ({d}, {r}), got {tuple(S.shape)}")
-    _check(
-        fn(
-            X.data_ptr(), _ld(X), dY.data_ptr(), _ld(dY), T, k, d,
-            ctypes.c_uint64(seed & (2**64 - 1)), r, S.data_ptr(), _ld(S), _stream_handle(S),
+    with _OnDevice(X, dY, S):
+        _check(
+            fn(
+                X.data_ptr(), _ld(X), dY.data_ptr(), _ld(dY), T, k, d,
+                ctypes.c_uint64(seed & (2**64 - 1)), r, S.data_ptr(), _ld(S), _stream_handle(S),
+            )
         )
-    )
     return S
 
 
@@ -355,8 +395,9 @@ def basis_normals(seed: int, r: int, k: int, device="cuda"):
     import torch
 
     out = torch.empty((r, k), dtype=torch.float32, device=device)
-    _check(load_library().logra_basis_normals(ctypes.c_uint64(seed & (2**64 - 1)), r, k,
-                                              out.data_ptr() if out.numel() else None, _stream_handle(out)))
+    with _OnDevice(out):
+        _check(load_library().logra_basis_normals(ctypes.c_uint64(seed & (2**64 - 1)), r, k,
+                                                  out.data_ptr() if out.numel() else None, _stream_handle(out)))
     return out
 
 
@@ -392,12 +433,13 @@ def project(X, seed: int, r: int, P=None):
     if P is None:
         P = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
     _need(P, torch.uint8, "P", ndim=1)
-    _check(
-        lib.logra_project(
-            X.data_ptr() if X.numel() else None, _ld(X) if k else 0, T, k,
-            ctypes.c_uint64(seed & (2**64 - 1)), r, P.data_ptr(), P.numel(), _stream_handle(P),
+    with _OnDevice(X, P):
+        _check(
+            lib.logra_project(
+                X.data_ptr() if X.numel() else None, _ld(X) if k else 0, T, k,
+                ctypes.c_uint64(seed & (2**64 - 1)), r, P.data_ptr(), P.numel(), _stream_handle(P),
+            )
         )
-    )
     return P
 
 
@@ -416,12 +458,13 @@ def contract(dY, P, r: int, S):
     T, d = dY.shape
     if tuple(S.shape) != (d, r):
         raise ValueError(f"S must be ({d}, {r}), got {tuple(S.shape)}")
-    _check(
-        lib.logra_contract(
-            dY.data_ptr(), _ld(dY), T, d, P.data_ptr(), P.numel(), r, S.data_ptr(), _ld(S),
-            _stream_handle(S),
+    with _OnDevice(dY, P, S):
+        _check(
+            lib.logra_contract(
+                dY.data_ptr(), _ld(dY), T, d, P.data_ptr(), P.numel(), r, S.data_ptr(), _ld(S),
+                _stream_handle(S),
+            )
         )
-    )
     return S
 
 
@@ -438,12 +481,13 @@ def merge_update(W, U, seed: int, r: int, scale: float):
     d, k = W.shape
     if tuple(U.shape) != (d, r):
         raise ValueError(f"U must be ({d}, {r}), got {tuple(U.shape)}")
-    _check(
-        lib.logra_merge_update(
-            W.data_ptr(), _ld(W), U.data_ptr(), _ld(U), d, k,
-            ctypes.c_uint64(seed & (2**64 - 1)), r, float(scale), _stream_handle(W),
+    with _OnDevice(W, U):
+        _check(
+            lib.logra_merge_update(
+                W.data_ptr(), _ld(W), U.data_ptr(), _ld(U), d, k,
+                ctypes.c_uint64(seed & (2**64 - 1)), r, float(scale), _stream_handle(W),
+            )
         )
-    )
     return W
 
 
@@ -465,7 +509,8 @@ def merge_update_grouped(items, r: int):
         arr[j] = MergeItem(W.data_ptr(), _ld(W), U.data_ptr(), _ld(U), d, k, seed & (2**64 - 1), float(scale))
         if stream is None:
             stream = _stream_handle(W)
-    _check(lib.logra_merge_update_grouped(arr, len(items), r, stream))
+    with _OnDevice(*[t for it in items for t in it[:2]]):
+        _check(lib.logra_merge_update_grouped(arr, len(items), r, stream))
 
 
 def _factor_items(factors, r: int):
@@ -502,7 +547,8 @@ def payload_pack(factors, r: int, out=None):
     dev = factors[0][0].device
     if out is None:
         out = torch.empty(n, dtype=torch.uint8, device=dev)
-    _check(lib.logra_payload_pack(arr, len(factors), r, out.data_ptr(), out.numel(), _stream_handle(out)))
+    with _OnDevice(out):
+        _check(lib.logra_payload_pack(arr, len(factors), r, out.data_ptr(), out.numel(), _stream_handle(out)))
     return out
 
 
@@ -538,8 +584,9 @@ def payload_apply(payload, header, entries, Ws):
         _need(W, torch.bfloat16, "W")
         ptrs[j] = W.data_ptr() if W.numel() else None
         lds[j] = _ld(W)
-    _check(lib.logra_payload_apply(payload.data_ptr(), payload.numel(), ctypes.byref(header), entries, ptrs, lds,
-                                   _stream_handle(payload)))
+    with _OnDevice(payload, *Ws):
+        _check(lib.logra_payload_apply(payload.data_ptr(), payload.numel(), ctypes.byref(header), entries, ptrs, lds,
+                                       _stream_handle(payload)))
 
 
 def rowadam_merge(W, S, v, seed: int, r: int, step: int, beta2: float, eps_rel: float, scale: float):
@@ -554,9 +601,10 @@ def rowadam_merge(W, S, v, seed: int, r: int, step: int, beta2: float, eps_rel: 
     d, k = W.shape
     if tuple(S.shape) != (d, r) or v.numel() != d:
         raise ValueError(f"S must be ({d}, {r}) and v ({d},)")
-    _check(lib.logra_rowadam_merge(W.data_ptr() if W.numel() else None, _ld(W), S.data_ptr(), _ld(S), v.data_ptr(),
-                                   d, k, ctypes.c_uint64(seed & (2**64 - 1)), r, step, beta2, eps_rel, scale,
-                                   _stream_handle(S)))
+    with _OnDevice(W, S, v):
+        _check(lib.logra_rowadam_merge(W.data_ptr() if W.numel() else None, _ld(W), S.data_ptr(), _ld(S), v.data_ptr(),
+                                       d, k, ctypes.c_uint64(seed & (2**64 - 1)), r, step, beta2, eps_rel, scale,
+                                       _stream_handle(S)))
     return W
 
 
@@ -570,8 +618,9 @@ def rowadam_scale(S, v, step: int, beta2: float, eps_rel: float = 1e-8):
     d, r = S.shape
     if v.numel() != d:
         raise ValueError("v must have one value per row of S")
-    _check(lib.logra_rowadam_scale(S.data_ptr(), _ld(S), v.data_ptr(), d, r, int(step),
-                                   float(beta2), float(eps_rel), _stream_handle(S)))
+    with _OnDevice(S, v):
+        _check(lib.logra_rowadam_scale(S.data_ptr(), _ld(S), v.data_ptr(), d, r, int(step),
+                                       float(beta2), float(eps_rel), _stream_handle(S)))
     return S
 
 
@@ -604,13 +653,14 @@ def predicted_kl(z, zdot, temperature: float, row_var=None, q=None):
         if row_var.numel() != n:
             raise ValueError("row_var must have one entry per row")
     dt = DTYPE_BF16 if z.dtype == torch.bfloat16 else DTYPE_F32
-    _check(
-        lib.logra_predicted_kl(
-            z.data_ptr() if n else None, _ld(z) if n else 0, zdot.data_ptr() if n else None,
-            _ld(zdot) if n else 0, n, V, dt, float(temperature),
-            row_var.data_ptr() if row_var is not None and n else None, q.data_ptr(), _stream_handle(q),
+    with _OnDevice(z, zdot, row_var, q):
+        _check(
+            lib.logra_predicted_kl(
+                z.data_ptr() if n else None, _ld(z) if n else 0, zdot.data_ptr() if n else None,
+                _ld(zdot) if n else 0, n, V, dt, float(temperature),
+                row_var.data_ptr() if row_var is not None and n else None, q.data_ptr(), _stream_handle(q),
+            )
         )
-    )
     return q
 
 
@@ -635,8 +685,9 @@ def signs(seed: int, r: int, k: int, device="cuda"):
 
     lib = load_library()
     out = torch.empty((r, k), dtype=torch.int8, device=device)
-    _check(lib.logra_signs(ctypes.c_uint64(seed & (2**64 - 1)), r, k, out.data_ptr() if k else None,
-                           _stream_handle(out)))
+    with _OnDevice(out):
+        _check(lib.logra_signs(ctypes.c_uint64(seed & (2**64 - 1)), r, k, out.data_ptr() if k else None,
+                               _stream_handle(out)))
     return out
 
 
@@ -651,8 +702,9 @@ def stream_read(t, sink):
     if not isinstance(sink, torch.Tensor) or sink.dtype != torch.int32 or not sink.is_cuda:
         raise TypeError("sink must be an int32 device tensor")
     nbytes = t.numel() * t.element_size()
-    _check(load_library().logra_stream_read(t.data_ptr() if nbytes else None, nbytes, sink.data_ptr(),
-                                            _stream_handle(t)))
+    with _OnDevice(t, sink):
+        _check(load_library().logra_stream_read(t.data_ptr() if nbytes else None, nbytes, sink.data_ptr(),
+                                                _stream_handle(t)))
 
 
 def workspace_bytes(T: int, d: int, k: int, r: int) -> int:

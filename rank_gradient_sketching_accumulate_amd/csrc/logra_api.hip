@@ -65,10 +65,29 @@ struct Arena {
 std::mutex g_arena_mu;
 std::map<std::pair<std::pair<int, int>, hipStream_t>, Arena> g_arenas;
 
+// Scratch lives on the current device, so the stream must belong to it (a
+// stream of another device would run the kernels there, on memory of this
+// one).  Handles the runtime cannot map to a device (the null stream and the
+// special per-thread handles) are taken to be the current device's.
+logra_status stream_on_device(hipStream_t stream, int dev) {
+  if (stream == nullptr) return LOGRA_OK;
+  hipDevice_t sd = 0;
+  if (hipStreamGetDevice(stream, &sd) != hipSuccess) {
+    (void)hipGetLastError();
+    return LOGRA_OK;
+  }
+  if ((int)sd != dev)
+    return fail(LOGRA_ERR_RANGE, "the stream belongs to device " + std::to_string((int)sd) + " but device " +
+                                     std::to_string(dev) + " is current: make the stream's device current");
+  return LOGRA_OK;
+}
+
 logra_status arena_get(int kind, hipStream_t stream, size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const logra_status sd = stream_on_device(stream, dev);
+  if (sd != LOGRA_OK) return sd;
   std::lock_guard<std::mutex> lk(g_arena_mu);
   Arena& a = g_arenas[{{dev, kind}, stream}];
   if (a.bytes < need) {
@@ -417,11 +436,13 @@ void* g_scratch_ptr[kMaxDevices] = {};
 
 // Device address of `scratch` on the current device (looked up once per
 // device).
-logra_status noalloc_scratch(void** out) {
+logra_status noalloc_scratch(hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(LOGRA_ERR_RANGE, "device ordinal above 63");
+  const logra_status sd = stream_on_device(stream, dev);
+  if (sd != LOGRA_OK) return sd;
   std::lock_guard<std::mutex> lk(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* ptr = nullptr;
@@ -472,7 +493,7 @@ logra_status logra_sketch_accumulate_noalloc(const void* X, int64_t ldx, const v
                                        std::to_string((size_t)LOGRA_NOALLOC_SCRATCH_BYTES) +
                                        " bytes: split the microbatch or use logra_sketch_accumulate");
     void* ptr = nullptr;
-    st = noalloc_scratch(&ptr);
+    st = noalloc_scratch(stream, &ptr);
     if (st != LOGRA_OK) return st;
     char* base = static_cast<char*>(ptr);
     unsigned* counters = nullptr;
