@@ -296,7 +296,7 @@ MergePlan plan_merge(int64_t d, int64_t k, int r, bool gauss) {
   // Tile per wave and chunk (two waves fit per SIMD): one 16-row block x 64
   // columns up to r = 128 with about 2048 workgroups; at r = 256, where the
   // U operands and sign expansion cost more, two 16-row blocks (each expanded
-  // sign operand feeds both) with about 1024 longer column ranges.  Measured
+  // sign operand feeds both) with longer column ranges.  Measured
   // with GPU-only timing over layers from 1536 x 1536 to 17408 x 5120.
   // Above r = 256 (NK = 16) one 16-row block x 64 columns: the U operands
   // alone take 128 registers.
@@ -311,12 +311,36 @@ MergePlan plan_merge(int64_t d, int64_t k, int r, bool gauss) {
   pl.NBW = NBW;
   pl.CB = CB;
   pl.n_rb = (int)((d + 64 * NBW - 1) / (64 * NBW));
-  // Column ranges: as long as possible while about `target` workgroups remain.
   const int64_t CW = 16 * CB;
   const int64_t chunks = (k + CW - 1) / CW;
-  int64_t target = env_int("LOGRA_MERGE_WGS", pl.NK >= 8 ? 1024 : 2048);
-  if (target < 1) target = 1;
-  int64_t n_cr = (target + pl.n_rb - 1) / pl.n_rb;
+  int64_t target = env_int("LOGRA_MERGE_WGS", 0);
+  int64_t n_cr;
+  if (target <= 0 && pl.NK >= 8) {
+    // Above rank 128 a workgroup's column range is long and two workgroups
+    // fit per CU (512 at once): choose the number of ranges that minimises
+    // rounds x (chunks per range + 3), the 3 standing for a range's fixed
+    // cost (U rows, the first sign block); ties go to more workgroups.
+    // Against about 1024 workgroups: 27B attention 53 -> 44 us, 7B down
+    // 107 -> 87 us, 7B q 37 -> 30 us, 7B up 109 -> 94 us, 27B up 138 -> 128 us.
+    int64_t best_cost = -1, best_g = 0;
+    n_cr = 1;
+    for (int64_t c = 1; c <= chunks; ++c) {
+      const int64_t per = (chunks + c - 1) / c;
+      const int64_t used = (chunks + per - 1) / per;
+      const int64_t g = pl.n_rb * used;
+      const int64_t cost = ((g + 511) / 512) * (per + 3);
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && g > best_g)) {
+        best_cost = cost;
+        best_g = g;
+        n_cr = used;
+      }
+    }
+  } else {
+    // Otherwise ranges as long as possible while about `target` workgroups
+    // remain (2048 up to rank 128).
+    if (target <= 0) target = 2048;
+    n_cr = (target + pl.n_rb - 1) / pl.n_rb;
+  }
   if (n_cr > chunks) n_cr = chunks;
   if (n_cr < 1) n_cr = 1;
   pl.cr_cols = ((chunks + n_cr - 1) / n_cr) * CW;
