@@ -468,11 +468,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   // LDS row (wkk * RP + row) with the row stride SROW (the ninth dword only
   // spreads the banks and is never read).  Blocks past k are drawn too;
   // their X is zeroed.
-  constexpr int NGEN = RP * WK / 512;
+  constexpr int NGEN = (RP * WK + 511) / 512;
   auto gen = [&](int j, int buf) {
 #pragma unroll 1
     for (int q = 0; q < NGEN; ++q) {
       const int b = threadIdx.x + 512 * q;
+      if (RP * WK % 512 != 0 && b >= RP * WK) break;  // NB = 4: half the threads draw
       const int row = b % RP, wkk = b / RP;
       uint32_t w[8];
       philox_sign_block(p.seed, (uint32_t)(p.row0 + row), (uint32_t)(cbb + WK * j + wkk), w);
@@ -1831,8 +1832,11 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
   // (attention), 70 -> 59 (up), 191 -> 155 us (down), 7B down at r = 128
   // 81 -> 71 us).  Small r*k otherwise: the whole k range's signs fit in
   // 64 KB of LDS.
-  pl.pwide = (pl.NB >= 8 && pl.ncb >= 2) ? 1 : 0;
-  pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 8 ? 1 : 0;
+  // The LDS-staged projection above rank 64; at ranks 33-64 only for long k
+  // (7B layers at r = 64: 3584 columns 18.8 -> 18.1 us, 18944 columns
+  // 65.4 -> 61.1 us; at 1536 columns the other kernels win, 6.9 against 9.9).
+  pl.pwide = ((pl.NB >= 8 && pl.ncb >= 2) || (pl.NB == 4 && pl.ncb >= 14)) ? 1 : 0;
+  pl.pwide = env_int("LOGRA_PROJ_WIDE", pl.pwide) != 0 && pl.NB >= 4 ? 1 : 0;
   pl.small_proj = (!pl.pwide && (size_t)RP * pl.ncb * 36 <= 65536 && pl.NB <= 8) ? 1 : 0;
   pl.small_proj = pl.pwide ? 0 : env_int("LOGRA_PROJ_SMALL", pl.small_proj);
   int64_t TT;
@@ -2100,6 +2104,7 @@ bool proj_launch(const SketchPlan& pl, const ProjParams& p, hipStream_t s) {
     const int grid = (int)align_up((size_t)pl.n_tt * pl.n_k, (size_t)8 * pl.n_k);
     if (pl.NB == 16) hipLaunchKernelGGL((proj_lds_kernel<16>), dim3(grid), dim3(512), 0, s, p);
     else if (pl.NB == 8) hipLaunchKernelGGL((proj_lds_kernel<8>), dim3(grid), dim3(512), 0, s, p);
+    else if (pl.NB == 4) hipLaunchKernelGGL((proj_lds_kernel<4>), dim3(grid), dim3(512), 0, s, p);
     else return false;
     return true;
   }

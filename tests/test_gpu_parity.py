@@ -343,17 +343,20 @@ def test_sketch_half_tiles_on_shorter_s(T, k, d, r):
 
 
 LDS_PROJ_EDGES = [(1, 264, 8, 128), (17, 520, 33, 65), (63, 1029, 40, 256), (65, 777, 20, 200),
-                  (130, 264, 7, 256), (300, 2056, 50, 96), (64, 1031, 9, 129)]
+                  (130, 264, 7, 256), (300, 2056, 50, 96), (64, 1031, 9, 129),
+                  # ranks 33-64 take it from 14 sign blocks of k on
+                  (63, 3600, 40, 64), (130, 4100, 33, 50), (300, 5000, 20, 33)]
 
 
 @pytest.mark.parametrize("T,k,d,r", LDS_PROJ_EDGES)
 @pytest.mark.parametrize("env", [{}, {"LOGRA_PROJ_NK": 2}, {"LOGRA_PROJ_NK": 8}], ids=_plan_id)
 def test_sketch_lds_projection_edges(T, k, d, r, env, monkeypatch):
-    """The LDS-staged projection (ranks above 64, k > 256) at its edges:
-    token tiles of 1 to 130 tokens (rows past T staged as zero), k with a
-    ragged last 256-column block and k % 8 != 0 (the slab's boundary chunk
-    masked element by element), r = 129 padded to 256 columns, and column splits
-    (with NK = 8 on small k most splits hold no block at all)."""
+    """The LDS-staged projection (ranks above 64 with k > 256; ranks 33-64
+    with k > 3328) at its edges: token tiles of 1 to 130 tokens (rows past T
+    staged as zero), k with a ragged last 256-column block and k % 8 != 0
+    (the slab's boundary chunk masked element by element), r = 129 padded to
+    256 columns, r = 33 padded to 64, and column splits (with NK = 8 on small
+    k most splits hold no block at all)."""
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, str(v_))
     _say("lds projection edges", T, k, d, r, env)
