@@ -27,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -45,10 +46,17 @@ MALL_BYTES = 256 * 2**20
 
 
 def kernel_source_sha() -> str:
+    """Hash of the library's sources with comments and trailing blanks
+    stripped: a profile taken under the same code keeps matching after an
+    edit of comments only."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

@@ -59,7 +59,7 @@ struct SketchPlan {
   int small_proj;         // 1: proj_small_kernel (all signs of k in LDS)
   int MBW, WK;            // projection: 16-token blocks per wave, waves along k
   int PNW;                // projection (round-based): waves per workgroup (4 or 8)
-  int pwide;              // 1: proj_lds_kernel (NB = 8 or 16, 64-token tiles, X staged through LDS)
+  int pwide;              // 1: proj_lds_kernel (NB = 4, 8 or 16, 64-token tiles, X staged through LDS)
   int n_tt, n_k, cbs_per, ncb;
   int64_t Tpad;
   int cvar;               // contraction variant (see contract_launch)

@@ -402,7 +402,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ===========================================================================
-// Projection for ranks above 64 (NB = 8 or 16), X staged through LDS.
+// Projection for ranks above 32 (NB = 4, 8 or 16), X staged through LDS.
 // Eight waves, two per SIMD.  Wave (wn, wk) keeps the workgroup's 64 tokens
 // x one half of P's 16*NB columns in accumulators (8*NB*2 registers: 128 at
 // NB = 16, pinned to the AGPR half of the wave's registers), so that each
@@ -421,7 +421,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 // the other LDS buffer at the end of step u, before the step's barrier.
 // Each round first draws the signs of the next round's four blocks into the
 // other LDS sign buffer (two Philox blocks per thread at NB = 16, one at
-// NB = 8); the signs never leave registers and LDS.  After the last round
+// NB = 8, one for half the threads at NB = 4); the signs never leave
+// registers and LDS.  After the last round
 // the four wave columns are summed through LDS in two halving rounds, and the wk = 0 waves write P (or, with column
 // splits across workgroups, their fp32 partial; the last split to arrive
 // sums the partials).
@@ -630,7 +631,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   __syncthreads();
   if (!s_last) return;
-  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2 or 4)
+  constexpr int ITEMS = TT * RP / 4 / 512;  // float4 items per thread (2, 4 or 8)
   f32x4 sum[ITEMS];
   int64_t e0[ITEMS];
 #pragma unroll
