@@ -308,8 +308,17 @@ class _OnDevice:
     None are ignored."""
 
     __slots__ = ("dev", "prev")
+    _single = None  # True once the process is known to see one device
 
     def __init__(self, *tensors):
+        self.prev = None
+        if _OnDevice._single is None:
+            import torch
+
+            _OnDevice._single = torch.cuda.device_count() == 1
+        if _OnDevice._single:
+            self.dev = None  # one device: it is the current one
+            return
         dev = None
         for t in tensors:
             if t is None or not t.is_cuda:
@@ -320,7 +329,6 @@ class _OnDevice:
             elif di != dev:
                 raise ValueError("the device tensors of one call must be on the same device")
         self.dev = dev
-        self.prev = None
 
     def __enter__(self):
         if self.dev is not None:
