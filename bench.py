@@ -176,7 +176,7 @@ def predicted_kl_timing(torch, lg, wl, stream, dev, calls: int):
         q = torch.empty(1, dtype=torch.float32, device=dev)
         t, h = gpu_time_per_call(torch, stream, lambda i: lg.predicted_kl(ins[i % ncopy][0], ins[i % ncopy][1], 1.0,
                                                                           row_var=rv, q=q), calls)
-        # the box's streaming-read time for the same two arrays (two launches)
+        # the GPU's streaming-read time for the same two arrays (two launches)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         t_rd, _ = gpu_time_per_call(torch, stream, lambda i: (lg.stream_read(ins[i % ncopy][0], sink),
                                                               lg.stream_read(ins[i % ncopy][1], sink)), calls)
@@ -522,7 +522,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
-        # Streaming ceilings measured on this machine for the same bytes, timed
+        # Streaming ceilings measured on this GPU for the same bytes, timed
         # the same way: the sketch call's two input streams read as two
         # launches, one window of the same size read in a single launch, and
         # the merge's W as an in-place read-modify-write over the copies.
@@ -536,7 +536,7 @@ def main():
         t_read2, _ = gpu_time(read_two, n_calls)
         t_rmw, _ = gpu_time(lambda i: Ws[i % n_w].mul_(1.0), n_merges)
         extras["ceiling"] = {
-            "what": "streaming reads/writes of the same bytes on this box (logra_stream_read; torch in-place mul for W)",
+            "what": "streaming reads/writes of the same bytes on this GPU (logra_stream_read; torch in-place mul for W)",
             "sketch_bytes_two_reads_us": t_read2 * 1e6,
             "sketch_frac_of_two_reads": t_read2 / t_call,
             "merge_w_rmw_us": t_rmw * 1e6,

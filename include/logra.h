@@ -482,7 +482,7 @@ logra_status logra_signs(uint64_t seed, int32_t r, int64_t k, int8_t* out,
 /* Measurement aid (not part of the method): streams `bytes` bytes from the
  * device buffer `ptr` with 16-byte loads, four per thread in flight, and
  * discards them (only a one-in-2^32 xor value is written to the device word
- * *sink).  Timing it over the bytes one sketch call reads gives the box's
+ * *sink).  Timing it over the bytes one sketch call reads gives the GPU's
  * streaming-read ceiling for that call.  ptr 16-byte aligned, bytes a
  * multiple of 16 (LOGRA_ERR_ALIGN otherwise); bytes == 0 is a no-op. */
 logra_status logra_stream_read(const void* ptr, size_t bytes, uint32_t* sink, hipStream_t stream);

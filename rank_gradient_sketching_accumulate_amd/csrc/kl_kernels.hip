@@ -265,7 +265,7 @@ KLPlan plan_kl(int64_t n, int64_t V) {
   KLPlan pl{};
   const int64_t blk = (int64_t)kKLThreads * kKLStep;
   // Column ranges only when there are fewer than ~2048 rows: on the
-  // 2048 x 151,936 probe one range per row ran at 0.92 of the box's
+  // 2048 x 151,936 probe one range per row ran at 0.92 of the GPU's
   // streaming-read time for the same bytes, and 4, 8 or 16 ranges per row
   // were 3-10 % slower.  Each range keeps at least two steps of its row.
   int64_t want = n > 0 ? (2048 + n - 1) / n : 1;
