@@ -1951,21 +1951,25 @@ SketchPlan plan_sketch(int64_t T, int64_t k, int64_t d, int r, bool det, bool hi
     const int tile = det ? 1 : env_int("LOGRA_CON_TILE", tall ? 0 : ((pl.NB == 8 || T <= 8192) ? 1 : 0));
     const int big = env_int("LOGRA_CON_BIG", tall ? 1 : -1);
     const bool use_big = big >= 0 ? big != 0 : ((d + bd8 - 1) / bd8) * (nks / 16) >= 256;
+    // The half tiles also beat the token-lane tiles on shorter S: 3584-row
+    // layers at 8192 tokens, 58-66 -> 49 us above rank 128 and 37 -> 32.5 us
+    // at rank 128 (at 1536 rows, 20 -> 26 us: not taken there).
+    const int64_t span = ((d + bd8 - 1) / bd8) * (nks / 16);
+    const bool half_short = pl.NB == 16 ? span >= 128 : span >= 96;
     // Rank 256 on large layers: the one-wave-per-SIMD 256 x 256 tiles.
     // (With P as a hi/lo pair contract_big_kernel is as fast; the shared-
-    // operand kernel serves the single-bf16 contraction.)
-    const int wide = (!det && pl.NB == 16) ? env_int("LOGRA_CON_WIDE", (hi_only && (tall || use_big)) ? 1 : 0) : 0;
+    // operand kernel serves the single-bf16 contraction, also on the shorter
+    // S where the half tiles serve the hi/lo one: 7B q at r = 256 81 -> 73 us
+    // per sketch call, 7B down 151 -> 141 us.)
+    const int wide = (!det && pl.NB == 16)
+                         ? env_int("LOGRA_CON_WIDE", (hi_only && (tall || use_big || half_short)) ? 1 : 0)
+                         : 0;
     // Otherwise the 256 x 256 tiles as two 256 x 128 workgroups per CU
     // (27B up layer 336 -> 314 us, attention 110 -> 105, 7B up 185 -> 174).
     // At NB = 8 one such workgroup holds the whole rank: used where the
     // 512 x 128 tiles would be too few for a round (1.5B up layer, r = 128:
     // 78.8 -> 67.1 us); on tall S (7B up) the 512 x 128 tiles stay ahead
     // (105.6 against 111.1 us).
-    // The half tiles also beat the token-lane tiles on shorter S: 3584-row
-    // layers at 8192 tokens, 58-66 -> 49 us above rank 128 and 37 -> 32.5 us
-    // at rank 128 (at 1536 rows, 20 -> 26 us: not taken there).
-    const int64_t span = ((d + bd8 - 1) / bd8) * (nks / 16);
-    const bool half_short = pl.NB == 16 ? span >= 128 : span >= 96;
     const int halfk = (!det && !wide && (tall || use_big || half_short))
                           ? env_int("LOGRA_CON_HALF", (pl.NB == 16 || !tall) ? 1 : 0)
                           : 0;
