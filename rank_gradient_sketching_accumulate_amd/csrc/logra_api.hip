@@ -246,7 +246,7 @@ logra_status basis_generate(uint64_t seed, int row0, int rr, int rp, int64_t k, 
 // P = X s^T into the hi/lo planes (Pk order); tokens in [T, Tpad) get zeros.
 // hi_only: the fused call contracts with P rounded once to bf16: its
 // projection writes no low plane when the contraction reads none (the
-// single-bf16 tiling), or a zero one otherwise.  The split call always
+// single-bf16 and half tilings), or a zero one otherwise.  The split call always
 // writes both planes.
 // counters: the split counters (zero, n_counters of them), or null to take
 // them from the library's per-stream region.
@@ -272,7 +272,7 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
     gp.Alo = al;
     gp.kpad = kpad;
     gp.Tw = (T + 31) / 32 * 32;
-    gp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
+    gp.hi_only = !hi_only ? 0 : ((pl.cvar == 6 || pl.cvar == 7) ? 1 : 2);
     if (!proj_gauss_launch(pl, gp, stream)) return fail(LOGRA_ERR_RANGE, "no Gaussian projection kernel for this rank");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "Gaussian projection launch");
@@ -294,7 +294,7 @@ logra_status enqueue_projection(const SketchPlan& pl, char* base, const void* X,
       if (st != LOGRA_OK) return st;
     }
   }
-  pp.hi_only = !hi_only ? 0 : (pl.cvar == 6 ? 1 : 2);
+  pp.hi_only = !hi_only ? 0 : ((pl.cvar == 6 || pl.cvar == 7) ? 1 : 2);
   if (!proj_launch(pl, pp, stream)) return fail(LOGRA_ERR_RANGE, "no projection kernel for this tile");
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "projection launch");
@@ -316,7 +316,7 @@ logra_status enqueue_contraction(const SketchPlan& pl, char* base, const void* d
   cp.n_dt = pl.n_dt; cp.n_ts = pl.n_ts; cp.ksp = pl.ksp;
   cp.atomic_out = pl.n_ts > 1 ? 1 : 0;
   cp.bands = pl.cbands;
-  cp.hi_only = (hi_only && pl.cvar == 6) ? 1 : 0;
+  cp.hi_only = (hi_only && (pl.cvar == 6 || pl.cvar == 7)) ? 1 : 0;
   if (pl.use_part) {
     cp.part = reinterpret_cast<float*>(base + pl.off_cpart);
     cp.part_split = d * 16 * pl.NB;

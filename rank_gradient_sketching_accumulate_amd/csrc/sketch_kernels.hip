@@ -1242,16 +1242,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void c
 // rows comes from L2.
 // NB = 8 (ranks 65-128): the same workgroup holds all of P's columns (one
 // "half" per tile), two workgroups per CU from different (tile, split) pairs.
-template <int DP, int NB>
+// HL = 1: P's high bf16 plane only (the single-bf16 contraction: one MFMA per
+// product, no low plane loaded).
+template <int DP, int NB, int HL = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void contract_half_kernel(ContractParams p) {
   static_assert(NB == 16 || NB == 8, "two halves of 128 columns, or one");
+  static_assert(HL == 1 || HL == 2, "one or two planes of P");
   constexpr int NBW = 8;                 // column blocks per wave (half of the tile)
   constexpr int NHALF = NB / NBW;
   constexpr int PVH = NBW * 64;          // u32x4 words per plane and step for the half
-  constexpr int PER = 2 * PVH / 256;     // words each thread moves per step
-  constexpr int PH = PER / 2;
+  constexpr int PH = PVH / 256;          // words each thread moves per plane and step
+  constexpr int PER = HL * PH;           // words each thread moves per step
   static_assert(PH * 256 == PVH, "whole planes per step");
-  __shared__ u32x4 pt[2][2 * PVH];
+  __shared__ u32x4 pt[2][HL * PVH];
   const int lin = xcd_linear_id(blockIdx.x, gridDim.x);
   const int half = NHALF == 2 ? (lin & 1) : 0;
   const int rest = NHALF == 2 ? (lin >> 1) : lin;
@@ -1296,14 +1299,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
     for (int j = 0; j < PH; ++j) {
       sl[j] = buf_load16(rph, base + 256 * 16 * j);
-      sl[PH + j] = buf_load16(rpl, base + 256 * 16 * j);
+      if constexpr (HL == 2) sl[PH + j] = buf_load16(rpl, base + 256 * 16 * j);
     }
   };
   auto store_p = [&](const u32x4 (&sl)[PER], int buf) {
 #pragma unroll
     for (int j = 0; j < PH; ++j) {
       pt[buf][threadIdx.x + 256 * j] = sl[j];
-      pt[buf][PVH + threadIdx.x + 256 * j] = sl[PH + j];
+      if constexpr (HL == 2) pt[buf][PVH + threadIdx.x + 256 * j] = sl[PH + j];
     }
   };
 
@@ -1333,11 +1336,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           const u32x4 bh = ph[nb * 64 + lane];
-          const u32x4 bl = ph[PVH + nb * 64 + lane];
+          if constexpr (HL == 2) {
+            const u32x4 bl = ph[PVH + nb * 64 + lane];
 #pragma unroll
-          for (int c = 0; c < kDC; ++c) {
-            acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
-            acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
+            for (int c = 0; c < kDC; ++c) {
+              acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
+              acc[c][nb] = mfma_16x16x32(a[c], bl, acc[c][nb]);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < kDC; ++c) acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
           }
         }
         if (m + 1 < nsteps) store_p(stg[(u + 1) % DP], (u + 1) & 1);
@@ -2185,8 +2193,14 @@ bool contract_launch(const SketchPlan& pl, const ContractParams& p, hipStream_t 
       else hipLaunchKernelGGL((contract_big_kernel<16, 2, 1>), dim3(grid), dim3(512), 0, s, p);
       return true;
     case 7:
-      if (pl.NB == 16)
+      if (pl.NB == 16 && p.hi_only)
+        hipLaunchKernelGGL((contract_half_kernel<2, 16, 1>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts * 2, 8)),
+                           dim3(256), 0, s, p);
+      else if (pl.NB == 16)
         hipLaunchKernelGGL((contract_half_kernel<2, 16>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts * 2, 8)),
+                           dim3(256), 0, s, p);
+      else if (pl.NB == 8 && p.hi_only)
+        hipLaunchKernelGGL((contract_half_kernel<2, 8, 1>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts, 8)),
                            dim3(256), 0, s, p);
       else if (pl.NB == 8)
         hipLaunchKernelGGL((contract_half_kernel<2, 8>), dim3((unsigned)align_up((size_t)pl.n_dt * pl.n_ts, 8)),
