@@ -210,8 +210,9 @@ void kl_launch(const KLPlan& pl, const KLParams& p, int bf16, float* row_var, fl
 // RowAdam and the sign dump.
 // ---------------------------------------------------------------------------
 // RowAdam: at most kRowAdamBlocks blocks per kernel; partial holds
-// 2 * kRowAdamBlocks doubles, partial2 kRowAdamBlocks.
-constexpr int kRowAdamBlocks = 512;
+// 2 * kRowAdamBlocks doubles, partial2 kRowAdamBlocks (its first two hold
+// the finished eps and rescale factor).
+constexpr int kRowAdamBlocks = 4096;
 void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float beta2, double inv_bias,
                     float eps_rel, float* root, float* ssq, double* partial, double* partial2, hipStream_t s,
                     float* rowmul = nullptr);

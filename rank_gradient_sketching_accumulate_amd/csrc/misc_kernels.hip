@@ -41,10 +41,20 @@ __device__ __forceinline__ double block_sum_256(double x, double* sh) {
 }
 
 // Fixed-order sum of n values spaced `stride` apart (every block that calls
-// it with the same arguments gets the same bits).
+// it with the same arguments gets the same bits).  Each thread adds its
+// values in increasing order; eight loads are issued before their adds so
+// that a long list does not wait out one memory latency per value.
 __device__ __forceinline__ double sum_partials(const double* p, int n, int stride, double* sh) {
   double a = 0.0;
-  for (int j = threadIdx.x; j < n; j += 256) a += p[(int64_t)j * stride];
+  int j = threadIdx.x;
+  for (; j + 256 * 7 < n; j += 256 * 8) {
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = p[(int64_t)(j + 256 * q) * stride];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a += v[q];
+  }
+  for (; j < n; j += 256) a += p[(int64_t)j * stride];
   return block_sum_256(a, sh);
 }
 
@@ -95,9 +105,12 @@ __global__ __launch_bounds__(256) void rowadam_rows_kernel(const float* S, int64
   }
 }
 
+// eps from the mean of the row roots and ||S||^2, both from the row
+// kernel's block partials in a fixed order (every block gets the same bits;
+// block 0 stores them in fin[0], fin[1]), then this block's share of
+// ||U~||^2 = sum_i ||S_i||^2 / (sqrt(vh_i) + eps)^2 into fin[2 + block].
 __global__ __launch_bounds__(256) void rowadam_norm_kernel(const double* partial, int nparts, const float* root,
-                                                          const float* ssq, int64_t d, float eps_rel,
-                                                          double* partial2) {
+                                                          const float* ssq, int64_t d, float eps_rel, double* fin) {
   __shared__ double sh[256];
   const double sum_root = sum_partials(partial, nparts, 2, sh);
   const double eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
@@ -107,34 +120,43 @@ __global__ __launch_bounds__(256) void rowadam_norm_kernel(const double* partial
     c += (double)ssq[row] / (den * den);
   }
   const double t = block_sum_256(c, sh);
-  if (threadIdx.x == 0) partial2[blockIdx.x] = t;
+  if (blockIdx.x == 0) {
+    const double norm_s2 = sum_partials(partial + 1, nparts, 2, sh);
+    if (threadIdx.x == 0) {
+      fin[0] = eps;
+      fin[1] = norm_s2;
+    }
+  }
+  if (threadIdx.x == 0) fin[2 + blockIdx.x] = t;
 }
 
-// FUSED (few rows): every block sums ||S_i||^2 / (sqrt(vh_i) + eps)^2 over
-// all rows itself, in one fixed order, instead of reading the partials of
-// rowadam_norm_kernel (one launch fewer).
+// FUSED (few rows): every block works eps and the factor out itself from
+// the row kernel's nparts block partials (one launch fewer); otherwise it
+// reads eps and ||S||^2 from fin and sums the nparts norm partials after them.
 template <bool VEC, bool FUSED>
 __global__ __launch_bounds__(256) void rowadam_apply_kernel(float* S, int64_t lds, int64_t d, int r, int L,
                                                            const float* root, const float* ssq,
                                                            const double* partial, int nparts,
-                                                           const double* partial2, int nparts2, float eps_rel,
-                                                           float* rowmul) {
-  __shared__ double sh[256];
-  const double sum_root = sum_partials(partial, nparts, 2, sh);
-  const double norm_s2 = sum_partials(partial + 1, nparts, 2, sh);
-  const double eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
-  double norm_u2;
+                                                           const double* fin, float eps_rel, float* rowmul) {
+  double eps, fac;
   if constexpr (FUSED) {
+    __shared__ double sh[256];
+    const double sum_root = sum_partials(partial, nparts, 2, sh);
+    const double norm_s2 = sum_partials(partial + 1, nparts, 2, sh);
+    eps = fmax((double)eps_rel * (sum_root / (double)d), 1e-30);
     double c = 0.0;
     for (int64_t row = threadIdx.x; row < d; row += 256) {
       const double den = (double)root[row] + eps;
       c += (double)ssq[row] / (den * den);
     }
-    norm_u2 = block_sum_256(c, sh);
+    const double norm_u2 = block_sum_256(c, sh);
+    fac = norm_u2 > 0.0 ? sqrt(norm_s2 / norm_u2) : 0.0;
   } else {
-    norm_u2 = sum_partials(partial2, nparts2, 1, sh);
+    __shared__ double sh[256];
+    eps = fin[0];
+    const double norm_u2 = sum_partials(fin + 2, nparts, 1, sh);
+    fac = norm_u2 > 0.0 ? sqrt(fin[1] / norm_u2) : 0.0;
   }
-  const double fac = norm_u2 > 0.0 ? sqrt(norm_s2 / norm_u2) : 0.0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane & (L - 1);
   const int rpw = 64 / L;
@@ -167,38 +189,39 @@ void rowadam_launch(float* S, int64_t lds, float* v, int64_t d, int r, float bet
   const bool vec = (((uintptr_t)S & 15) == 0) && (lds % 4 == 0) && (r % 4 == 0);
   int L = 1;
   while (L < 64 && 4 * L < r) L <<= 1;  // float4 lanes per row (the scalar path uses the same grouping)
+  // One pass over the rows per block where the block cap allows: the row
+  // statistics are latency-bound (a row's load, its reduction, then v).
   const int64_t rpb = 4 * (int64_t)(64 / L);
   int64_t blocks = (d + rpb - 1) / rpb;
   if (blocks > kRowAdamBlocks) blocks = kRowAdamBlocks;
-  int64_t nblocks = (d + 255) / 256;
-  if (nblocks > kRowAdamBlocks) nblocks = kRowAdamBlocks;
   if (vec)
     hipLaunchKernelGGL(rowadam_rows_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, v, d, r, L, beta2,
                        inv_bias, root, ssq, partial);
   else
     hipLaunchKernelGGL(rowadam_rows_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, S, lds, v, d, r, L, beta2,
                        inv_bias, root, ssq, partial);
-  // Up to 2048 rows every rescale block sums the second norm itself (at most
-  // 16 KB of L2 reads per block) and the middle kernel is skipped: 1536 rows
-  // at r = 64 take 11.1 us instead of 12.7; at 3584 rows the extra reads
-  // cost more than the launch (13.7 against 13.3 us).
+  // Up to 2048 rows every rescale block works out eps and the factor itself
+  // (at most 16 KB of L2 reads per block) and the middle kernel is skipped:
+  // 1536 rows at r = 64 take 11.1 us instead of 12.7.
   if (d <= 2048) {
     if (vec)
       hipLaunchKernelGGL((rowadam_apply_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel, rowmul);
+                         root, ssq, partial, (int)blocks, partial2, eps_rel, rowmul);
     else
       hipLaunchKernelGGL((rowadam_apply_kernel<false, true>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                         root, ssq, partial, (int)blocks, partial2, 0, eps_rel, rowmul);
+                         root, ssq, partial, (int)blocks, partial2, eps_rel, rowmul);
     return;
   }
+  int64_t nblocks = (d + 255) / 256;
+  if (nblocks > 256) nblocks = 256;
   hipLaunchKernelGGL(rowadam_norm_kernel, dim3((unsigned)nblocks), dim3(256), 0, s, partial, (int)blocks, root, ssq, d,
                      eps_rel, partial2);
   if (vec)
     hipLaunchKernelGGL((rowadam_apply_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel, rowmul);
+                       root, ssq, partial, (int)nblocks, partial2, eps_rel, rowmul);
   else
     hipLaunchKernelGGL((rowadam_apply_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0, s, S, lds, d, r, L,
-                       root, ssq, partial, (int)blocks, partial2, (int)nblocks, eps_rel, rowmul);
+                       root, ssq, partial, (int)nblocks, partial2, eps_rel, rowmul);
 }
 
 // Signs s (r x k) as int8 +-1; one thread per (row, 256-column block).
