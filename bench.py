@@ -342,6 +342,12 @@ def sweep(steps: int):
                 nm = max(steps, 2 * n_w)
                 t_merge, _ = gpu_time_per_call(
                     torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]), nm)
+                prev = lg.set_precision(PRECISIONS["bf16"])
+                try:
+                    t_merge1, _ = gpu_time_per_call(
+                        torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]), nm)
+                finally:
+                    lg.set_precision(prev)
                 t_ra, _ = rowadam_time(torch, lg, stream, S, steps)
                 del Ws, S
                 torch.cuda.empty_cache()
@@ -352,6 +358,7 @@ def sweep(steps: int):
                     "sketch_GBps": sb / t_call / 1e9, "sketch_frac": sb / t_call / 1e9 / HBM_PEAK_GBS,
                     "merge_us": t_merge * 1e6, "merge_GBps": mb / t_merge / 1e9,
                     "merge_frac": mb / t_merge / 1e9 / HBM_PEAK_GBS,
+                    "merge_bf16_us": t_merge1 * 1e6, "merge_bf16_frac": mb / t_merge1 / 1e9 / HBM_PEAK_GBS,
                     "rowadam_us": t_ra * 1e6, "rowadam_GBps": rowadam_bytes(d, r) / t_ra / 1e9,
                     "kernel_source_sha": kernel_source_sha(),
                 }), flush=True)
@@ -381,10 +388,16 @@ def layer_rates(torch, lg, wl, stream, dev, w, li, r, calls, precisions=("bf16x2
     torch.cuda.empty_cache()
     n_w = max(2, math.ceil(2.5 * MALL_BYTES / (2 * d * k)))
     Ws = [wl.layer_weight(w, li, device=dev) for _ in range(n_w)]
-    t, _ = gpu_time_per_call(torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]),
-                             max(calls, 2 * n_w))
     mb = merge_bytes(d, k, r)
-    out["merge"] = {"us": t * 1e6, "GBps": mb / t / 1e9, "frac": mb / t / 1e9 / HBM_PEAK_GBS}
+    for prec in precisions:
+        prev = lg.set_precision(PRECISIONS[prec])
+        try:
+            t, _ = gpu_time_per_call(torch, stream, lambda j: lg.merge_update(Ws[j % n_w], S, seed, r, w.scales[-1]),
+                                     max(calls, 2 * n_w))
+        finally:
+            lg.set_precision(prev)
+        key = "merge" if prec == "bf16x2" else f"merge_{prec}"
+        out[key] = {"us": t * 1e6, "GBps": mb / t / 1e9, "frac": mb / t / 1e9 / HBM_PEAK_GBS}
     del Ws, S
     torch.cuda.empty_cache()
     return out
@@ -542,15 +555,19 @@ def main():
             "merge_w_rmw_us": t_rmw * 1e6,
             "merge_frac_of_rmw": t_rmw / t_merge,
         }
-        # The other precision mode on the same inputs.
+        # The other precision mode on the same inputs (sketch call, merge and
+        # the step they make up).
         other = "bf16" if args.precision == "bf16x2" else "bf16x2"
         prev = lg.set_precision(PRECISIONS[other])
         try:
             t_other, _ = gpu_time(sketch_call, n_calls)
+            t_mother, _ = gpu_time(lambda i: lg.merge_update(Ws[i % n_w], S, seed, r, scale), n_merges)
         finally:
             lg.set_precision(prev)
         extras["sketch_" + other] = {"avg_call_us": t_other * 1e6, "achieved": sb / t_other / 1e9,
-                                     "frac": sb / t_other / 1e9 / HBM_PEAK_GBS, "tokens_per_s": T / t_other}
+                                     "frac": sb / t_other / 1e9 / HBM_PEAK_GBS, "tokens_per_s": T / t_other,
+                                     "merge_us": t_mother * 1e6, "merge_frac": mb / t_mother / 1e9 / HBM_PEAK_GBS,
+                                     "step_tokens_per_s_from_kernel_times": M * T / (M * t_other + t_mother)}
         # The Gaussian basis on the same inputs (sketch call, and the merge
         # including its basis generation).
         prev = lg.set_basis(lg.BASIS_GAUSSIAN)

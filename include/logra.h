@@ -176,9 +176,9 @@ logra_status logra_basis_normals(uint64_t seed, int32_t r, int64_t k, float* out
 int logra_set_deterministic(int enable);
 
 /*
- * Precision of the contraction (a setting of the calling thread; returns the
- * previous mode).  The projected inputs P are fp32 sums; the contraction
- * multiplies them on bf16 matrix cores.
+ * Precision of the contraction and of the merge (a setting of the calling
+ * thread; returns the previous mode).  The projected inputs P are fp32 sums;
+ * the contraction multiplies them on bf16 matrix cores.
  *
  *   LOGRA_PRECISION_BF16X2 (default): P is carried as a bf16 high part plus
  *     a bf16 low part of the remainder (about 16 significant bits) and each
@@ -192,6 +192,16 @@ int logra_set_deterministic(int enable);
  * Applies to logra_sketch_accumulate and logra_sketch_accumulate_noalloc.
  * The split calls always use both planes: logra_project writes them and
  * logra_contract reads them.
+ *
+ * The mode also sets how the merges (logra_merge_update,
+ * logra_merge_update_grouped, logra_rowadam_merge) carry the factor U with
+ * the random-sign basis: as a bf16 high/low pair (default; two MFMAs per
+ * product) or rounded once to bf16 (one MFMA per product).  The latter puts
+ * about 1.1e-3 relative (Frobenius) error into the update before W is
+ * rounded; on a weight the update only nudges, W stays within the same
+ * tolerance either way.  With the Gaussian basis the merges keep both halves.
+ * A trainer and a receiver that must agree bitwise (section 2.2's sync
+ * apply) merge in the same mode.
  */
 #define LOGRA_PRECISION_BF16X2 0
 #define LOGRA_PRECISION_BF16 1

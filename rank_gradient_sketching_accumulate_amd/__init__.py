@@ -414,9 +414,10 @@ PRECISION_BF16 = 1
 
 
 def set_precision(mode: int) -> int:
-    """Contraction precision on the calling thread: PRECISION_BF16X2 (P as a
-    bf16 high/low pair, the default) or PRECISION_BF16 (P rounded once to
-    bf16).  Returns the previous mode."""
+    """Precision on the calling thread: PRECISION_BF16X2 (P in the fused
+    sketch, and U in the merges with the sign basis, as a bf16 high/low
+    pair; the default) or PRECISION_BF16 (each rounded once to bf16).
+    Returns the previous mode."""
     return int(load_library().logra_set_precision(int(mode)))
 
 

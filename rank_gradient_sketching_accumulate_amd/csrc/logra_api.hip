@@ -360,6 +360,7 @@ logra_status prepare_merge(void* W, int64_t ldw, const float* U, int64_t ldu, in
   }
   pl = merge_plan_for(d, k, r);
   mp = MergeParams{};
+  mp.hi_only = g_precision_hi_only ? 1 : 0;
   mp.W = static_cast<uint16_t*>(W);
   mp.ldw = ldw; mp.d = d; mp.k = k; mp.U = U; mp.ldu = ldu; mp.r = r;
   mp.u_vec = (((uintptr_t)U & 15) == 0 && (ldu & 3) == 0) ? 1 : 0;

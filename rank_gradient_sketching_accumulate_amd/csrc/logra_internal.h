@@ -114,6 +114,9 @@ struct MergeParams {
   // RowAdam folded into the merge: U = S with row i multiplied by rowmul[i]
   // (fp32) as it is loaded; null for a plain U.
   const float* rowmul;
+  // 1: U rounded once to bf16, one MFMA per product (sign basis only);
+  // 0: U as a bf16 hi/lo pair, two MFMAs per product.
+  int hi_only;
   int n_rb, n_cr;   // row blocks, column ranges
   int64_t cr_cols;  // columns per range (a multiple of the chunk width)
 };

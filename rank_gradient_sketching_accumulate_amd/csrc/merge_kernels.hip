@@ -46,8 +46,10 @@ __device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
 // GAUSS: the basis is the dense Gaussian one; its column-major bf16 hi/lo
 // planes (p.Athi, p.Atlo) feed the MFMA A operand directly and each product
 // takes three MFMAs (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-32 relative).
-template <int NBW, int CB, int NK, int PD, bool GAUSS = false>
+// HL = 1 (sign basis only): U rounded once to bf16, one MFMA per product.
+template <int NBW, int CB, int NK, int PD, bool GAUSS = false, int HL = 2>
 __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
+  static_assert(HL == 2 || !GAUSS, "the Gaussian basis keeps both halves of U");
   constexpr int STR = 9;        // dwords per row of row-major bits (8 + 1 pad)
   constexpr int CSTR = NK < 8 ? 9 : NK + 1;  // dwords per column of column-major bits (odd)
   constexpr int CW = 16 * CB;   // columns per chunk
@@ -175,7 +177,7 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
     if (nch > 0) build_block(c_begin);
   }
 
-  u32x4 uh[NK][NBW], ul[NK][NBW];
+  u32x4 uh[NK][NBW], ul[NK][HL == 2 ? NBW : 1];
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
@@ -183,10 +185,14 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float h0 = uraw[kk][nb][2 * q], h1 = uraw[kk][nb][2 * q + 1];
-        uint32_t h, l;
-        split_hi_lo2(h0, h1, h, l);
-        uh[kk][nb][q] = h;
-        ul[kk][nb][q] = l;
+        if constexpr (HL == 2) {
+          uint32_t h, l;
+          split_hi_lo2(h0, h1, h, l);
+          uh[kk][nb][q] = h;
+          ul[kk][nb][q] = l;
+        } else {
+          uh[kk][nb][q] = pack_bf16x2(h0, h1);
+        }
       }
 
   const SignExpander ex(g);
@@ -227,7 +233,7 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
 #pragma unroll
               for (int nb = 0; nb < NBW; ++nb) {
                 acc[mb][nb] = mfma_16x16x32(a, uh[kk][nb], acc[mb][nb]);
-                acc[mb][nb] = mfma_16x16x32(a, ul[kk][nb], acc[mb][nb]);
+                if constexpr (HL == 2) acc[mb][nb] = mfma_16x16x32(a, ul[kk][nb], acc[mb][nb]);
               }
             }
           }
@@ -269,21 +275,21 @@ __device__ __forceinline__ void merge_tile(const MergeParams& p, int lin) {
   }
 }
 
-template <int NBW, int CB, int NK, int PD, bool GAUSS = false>
+template <int NBW, int CB, int NK, int PD, bool GAUSS = false, int HL = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_kernel(MergeParams p) {
-  merge_tile<NBW, CB, NK, PD, GAUSS>(p, xcd_linear_id_m(blockIdx.x, gridDim.x));
+  merge_tile<NBW, CB, NK, PD, GAUSS, HL>(p, xcd_linear_id_m(blockIdx.x, gridDim.x));
 }
 
 // Several matrices in one launch (same rank, so the same tiling): the
 // logical workgroup ids are dealt to the matrices by the prefix table
 // `start`; each matrix's tiles are exactly those of its own launch.
-template <int NBW, int CB, int NK, int PD>
+template <int NBW, int CB, int NK, int PD, int HL = 2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void merge_group_kernel(MergeGroup grp) {
   const int lin = xcd_linear_id_m(blockIdx.x, gridDim.x);
   int j = 0;
   while (j + 1 < grp.count && lin >= grp.start[j + 1]) ++j;
   if (lin >= grp.start[grp.count]) return;
-  merge_tile<NBW, CB, NK, PD>(grp.p[j], lin - grp.start[j]);
+  merge_tile<NBW, CB, NK, PD, false, HL>(grp.p[j], lin - grp.start[j]);
 }
 
 namespace {
@@ -362,10 +368,13 @@ bool merge_launch(const MergePlan& pl, const MergeParams& mp, hipStream_t s) {
 #undef LOGRA_MERGE_GAUSS
     return false;
   }
-#define LOGRA_MERGE(nbw, cb, nk)                                                            \
-  if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                        \
-    hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, mp);    \
-    return true;                                                                            \
+#define LOGRA_MERGE(nbw, cb, nk)                                                                     \
+  if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                                 \
+    if (mp.hi_only)                                                                                  \
+      hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2, false, 1>), dim3(grid), dim3(256), 0, s, mp); \
+    else                                                                                             \
+      hipLaunchKernelGGL((merge_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, mp);           \
+    return true;                                                                                     \
   }
   LOGRA_MERGE(1, 4, 1) LOGRA_MERGE(1, 8, 1) LOGRA_MERGE(2, 4, 1) LOGRA_MERGE(2, 8, 1)
   LOGRA_MERGE(1, 4, 2) LOGRA_MERGE(1, 8, 2) LOGRA_MERGE(2, 4, 2) LOGRA_MERGE(2, 8, 2)
@@ -384,7 +393,10 @@ bool merge_group_launch(const MergePlan& pl, const MergeGroup& g, hipStream_t s)
   const int grid = (int)align_up_m((size_t)g.start[g.count], 8);
 #define LOGRA_MERGE_G(nbw, cb, nk)                                                                \
   if (pl.NBW == nbw && pl.CB == cb && pl.NK == nk) {                                              \
-    hipLaunchKernelGGL((merge_group_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, g);     \
+    if (g.p[0].hi_only)                                                                           \
+      hipLaunchKernelGGL((merge_group_kernel<nbw, cb, nk, 2, 1>), dim3(grid), dim3(256), 0, s, g); \
+    else                                                                                          \
+      hipLaunchKernelGGL((merge_group_kernel<nbw, cb, nk, 2>), dim3(grid), dim3(256), 0, s, g);    \
     return true;                                                                                  \
   }
   LOGRA_MERGE_G(1, 4, 1) LOGRA_MERGE_G(1, 8, 1) LOGRA_MERGE_G(2, 4, 1) LOGRA_MERGE_G(2, 8, 1)

@@ -1,7 +1,9 @@
-"""GPU parity of the single-bf16 contraction (logra_set_precision).
+"""GPU parity of the single-bf16 mode (logra_set_precision).
 
 With LOGRA_PRECISION_BF16 the fused sketch rounds the projected inputs P
-once to bf16 (round to nearest even) before the backward multiply.  It is
+once to bf16 (round to nearest even) before the backward multiply, and the
+merges (single, grouped, RowAdam folded in) round the factor U once to bf16
+before it meets the signs.  The sketch is
 compared (a) with the float64 oracle of the method, against the stated
 bar of 2e-3 relative Frobenius error, and (b) with the oracle that rounds P
 the same way (sketch_accumulate_rounded_projection), where the only
@@ -14,7 +16,9 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests._util import S_TOL, f64, padded_ld, rel_frob
+import math
+
+from tests._util import S_TOL, assert_weight_close, bf16_ulp, f64, padded_ld, rel_frob
 
 torch = pytest.importorskip("torch")
 lg = pytest.importorskip("rank_gradient_sketching_accumulate_amd")
@@ -129,3 +133,102 @@ def test_bf16_mode_every_layer(key, li, r, bf16_mode):
     print(f"[case] bf16 mode {key} {L.name} r={r}: vs method {e_m:.3e}, vs rounded-P oracle {e_r:.3e}", flush=True)
     assert e_m <= S_TOL
     assert e_r <= 1e-4
+
+
+def _u_rounding_bound(U, r, scale):
+    """Per-row bound on |dW_gpu - dW_exact| before the final rounding when U
+    is rounded once to bf16 (<= 2^-9 relative per entry) and the r products
+    accumulate in fp32: (2^-9 + r 2^-24) |scale|/sqrt(r) sum_j |U_ij|,
+    doubled for margin."""
+    U = np.abs(np.asarray(U, dtype=np.float64))
+    return 2.0 * (2.0**-9 + r * 2.0**-24) * abs(scale) / math.sqrt(r) * U.sum(axis=1, keepdims=True)
+
+
+MERGE_CASES = [(300, 1030, 64), (130, 2052, 256), (700, 1536, 128), (257, 4100, 300), (1000, 700, 512),
+               (64, 96, 1), (3584, 1024, 256)]
+
+
+@pytest.mark.parametrize("d,k,r", MERGE_CASES, ids=lambda v: str(v))
+def test_single_bf16_merge(d, k, r, bf16_mode):
+    """The merge with U rounded once to bf16.  From W = 0 the result is the
+    rounded update itself: it must equal the oracle fed the rounded U (up to
+    fp32 accumulation at rounding ties), and each entry must lie within one
+    bf16 ulp plus U's rounding bound of the exact oracle.  (From W = 0 the
+    Frobenius error stacks U's rounding, about 1.1e-3, on W's own, about
+    2.5e-3 in all, so the 2e-3 bar is checked from a realistic W, where the
+    update is a small change on top of the weight.)"""
+    seed = 7000 + d + r
+    print(f"[case] bf16 merge {d} {k} {r}", flush=True)
+    U = wl.random_tensor((d, r), seed, device=DEV, std=3.0)
+    A = oracle.rademacher_projection(seed, r, k)
+    Uh = f64(U)
+    bound = _u_rounding_bound(Uh, r, 0.5)
+    W = torch.zeros((d, padded_ld(k, 4)), dtype=torch.bfloat16, device=DEV)[:, :k]
+    lg.merge_update(W, U, seed, r, 0.5)
+    got = f64(W)
+    exact = oracle.merge_update(np.zeros((d, k)), Uh, A, 0.5)
+    rounded = oracle.merge_update(np.zeros((d, k)), oracle.round_to_bf16(Uh), A, 0.5)
+    err = np.abs(got - exact)
+    ulp = bf16_ulp(np.maximum(np.abs(got), np.abs(exact)))
+    assert not (err > ulp * 1.0000001 + bound).any()
+    same = float((got == rounded).mean())
+    print(f"[case]   equal to the rounded-U oracle: {same:.5f}", flush=True)
+    assert same >= 0.995
+    # a realistic weight: the update is a small change on top of it
+    W = wl.gaussian_bf16((d, k), 0.02, seed + 1, device=DEV, ld=padded_ld(k, 4))
+    W0 = f64(W)
+    lg.merge_update(W, U, seed, r, 1e-3)
+    assert_weight_close(f64(W), oracle.merge_update(W0, Uh, A, 1e-3), bound=_u_rounding_bound(Uh, r, 1e-3))
+
+
+def test_single_bf16_merge_is_not_the_pair():
+    """The mode changes what the merge computes: from W = 0 at r = 256 the
+    two modes differ on a visible share of entries (and agree after the
+    mode is switched back)."""
+    d, k, r = 512, 1024, 256
+    U = wl.random_tensor((d, r), 77, device=DEV, std=3.0)
+    out = []
+    for mode in (lg.PRECISION_BF16X2, lg.PRECISION_BF16, lg.PRECISION_BF16X2):
+        prev = lg.set_precision(mode)
+        try:
+            W = torch.zeros((d, k), dtype=torch.bfloat16, device=DEV)
+            lg.merge_update(W, U, 77, r, 0.5)
+            out.append(W)
+        finally:
+            lg.set_precision(prev)
+    assert torch.equal(out[0], out[2])
+    assert float((out[0] != out[1]).float().mean()) > 0.05
+
+
+def test_single_bf16_grouped_and_folded(bf16_mode):
+    """In the single-bf16 mode the grouped merge is bitwise the separate
+    merges, and RowAdam folded into the merge is bitwise RowAdam followed by
+    the merge."""
+    r = 256
+    shapes = [(300, 1032), (1536, 1536), (130, 4100)]
+    items, refs = [], []
+    for j, (d, k) in enumerate(shapes):
+        U = wl.random_tensor((d, r), 90 + j, device=DEV, std=2.0)
+        W = wl.gaussian_bf16((d, k), 0.02, 95 + j, device=DEV, ld=padded_ld(k, 4))
+        W2 = W.clone()
+        lg.merge_update(W2, U, 40 + j, r, 1e-3)
+        items.append((W, U, 40 + j, 1e-3))
+        refs.append(W2)
+    lg.merge_update_grouped(items, r)
+    torch.cuda.synchronize()
+    for (W, _, _, _), W2 in zip(items, refs):
+        assert torch.equal(W, W2)
+    d, k = 3584, 1024
+    W1 = wl.gaussian_bf16((d, k), 0.02, 11, device=DEV)
+    W2 = W1.clone()
+    v1 = torch.zeros(d, dtype=torch.float32, device=DEV)
+    v2 = torch.zeros_like(v1)
+    for t in (1, 2):
+        S = wl.random_tensor((d, r), 20 + t, device=DEV, std=0.5 * t)
+        U = S.clone()
+        lg.rowadam_scale(U, v1, t, 0.999, 1e-8)
+        lg.merge_update(W1, U, 5 + t, r, 1e-2)
+        lg.rowadam_merge(W2, S, v2, 5 + t, r, t, 0.999, 1e-8, 1e-2)
+        torch.cuda.synchronize()
+        assert torch.equal(v1, v2)
+        assert torch.equal(W1, W2)
