@@ -82,17 +82,21 @@ def merge_bytes(d, k, r):
     return 4 * d * k + 4 * d * r
 
 
-def load_traffic(workload: str):
-    """HBM bytes per sketch call from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources (else None)."""
+def load_traffic(workload: str, layer: str, r: int, precision: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary:
+    (bytes per sketch call, bytes per merge or None).  Both are None unless
+    the summary was taken on the current kernel sources for this layer, rank
+    and precision mode."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_sha():
-        return None
-    return t.get("sketch_call_bytes")
+    if (t.get("kernel_source_sha") != kernel_source_sha() or t.get("layer") != layer or t.get("r") != r
+            or t.get("precision") != precision):
+        return None, None
+    merge = [v for k, v in t.get("kernels", {}).items() if k.startswith("logra::merge_kernel")]
+    return t.get("sketch_call_bytes"), (merge[0] if len(merge) == 1 else None)
 
 
 def gpu_time_per_call(torch, stream, fn, n):
@@ -631,7 +635,7 @@ def main():
         if not args.no_kl:
             extras["predicted_kl"] = predicted_kl_timing(torch, lg, wl, stream, dev, max(10, args.steps))
 
-    traffic = load_traffic(args.workload)
+    traffic, merge_traffic = load_traffic(args.workload, f"{L.name} d={d} k={k}", r, args.precision)
     out = {
         "metric": "sketch-accumulate tokens/s/layer + merge GB/s, % of MI355X HBM roofline",
         "value": M * T / (step_ms * 1e-3),
@@ -680,6 +684,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": mg_gbs / HBM_PEAK_GBS,
+            "traffic": merge_traffic,
             "algorithmic_bytes": mb,
             "avg_us": t_merge * 1e6,
             "merges_timed": n_merges,

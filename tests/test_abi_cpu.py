@@ -457,3 +457,28 @@ def test_workspace_holds_no_signs(lib):
     for r in (64, 128, 256):
         sizes = {lib.logra_workspace_bytes(16384, 17408, k, r) for k in (1024, 5120, 17408, 65536)}
         assert len(sizes) == 1, (r, sizes)
+
+
+def test_bench_traffic_matches_only_its_own_configuration():
+    """The committed counter summary fills `traffic` only for the layer, rank
+    and precision mode it was taken on (and only on the current sources)."""
+    import json
+    import os
+
+    import bench
+
+    path = os.path.join(bench.ROOT, "profiles", "traffic_layer27b.json")
+    with open(path) as f:
+        t = json.load(f)
+    layer, r, prec = t["layer"], t["r"], t["precision"]
+    current = t["kernel_source_sha"] == bench.kernel_source_sha()
+    sk, mg = bench.load_traffic("layer27b", layer, r, prec)
+    if current:
+        assert sk == t["sketch_call_bytes"] and mg is not None and mg > 0
+    else:
+        assert sk is None and mg is None
+    assert bench.load_traffic("layer27b", layer, r + 1, prec) == (None, None)
+    assert bench.load_traffic("layer27b", "other d=1 k=1", r, prec) == (None, None)
+    other = "bf16" if prec == "bf16x2" else "bf16x2"
+    assert bench.load_traffic("layer27b", layer, r, other) == (None, None)
+    assert bench.load_traffic("no_such_workload", layer, r, prec) == (None, None)
