@@ -1333,6 +1333,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         u32x4 a[kDC];
         transpose_dy(y[u % (DP + 1)], a);
         const u32x4* ph = &pt[u & 1][0];
+        // Raised issue priority over the step's MFMAs: of the two workgroups
+        // sharing each SIMD, the one multiplying keeps the matrix core fed
+        // while the other issues its loads and transposes.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
           const u32x4 bh = ph[nb * 64 + lane];
@@ -1348,6 +1352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             for (int c = 0; c < kDC; ++c) acc[c][nb] = mfma_16x16x32(a[c], bh, acc[c][nb]);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (m + 1 < nsteps) store_p(stg[(u + 1) % DP], (u + 1) & 1);
         __syncthreads();
       }
